@@ -1,0 +1,273 @@
+"""Pins for the CPU oracle (runs without a GPU).
+
+The oracle is checked against things other than itself: hand-derived bytes
+and outputs of worked examples (tests/golden/pack_examples.txt), NumPy
+brute force on the dequantized dense matrix, closed forms (one-hot inputs,
+exact binary fractions, rounding ties), invariants (pack/unpack round trip,
+sign symmetry, zero weights) and the parameter counts printed on the pages.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from ternary_weight_decode_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pack_examples.txt")
+
+
+def _read_golden():
+    ex, cur = {}, None
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        if tok[0] == "example":
+            cur = {"name": tok[1], "N": int(tok[3]), "K": int(tok[5]), "total": int(tok[7]),
+                   "w": [], "bytes": {}, "y": {}}
+        elif tok[0] == "w":
+            cur["w"].append((int(tok[1]), int(tok[2]), int(tok[3])))
+        elif tok[0] == "byte":
+            cur["bytes"][int(tok[1])] = int(tok[2], 16)
+        elif tok[0] == "y":
+            cur["y"][int(tok[1])] = float(tok[2])
+        elif tok[0] in ("scale_rule", "x_rule"):
+            cur[tok[0]] = " ".join(tok[1:])
+        elif tok[0] == "end":
+            ex[cur["name"]] = cur
+    return ex
+
+
+def _golden_inputs(e):
+    n, k = e["N"], e["K"]
+    t = np.zeros((n, k), np.int8)
+    for (r, c, v) in e["w"]:
+        t[r, c] = v
+    s = np.zeros((n, k // 128), np.uint16)
+    if e["name"] == "ex1":
+        s[0, 0] = 0x3C00
+    else:
+        for r in range(n):
+            for b in range(k // 128):
+                s[r, b] = 0x3C00 + 8 * r + b
+    x = synth.f32_to_bf16_bits((np.arange(k) % 7 - 3).astype(np.float32)[None, :])
+    return t, s, x
+
+
+@pytest.mark.parametrize("name", ["ex1", "ex2"])
+def test_golden_bytes(name):
+    e = _read_golden()[name]
+    t, s, _ = _golden_inputs(e)
+    p = oracle.pack(t, s)
+    assert p.size == e["total"] == oracle.packed_bytes(e["N"], e["K"])
+    scale_start = (((e["N"] + 15) // 16 * 16) * e["K"] // 4 + 255) // 256 * 256
+    for off, val in e["bytes"].items():
+        assert p[off] == val, (off, p[off], val)
+    planes = p[:scale_start].copy()
+    listed = [o for o in e["bytes"] if o < scale_start]
+    planes[listed] = 0
+    assert not planes.any(), np.nonzero(planes)
+
+
+@pytest.mark.parametrize("name", ["ex1", "ex2"])
+def test_golden_gemv(name):
+    e = _read_golden()[name]
+    t, s, x = _golden_inputs(e)
+    p = oracle.pack(t, s)
+    y64, y32 = oracle.gemv_bf16(p, e["N"], e["K"], x)
+    want = np.zeros(e["N"])
+    for r, v in e["y"].items():
+        want[r] = v
+    assert np.array_equal(y64[0], want)
+    assert np.array_equal(y32[0], want.astype(np.float32))
+
+
+@pytest.mark.parametrize("n,k", [(1, 128), (16, 512), (20, 640), (33, 1152), (48, 2048), (5, 384)])
+def test_roundtrip(n, k):
+    rng = np.random.default_rng(n * 1000 + k)
+    t = synth.gen_ternary(rng, n, k)
+    s = synth.gen_scales(rng, n, k // 128)
+    p = oracle.pack(t, s)
+    t2, s2 = oracle.unpack(p, n, k)
+    assert np.array_equal(t, t2) and np.array_equal(s, s2)
+    c = oracle.stats(p, n, k)
+    assert c[0] == np.count_nonzero(t) and c[1] == np.count_nonzero(t < 0) and c[2] == 0
+
+
+def test_packed_size_formula():
+    # 34 bytes per 128 weights (2.125 bits per weight) plus row padding and alignment
+    for (n, k) in [(3072, 1024), (4096, 4096), (12288, 4096), (4096, 12288), (1024, 4096)]:
+        assert oracle.packed_bytes(n, k) == n * k // 128 * 34
+    assert oracle.packed_bytes(3072, 1024) == 835_584
+    assert oracle.packed_bytes(10, 100) == -1
+
+
+@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (37, 640, 3), (64, 1536, 8), (3, 256, 2)])
+def test_gemv_vs_bruteforce(n, k, m):
+    rng = np.random.default_rng(7 + n + k + m)
+    t = synth.gen_ternary(rng, n, k)
+    s = synth.gen_scales(rng, n, k // 128)
+    x = synth.gen_x_bf16(rng, m, k)
+    p = oracle.pack(t, s)
+    y64, y32 = oracle.gemv_bf16(p, n, k, x)
+    ref = brute.gemv_bf16(t, s, x)
+    assert oracle.rel_l2(y64, ref) < 1e-13
+    assert np.array_equal(y32, y64.astype(np.float32))
+    rows = np.array([n - 1, 0, n // 2])
+    y64r, _ = oracle.gemv_bf16(p, n, k, x, rows=rows)
+    assert np.array_equal(y64r, y64[:, rows])
+
+
+def test_gemv_special_cases():
+    rng = np.random.default_rng(11)
+    n, k = 40, 768
+    t = synth.gen_ternary(rng, n, k)
+    s = synth.gen_scales(rng, n, k // 128)
+    x = synth.gen_x_bf16(rng, 2, k)
+    # all-zero weights give exactly zero
+    y0, _ = oracle.gemv_bf16(oracle.pack(np.zeros_like(t), s), n, k, x)
+    assert not y0.any()
+    # negating every weight negates the output exactly
+    ya, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    yb, _ = oracle.gemv_bf16(oracle.pack(-t, s), n, k, x)
+    assert np.array_equal(ya, -yb)
+    # a one-hot activation picks one dequantized weight: t[n,k] * scale[n, k//128]
+    for kk in (0, 129, 767):
+        e = np.zeros((1, k), np.float32)
+        e[0, kk] = 1.0
+        y, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, synth.f32_to_bf16_bits(e))
+        want = t[:, kk] * s[:, kk // 128].view(np.float16).astype(np.float64)
+        assert np.array_equal(y[0], want)
+    # scales 2^-6 and small-integer activations: the result is an exact binary fraction
+    s6 = np.full_like(s, 0x2400)   # fp16 2^-6
+    xi = synth.f32_to_bf16_bits(rng.integers(-8, 9, size=(1, k)).astype(np.float32))
+    y, _ = oracle.gemv_bf16(oracle.pack(t, s6), n, k, xi)
+    want = (t.astype(np.int64) @ synth.bf16_bits_to_f32(xi)[0].astype(np.int64)) / 64.0
+    assert np.array_equal(y[0], want)
+
+
+def test_f16_conversion():
+    L = oracle.lib()
+    assert L.oracle_f16_to_f64(0x3C00) == 1.0
+    assert L.oracle_f16_to_f64(0xC000) == -2.0
+    assert L.oracle_f16_to_f64(0x0001) == 2.0 ** -24          # smallest subnormal
+    assert L.oracle_f16_to_f64(0x7BFF) == 65504.0              # largest normal
+    bits = np.arange(0, 0x7C00, 97, dtype=np.uint16)
+    assert all(L.oracle_f16_to_f64(int(b)) == float(np.uint16(b).view(np.float16)) for b in bits)
+
+
+def test_quantize_closed_forms():
+    # absmax 127 -> s = 1 exactly, so q = rint(x) with ties to even
+    row = np.array([127.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 126.5, -127.0, 0.0], np.float32)
+    q, s = oracle.quantize_i8(synth.f32_to_bf16_bits(row[None, :]))
+    assert s[0] == 1.0
+    assert q[0].tolist() == [127, 2, 4, -2, 0, 0, 2, 126, -127, 0]
+    # absmax 254 -> s = 2 exactly
+    row2 = np.array([254.0, 5.0, 7.0, -5.0, -254.0], np.float32)
+    q, s = oracle.quantize_i8(synth.f32_to_bf16_bits(row2[None, :]))
+    assert s[0] == 2.0 and q[0].tolist() == [127, 2, 4, -2, -127]
+    # all-zero row
+    q, s = oracle.quantize_i8(np.zeros((1, 256), np.uint16))
+    assert s[0] == 0.0 and not q.any()
+
+
+def test_quantize_properties():
+    rng = np.random.default_rng(5)
+    x = synth.gen_x_bf16(rng, 6, 4096)
+    q, s = oracle.quantize_i8(x)
+    xf = synth.bf16_bits_to_f32(x)
+    amax = np.abs(xf).max(axis=1)
+    for m in range(6):
+        i = int(np.argmax(np.abs(xf[m])))
+        assert abs(int(q[m, i])) == 127 and np.sign(q[m, i]) == np.sign(xf[m, i])
+        assert abs(s[m] - amax[m] / 127) <= 1e-7 * amax[m]
+        err = np.abs(xf[m] / np.float64(s[m]) - q[m])
+        assert err.max() <= 0.5 + 1e-5
+    assert np.abs(q.astype(int)).max() <= 127
+    # a power-of-two rescale of x leaves q unchanged and rescales s exactly
+    q2, s2 = oracle.quantize_i8(synth.f32_to_bf16_bits(xf * 4))
+    assert np.array_equal(q, q2) and np.array_equal(s2, s * 4)
+
+
+@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (37, 640, 3), (50, 1024, 8), (70, 256, 65)])
+def test_tern_i8_vs_bruteforce(n, k, m):
+    rng = np.random.default_rng(n + 3 * k + m)
+    t = synth.gen_ternary(rng, n, k)
+    s = synth.gen_scales(rng, n, k // 128)
+    q, sx = oracle.quantize_i8(synth.gen_x_bf16(rng, m, k))
+    p = oracle.pack(t, s)
+    acc, y64, y32 = oracle.tern_i8(p, n, k, q, sx)
+    acc_ref, y_ref = brute.tern_i8(t, s, q, sx)
+    assert np.array_equal(acc, acc_ref)
+    assert oracle.rel_l2(y64, y_ref) < 1e-13
+    # all-ones activations count (#+1) - (#-1) per block
+    ones = np.ones((1, k), np.int8)
+    acc1, _, _ = oracle.tern_i8(p, n, k, ones, np.ones(1, np.float32))
+    tb = t.reshape(n, k // 128, 128)
+    assert np.array_equal(acc1[0], (tb == 1).sum(-1) - (tb == -1).sum(-1))
+
+
+def test_tern_i8_unit_scale_integer():
+    # scales 1.0 and s_x = 1: y is the exact integer sum of the block accumulators
+    rng = np.random.default_rng(9)
+    n, k = 32, 1024
+    t = synth.gen_ternary(rng, n, k)
+    s1 = np.full((n, k // 128), 0x3C00, np.uint16)
+    q = rng.integers(-127, 128, size=(2, k)).astype(np.int8)
+    acc, y64, y32 = oracle.tern_i8(oracle.pack(t, s1), n, k, q, np.ones(2, np.float32))
+    assert np.array_equal(y64, (q.astype(np.int64) @ t.T.astype(np.int64)).astype(np.float64))
+
+
+def test_head_vs_bruteforce():
+    rng = np.random.default_rng(3)
+    v, k = 300, 512
+    w, rs = synth.gen_head(rng, rng, v, k)
+    x = synth.gen_x_bf16(rng, 3, k)
+    y64, _ = oracle.head_bf16(w, rs, x)
+    assert oracle.rel_l2(y64, brute.head_bf16(w, rs, x)) < 1e-13
+    # one-hot activation: logits = rs[v] * W[v, k]
+    e = np.zeros((1, k), np.float32)
+    e[0, 77] = 1.0
+    y, _ = oracle.head_bf16(w, rs, synth.f32_to_bf16_bits(e))
+    assert np.array_equal(y[0], rs.astype(np.float64) * w[:, 77])
+    q, sx = oracle.quantize_i8(x)
+    acc, y64i, _ = oracle.head_i8(w, rs, q, sx)
+    assert np.array_equal(acc, q.astype(np.int64) @ w.T.astype(np.int64))
+    assert oracle.rel_l2(y64i, acc * sx[:, None].astype(np.float64) * rs[None, :].astype(np.float64)) < 1e-15
+
+
+def test_parameter_counts_match_pages():
+    """Shapes reproduce the parameter accounting on the discuss.pytorch.kr page
+    (table in "세 모델과 하나의 컨테이너" and section "파라미터와 바이트는 서로 다른 회계다")."""
+    def tern(cfg):
+        return sum(l.n * l.k for l in synth.model_linears(cfg))
+    assert tern(2) == 6_945_767_424
+    assert tern(1) == 440_401_920
+    head8, head06 = 2 * synth.VOCAB * 4096, synth.VOCAB * 1024
+    assert head8 == 1_244_659_712 and head06 == 155_582_464
+    norms8 = 36 * (2 * 4096 + 2 * 128) + 4096
+    norms06 = 28 * (2 * 1024 + 2 * 128) + 1024
+    assert norms8 == 308_224
+    assert tern(2) + head8 + norms8 == 8_190_735_360
+    assert tern(1) + head06 + norms06 == 596_049_920
+    # the 3.0 bits-per-weight container lane (section "fp16의 8분의 1은 어떤 축의 이야기인가")
+    assert tern(2) * 3 // 8 == 2_604_662_784
+    # 252 linears per 8B token (aiatolah.com article, first paragraph)
+    assert len(synth.model_linears(2)) == 252
+
+
+def test_generator_statistics():
+    # occupancy of the generated states matches the configured probabilities within 5 sigma
+    for (p0, pp, seed) in [(synth.P_ZERO, synth.P_PLUS, 1), (synth.P_ZERO_SPARSE, synth.P_PLUS_SPARSE, 2)]:
+        t = synth.gen_ternary(np.random.default_rng(seed), 512, 4096, p0, pp)
+        n = t.size
+        for frac, p in [((t == 0).mean(), p0), ((t == 1).mean(), pp), ((t == -1).mean(), 1 - p0 - pp)]:
+            assert abs(frac - p) < 5 * np.sqrt(p * (1 - p) / n)
+    # fp16 scales land in [0.01, 0.05]; bf16 rounding is nearest-even
+    s = synth.gen_scales(np.random.default_rng(3), 64, 32).view(np.float16).astype(np.float64)
+    assert s.min() >= 0.0099 and s.max() <= 0.0501
+    assert synth.f32_to_bf16_bits(np.array([1.00390625], np.float32))[0] == 0x3F80   # tie -> even
+    assert synth.f32_to_bf16_bits(np.array([1.01171875], np.float32))[0] == 0x3F82   # tie -> even (up)
