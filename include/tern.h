@@ -1,0 +1,166 @@
+/*
+ * tern.h — C ABI of libtern.so: ternary-weight GEMV / GEMM kernels for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The decode step these calls implement: every transformer linear of a
+ * single-stream decode is a matrix-vector product over weights in {-1, 0, +1}
+ * (add, skip or subtract), kept packed in HBM and decoded inside the matrix
+ * kernel, plus an int8 output head.  Sources (pages on the Neutrino-1
+ * ternary-family models):
+ *   [P2] "Fermion Research, 3진 계열 포맷으로 직접 학습한 Neutrino-1 모델군 3종
+ *        공개" (discuss.pytorch.kr).  Sections cited by their headings.
+ *   [P4] aiatolah.com article announcing Neutrino-1 8B (Portuguese), sections
+ *        cited by their headings.
+ *   [P5] origotech.dev low-bit essay ("더 적은 비트로 계산하기"), Figure I.
+ *
+ * Conventions for every call
+ *  - All data pointers are DEVICE pointers allocated by the caller (for
+ *    example torch tensors), row-major and contiguous.  The library never
+ *    allocates, frees or synchronises; each call enqueues its kernels on
+ *    `stream` (a hipStream_t; NULL = the null stream) and returns at once.
+ *  - Outputs are fully overwritten.  Inputs are never written.
+ *  - Shapes are validated on the host before any HIP call, so a bad shape
+ *    returns TERN_E_SHAPE without touching the device.  Empty problems
+ *    (N == 0 or M == 0) return TERN_OK and enqueue nothing; K == 0 writes
+ *    zeros.
+ *  - Alignment: packed blobs, x, q and head rows must be 16-byte aligned.
+ *  - Errors: a non-zero tern_status; tern_last_error() gives the HIP error
+ *    string of the calling thread's last TERN_E_HIP.  Faults inside a kernel
+ *    surface at the caller's next synchronisation.
+ *  - The library keeps no mutable global state; calls are thread-safe.
+ *
+ * Packed ternary layout ("plane blob"), this library's own definition (the
+ * shipped FV5 internals are not published, [P2] section "FV5와 FV5B"):
+ *   W[N][K] with K % 128 == 0.  Block (n, b) covers k in [128b, 128b+128) of
+ *   row n and has one fp16 scale (block-wise scaling, [P5] section
+ *   "어떻게 작동하나"), a 128-bit nonzero plane and a 128-bit sign plane
+ *   (34 bytes per 128 weights = 2.125 bits per weight).  Each plane is four
+ *   little-endian 32-bit words; word w holds weights k = 128b + 32w + i,
+ *   i = 0..31, with weight i at bit 16*(i&1) + (i>>1).  Rows are padded to
+ *   Np = 16*ceil(N/16).  With rt = n/16, r = n%16, kt = b/4, bq = b%4,
+ *   nb = K/128, nbq = min(4, nb - 4kt):
+ *     word index  = (rt*nb + 4kt)*128 + ((plane*4 + w)*16 + r)*nbq + bq
+ *                   (plane 0 = nonzero, 1 = sign; byte offset = 4*index)
+ *     scale index = (rt*nb + 4kt)*16 + r*nbq + bq, fp16, starting at byte
+ *                   align256(Np*K/4)
+ *   Decoding: t = nz ? (sign ? -1 : +1) : 0.  Canonical form has sign = 0
+ *   wherever nz = 0; tern_pack emits it and the int8 kernels require it.
+ *   Dequantized weight: W[n][k] = t[n][k] * scale[n][k/128].
+ */
+#ifndef TERN_H
+#define TERN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TERN_OK = 0,
+    TERN_E_NULL = 1,    /* a required pointer is NULL */
+    TERN_E_SHAPE = 2,   /* negative size, K % 128 != 0, M out of range */
+    TERN_E_ALIGN = 3,   /* a pointer is not 16-byte aligned */
+    TERN_E_HIP = 4,     /* a HIP call or kernel launch failed */
+    TERN_E_DEVICE = 5   /* the current device is not gfx950 */
+} tern_status;
+
+#define TERN_ABI_VERSION 1
+#define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
+
+/* Human-readable name of a tern_status value (static string). */
+const char* tern_strerror(int status);
+
+/* HIP error text of this thread's last TERN_E_HIP ("" if none). */
+const char* tern_last_error(void);
+
+/* TERN_ABI_VERSION of the loaded library. */
+int tern_abi_version(void);
+
+/* Bytes of the packed blob for an N x K ternary matrix:
+ * align256(Np*K/4) + Np*(K/128)*2, Np = 16*ceil(N/16).  -1 on a bad shape. */
+int64_t tern_packed_bytes(int64_t N, int64_t K);
+
+/* Pack ternary weights (load-time work: the loader resolves backend layout
+ * once at load time with values unchanged, [P2] section "하나의 파일, 네 개의
+ * 백엔드"; bit-planes per block after the FV5 table of [P2]).
+ *   t      int8 [N][K], values in {-1, 0, +1} (other values are taken as
+ *          their sign)
+ *   scale  fp16 bit patterns [N][K/128]
+ *   packed output, tern_packed_bytes(N, K) bytes, 16-byte aligned; padding
+ *          rows are written as zeros. */
+int tern_pack(const int8_t* t, const uint16_t* scale, int64_t N, int64_t K, void* packed, void* stream);
+
+/* Occupancy of a packed matrix (the analogue of the container walk that
+ * counts zero / +1 / -1 states, [P2] section "출하된 컨테이너를 직접 읽기: 62.63%의 침묵").
+ *   counts  device uint64 [3]: nonzero weights, -1 weights, non-canonical
+ *           bits (sign set where nonzero is clear), over the N real rows. */
+int tern_stats(const void* packed, int64_t N, int64_t K, uint64_t* counts, void* stream);
+
+/* Per-row absmax int8 quantization of bf16 activations (an int8-activation
+ * runtime is mentioned in [P2] section "토큰 동일성의 경계: 그리디, float32,
+ * 그리고 두 개의 근접 동점"; the quantizer is
+ * not described there, so this plain reading is used):
+ *   a = max_k |x[m][k]|, s_x[m] = a / 127 (fp32, IEEE division, nearest-even),
+ *   q[m][k] = clamp(rint(x[m][k] / s_x[m]), -127, 127) (fp32 quotient, ties
+ *   to even); a == 0 gives s_x = 0 and q = 0.
+ *   x  bf16 bits [M][K] (K % 16 == 0);  q  int8 [M][K];  s_x  fp32 [M]. */
+int tern_quantize_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s_x, void* stream);
+
+/* Ternary GEMV / small-M GEMM with bf16 activations and fp32 accumulation
+ * (the linear y_j = sum_i w_ij x_i of [P2] section "학습 중에 포맷이 있어야
+ * 하는 이유"; add / skip / subtract of [P5] Figure I; weights decoded inside
+ * the matrix kernel, [P4] opening paragraphs; up to 7 speculative positions per
+ * batched forward, [P2] section "검증된 추측 디코딩: 속도만 바꾸고 답은 바꾸지
+ * 않는다"):
+ *   y[m][n] = sum_b scale[n][b] * sum_{k in block b} t[n][k] * x[m][k]
+ *   packed  plane blob of an N x K matrix
+ *   x       bf16 bits [M][K], 1 <= M <= TERN_MAX_M_GEMV
+ *   y       fp32 [M][N]
+ * Accuracy: fp32 accumulation; relative L2 error against the exact value is
+ * ~1e-7 (any summation order). */
+int tern_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream);
+
+/* Ternary GEMV / small-M GEMM with int8 activations (q, s_x from
+ * tern_quantize_i8 or the caller):
+ *   acc[m][n][b] = sum_{k in block b} t[n][k] * q[m][k]   (exact int32)
+ *   y[m][n] = s_x[m] * sum_b scale[n][b] * acc[m][n][b]  (fp32)
+ *   q        int8 [M][K];  s_x fp32 [M];  1 <= M <= TERN_MAX_M_GEMV
+ *   acc_dbg  NULL or int32 [M][N][K/128]: the block accumulators (debug;
+ *            for small shapes). */
+int tern_gemv_i8(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
+                 float* y, int32_t* acc_dbg, void* stream);
+
+/* int8 output-head GEMV with a per-row fp32 scale and bf16 activations
+ * (embedding and head stay int8, [P2] section "3진 계열이라는 이름의 실체";
+ * the unembedding runs on the DRAM roofline, [P2] section "뉴트리노 엔진:
+ * 토큰 하나의 시간은 어디로 가는가"):
+ *   logits[m][v] = row_scale[v] * sum_k W[v][k] * x[m][k]
+ *   W  int8 [V][K] (K % 16 == 0);  row_scale fp32 [V];  x bf16 bits [M][K];
+ *   logits fp32 [M][V];  1 <= M <= TERN_MAX_M_GEMV. */
+int i8_head_gemv(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                 float* logits, void* stream);
+
+/* int8 output head with int8 activations:
+ *   acc[m][v] = sum_k W[v][k] * q[m][k] (exact int32),
+ *   logits[m][v] = row_scale[v] * s_x[m] * acc[m][v]
+ *   acc_dbg NULL or int32 [M][V]. */
+int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                    const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
+
+/* Prefill-size ternary GEMM with int8 activations (batched prefill, [P2]
+ * section "실행해보기: pip부터 llama.cpp 포크까지"; batched verify is
+ * compute-bound, section "노트북에서는 이야기가 다르다"),
+ * same arithmetic as tern_gemv_i8 for any M >= 1, built for M >= 64: planes
+ * are decoded to int8 and fed to the int8 matrix cores.
+ *   q int8 [M][K]; s_x fp32 [M]; y fp32 [M][N];
+ *   acc_dbg NULL or int32 [M][N][K/128] (debug; small shapes). */
+int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
+                      float* y, int32_t* acc_dbg, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TERN_H */

@@ -1,0 +1,184 @@
+"""Python binding of libtern.so — gfx950 ternary-weight GEMV / GEMM kernels.
+
+Thin argument marshalling over the C ABI of ``include/tern.h``: every call
+takes torch tensors that already live on the GPU, passes their device
+pointers and the current HIP stream to the library, and raises
+``RuntimeError`` with the library's status text on any error.  torch is used
+for device memory and streams only; every step of the computation runs in the
+library's HIP kernels.  There is no fallback: if ``libtern.so`` is missing or
+fails to load, every call raises.
+
+Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
+``tern_gemv``, ``tern_gemv_i8``, ``i8_head_gemv``, ``i8_head_gemv_i8``,
+``tern_gemm_prefill``, ``tern_packed_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtern.so")
+MAX_M_GEMV = 16
+SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
+           "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill")
+
+_lib = None
+_i64 = ctypes.c_int64
+_p = ctypes.c_void_p
+
+
+def lib():
+    """Load libtern.so (built in-tree by ternary_weight_decode_amd.build); raise if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run `python -m ternary_weight_decode_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.tern_strerror.restype = ctypes.c_char_p
+        L.tern_strerror.argtypes = [ctypes.c_int]
+        L.tern_last_error.restype = ctypes.c_char_p
+        L.tern_abi_version.restype = ctypes.c_int
+        L.tern_packed_bytes.restype = _i64
+        L.tern_packed_bytes.argtypes = [_i64, _i64]
+        L.tern_pack.argtypes = [_p, _p, _i64, _i64, _p, _p]
+        L.tern_stats.argtypes = [_p, _i64, _i64, _p, _p]
+        L.tern_quantize_i8.argtypes = [_p, _i64, _i64, _p, _p, _p]
+        L.tern_gemv.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
+        L.tern_gemv_i8.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        L.i8_head_gemv.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.i8_head_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        L.tern_gemm_prefill.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        for name in SYMBOLS[4:]:
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(name: str, rc: int):
+    if rc != 0:
+        L = lib()
+        raise RuntimeError(f"{name}: {L.tern_strerror(rc).decode()} {L.tern_last_error().decode()}".strip())
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtypes, ndim=None):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise RuntimeError(f"{name} must be a CUDA/HIP tensor")
+    if t.dtype not in dtypes:
+        raise RuntimeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise RuntimeError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise RuntimeError(f"{name} must have {ndim} dimensions")
+
+
+def tern_packed_bytes(n: int, k: int) -> int:
+    return int(lib().tern_packed_bytes(n, k))
+
+
+def tern_pack(t, scale, out=None, stream=None):
+    """t int8 [N,K] in {-1,0,1}; scale fp16 bits [N,K/128] (int16/uint16/float16) -> packed uint8 blob."""
+    import torch
+    _need(t, "t", (torch.int8,), 2)
+    _need(scale, "scale", (torch.int16, torch.uint16, torch.float16), 2)
+    n, k = t.shape
+    nbytes = tern_packed_bytes(n, k)
+    if nbytes < 0:
+        _check("tern_pack", 2)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=t.device)
+    _check("tern_pack", lib().tern_pack(_ptr(t), _ptr(scale), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def tern_stats(packed, n: int, k: int, out=None, stream=None):
+    """-> int64 [3]: nonzero weights, -1 weights, non-canonical sign bits."""
+    import torch
+    if out is None:
+        out = torch.empty(3, dtype=torch.int64, device=packed.device)
+    _check("tern_stats", lib().tern_stats(_ptr(packed), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def tern_quantize_i8(x, q=None, s_x=None, stream=None):
+    """x bf16 [M,K] -> (q int8 [M,K], s_x fp32 [M])."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m, k = x.shape
+    if q is None:
+        q = torch.empty((m, k), dtype=torch.int8, device=x.device)
+    if s_x is None:
+        s_x = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("tern_quantize_i8", lib().tern_quantize_i8(_ptr(x), m, k, _ptr(q), _ptr(s_x), _stream(stream)))
+    return q, s_x
+
+
+def tern_gemv(packed, n: int, k: int, x, y=None, stream=None):
+    """y[m,n] = sum_b scale[n,b] sum_{k in b} t[n,k] x[m,k]; x bf16 [M,K], M <= 16 -> y fp32 [M,N]."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check("tern_gemv", lib().tern_gemv(_ptr(packed), n, k, _ptr(x), m, _ptr(y), _stream(stream)))
+    return y
+
+
+def tern_gemv_i8(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=None):
+    """int8 activations: y = s_x[m] * sum_b scale[n,b] acc[m,n,b]; acc (optional) int32 [M,N,K/128]."""
+    import torch
+    _need(q, "q", (torch.int8,), 2)
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=q.device)
+    _check("tern_gemv_i8", lib().tern_gemv_i8(_ptr(packed), n, k, _ptr(q), _ptr(s_x), m, _ptr(y), _ptr(acc),
+                                              _stream(stream)))
+    return y
+
+
+def i8_head_gemv(w, row_scale, x, y=None, stream=None):
+    """logits[m,v] = row_scale[v] sum_k W[v,k] x[m,k]; W int8 [V,K], x bf16 [M,K]."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    v, k = w.shape
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=x.device)
+    _check("i8_head_gemv", lib().i8_head_gemv(_ptr(w), _ptr(row_scale), v, k, _ptr(x), m, _ptr(y),
+                                              _stream(stream)))
+    return y
+
+
+def i8_head_gemv_i8(w, row_scale, q, s_x, y=None, acc=None, stream=None):
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(q, "q", (torch.int8,), 2)
+    v, k = w.shape
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=q.device)
+    _check("i8_head_gemv_i8", lib().i8_head_gemv_i8(_ptr(w), _ptr(row_scale), v, k, _ptr(q), _ptr(s_x), m, _ptr(y),
+                                                    _ptr(acc), _stream(stream)))
+    return y
+
+
+def tern_gemm_prefill(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=None):
+    import torch
+    _need(q, "q", (torch.int8,), 2)
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=q.device)
+    _check("tern_gemm_prefill", lib().tern_gemm_prefill(_ptr(packed), n, k, _ptr(q), _ptr(s_x), m, _ptr(y),
+                                                        _ptr(acc), _stream(stream)))
+    return y

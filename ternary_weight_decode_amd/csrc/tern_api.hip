@@ -1,0 +1,191 @@
+// tern_api.hip — the extern "C" surface declared in include/tern.h.
+//
+// Every entry point validates shapes, pointers and alignment on the host
+// before any HIP call (so argument errors are testable without a device),
+// checks once per device that it is a gfx950, and enqueues the launchers of
+// tern_launch.h on the caller's stream.  Nothing here allocates, frees or
+// synchronises.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/tern.h"
+#include "tern_launch.h"
+
+namespace {
+
+thread_local char g_last_error[256] = "";
+
+int hip_fail(hipError_t e)
+{
+    const char* s = hipGetErrorString(e);
+    std::strncpy(g_last_error, s ? s : "unknown HIP error", sizeof(g_last_error) - 1);
+    g_last_error[sizeof(g_last_error) - 1] = 0;
+    return TERN_E_HIP;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+// per-device result of the gfx950 check: 0 unknown, 1 ok, 2 not gfx950
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];
+
+int check_device()
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e);
+    if (dev < 0 || dev >= kMaxDevices) return TERN_E_DEVICE;
+    int st = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_fail(e);
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_device_ok[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? TERN_OK : TERN_E_DEVICE;
+}
+
+int finish(hipError_t e) { return e == hipSuccess ? TERN_OK : hip_fail(e); }
+
+bool bad_nk(int64_t N, int64_t K) { return N < 0 || K < 0 || K % 128 != 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* tern_strerror(int status)
+{
+    switch (status) {
+    case TERN_OK: return "ok";
+    case TERN_E_NULL: return "null pointer argument";
+    case TERN_E_SHAPE: return "invalid shape (negative size, K not a multiple of 128, or M out of range)";
+    case TERN_E_ALIGN: return "pointer not 16-byte aligned";
+    case TERN_E_HIP: return "HIP error (see tern_last_error)";
+    case TERN_E_DEVICE: return "current device is not a gfx950 (MI355X)";
+    default: return "unknown tern status";
+    }
+}
+
+const char* tern_last_error(void) { return g_last_error; }
+
+int tern_abi_version(void) { return TERN_ABI_VERSION; }
+
+int64_t tern_packed_bytes(int64_t N, int64_t K)
+{
+    if (bad_nk(N, K)) return -1;
+    return tern::align256(tern::npad16(N) * K / 4) + tern::npad16(N) * (K / 128) * 2;
+}
+
+int tern_pack(const int8_t* t, const uint16_t* scale, int64_t N, int64_t K, void* packed, void* stream)
+{
+    if (bad_nk(N, K)) return TERN_E_SHAPE;
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!t || !scale || !packed) return TERN_E_NULL;
+    if (!aligned16(t) || !aligned16(packed) || ((uintptr_t)scale & 1u)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_pack(t, scale, N, K, (uint8_t*)packed, (hipStream_t)stream));
+}
+
+int tern_stats(const void* packed, int64_t N, int64_t K, uint64_t* counts, void* stream)
+{
+    if (bad_nk(N, K)) return TERN_E_SHAPE;
+    if (!counts || (!packed && N > 0 && K > 0)) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || ((uintptr_t)counts & 7u)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_stats((const uint8_t*)packed, N, K, counts, (hipStream_t)stream));
+}
+
+int tern_quantize_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s_x, void* stream)
+{
+    if (M < 0 || K < 0 || K % 16 != 0) return TERN_E_SHAPE;
+    if (M == 0) return TERN_OK;
+    if (!s_x || (K > 0 && (!x || !q))) return TERN_E_NULL;
+    if ((x && !aligned16(x)) || (q && !aligned16(q)) || !aligned4(s_x)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_quantize(x, M, K, q, s_x, (hipStream_t)stream));
+}
+
+int tern_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream)
+{
+    if (bad_nk(N, K) || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (N == 0 || M == 0) return TERN_OK;
+    if (!y || (K > 0 && (!packed || !x))) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || (x && !aligned16(x)) || !aligned4(y)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
+    return finish(tern::launch_gemv_bf16((const uint8_t*)packed, N, K, x, M, y, (hipStream_t)stream));
+}
+
+int tern_gemv_i8(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M, float* y,
+                 int32_t* acc_dbg, void* stream)
+{
+    if (bad_nk(N, K) || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (N == 0 || M == 0) return TERN_OK;
+    if (!y || !s_x || (K > 0 && (!packed || !q))) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || (q && !aligned16(q)) || !aligned4(y) || !aligned4(s_x) ||
+        (acc_dbg && !aligned4(acc_dbg)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
+    return finish(tern::launch_gemv_i8((const uint8_t*)packed, N, K, q, s_x, M, y, acc_dbg, (hipStream_t)stream));
+}
+
+int i8_head_gemv(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                 float* logits, void* stream)
+{
+    if (bad_nk(V, K) || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (V == 0 || M == 0) return TERN_OK;
+    if (!logits || !row_scale || (K > 0 && (!W || !x))) return TERN_E_NULL;
+    if ((W && !aligned16(W)) || (x && !aligned16(x)) || !aligned4(logits) || !aligned4(row_scale))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(logits, M * V * 4, (hipStream_t)stream));
+    return finish(tern::launch_head_bf16(W, row_scale, V, K, x, M, logits, (hipStream_t)stream));
+}
+
+int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                    const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream)
+{
+    if (bad_nk(V, K) || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (V == 0 || M == 0) return TERN_OK;
+    if (!logits || !row_scale || !s_x || (K > 0 && (!W || !q))) return TERN_E_NULL;
+    if ((W && !aligned16(W)) || (q && !aligned16(q)) || !aligned4(logits) || !aligned4(row_scale) ||
+        !aligned4(s_x) || (acc_dbg && !aligned4(acc_dbg)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) {
+        rc = finish(tern::launch_fill_zero(logits, M * V * 4, (hipStream_t)stream));
+        if (rc || !acc_dbg) return rc;
+        return finish(tern::launch_fill_zero(acc_dbg, M * V * 4, (hipStream_t)stream));
+    }
+    return finish(tern::launch_head_i8(W, row_scale, V, K, q, s_x, M, logits, acc_dbg, (hipStream_t)stream));
+}
+
+int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
+                      float* y, int32_t* acc_dbg, void* stream)
+{
+    if (bad_nk(N, K) || M < 0) return TERN_E_SHAPE;
+    if (N == 0 || M == 0) return TERN_OK;
+    if (!y || !s_x || (K > 0 && (!packed || !q))) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || (q && !aligned16(q)) || !aligned4(y) || !aligned4(s_x) ||
+        (acc_dbg && !aligned4(acc_dbg)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
+    return finish(tern::launch_prefill((const uint8_t*)packed, N, K, q, s_x, M, y, acc_dbg, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// tern_launch.h — host-side launchers of the gfx950 kernels.  Arguments are
+// already validated by the C ABI layer (tern_api.cpp); each launcher enqueues
+// on `stream` and returns hipGetLastError() of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+
+__host__ __device__ inline int64_t npad16(int64_t n) { return (n + 15) / 16 * 16; }
+__host__ __device__ inline int64_t align256(int64_t v) { return (v + 255) / 256 * 256; }
+__host__ __device__ inline int64_t scale_region_offset(int64_t N, int64_t K) { return align256(npad16(N) * K / 4); }
+
+hipError_t launch_fill_zero(void* dst, int64_t bytes, hipStream_t stream);
+hipError_t launch_pack(const int8_t* t, const uint16_t* scale, int64_t N, int64_t K, uint8_t* packed,
+                       hipStream_t stream);
+hipError_t launch_stats(const uint8_t* packed, int64_t N, int64_t K, uint64_t* counts, hipStream_t stream);
+hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* s, hipStream_t stream);
+hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                            hipStream_t stream);
+hipError_t launch_gemv_i8(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
+                          int64_t M, float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                            float* y, hipStream_t stream);
+hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                          const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
+                          int64_t M, float* y, int32_t* acc, hipStream_t stream);
+
+}  // namespace tern

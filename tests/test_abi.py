@@ -1,0 +1,107 @@
+"""The C ABI loads, exports every declared symbol, and rejects bad arguments
+on the host before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import ternary_weight_decode_amd as tw
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tern.h")
+
+E_OK, E_NULL, E_SHAPE, E_ALIGN = 0, 1, 2, 3
+ALIGNED = ctypes.c_void_p(0x10000)      # never dereferenced: every call below fails validation first
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 12
+    L = tw.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(tw.SYMBOLS)
+
+
+def test_version_and_strings():
+    L = tw.lib()
+    assert L.tern_abi_version() == 1
+    for rc in range(6):
+        assert len(L.tern_strerror(rc)) > 0
+    assert L.tern_last_error() == b""
+
+
+def test_packed_bytes():
+    assert tw.tern_packed_bytes(3072, 1024) == 835_584
+    assert tw.tern_packed_bytes(1, 128) == 544
+    assert tw.tern_packed_bytes(20, 640) == 5440
+    assert tw.tern_packed_bytes(12288, 4096) == 12288 * 4096 // 128 * 34
+    assert tw.tern_packed_bytes(0, 128) == 0
+    assert tw.tern_packed_bytes(16, 100) == -1
+    assert tw.tern_packed_bytes(-1, 128) == -1
+
+
+def test_shape_errors_before_any_device_call():
+    L = tw.lib()
+    p, s = ALIGNED, None
+    assert L.tern_gemv(p, 16, 100, p, 1, p, s) == E_SHAPE          # K % 128
+    assert L.tern_gemv(p, -1, 128, p, 1, p, s) == E_SHAPE          # negative N
+    assert L.tern_gemv(p, 16, 128, p, 17, p, s) == E_SHAPE         # M > 16
+    assert L.tern_gemv(p, 16, 128, p, -1, p, s) == E_SHAPE
+    assert L.tern_gemv_i8(p, 16, 128, p, p, 17, p, None, s) == E_SHAPE
+    assert L.i8_head_gemv(p, p, 100, 96, p, 1, p, s) == E_SHAPE
+    assert L.i8_head_gemv_i8(p, p, 100, 128, p, p, 20, p, None, s) == E_SHAPE
+    assert L.tern_gemm_prefill(p, 16, 200, p, p, 64, p, None, s) == E_SHAPE
+    assert L.tern_gemm_prefill(p, 16, 128, p, p, -5, p, None, s) == E_SHAPE
+    assert L.tern_pack(p, p, 16, 130, p, s) == E_SHAPE
+    assert L.tern_stats(p, 16, 130, p, s) == E_SHAPE
+    assert L.tern_quantize_i8(p, 4, 24, p, p, s) == E_SHAPE        # K % 16
+    assert L.tern_quantize_i8(p, -4, 32, p, p, s) == E_SHAPE
+
+
+def test_empty_problems_are_no_ops():
+    L = tw.lib()
+    assert L.tern_gemv(None, 0, 128, None, 1, None, None) == E_OK
+    assert L.tern_gemv(None, 16, 128, None, 0, None, None) == E_OK
+    assert L.tern_gemv_i8(None, 16, 128, None, None, 0, None, None, None) == E_OK
+    assert L.i8_head_gemv(None, None, 0, 128, None, 1, None, None) == E_OK
+    assert L.tern_gemm_prefill(None, 16, 128, None, None, 0, None, None, None) == E_OK
+    assert L.tern_pack(None, None, 0, 128, None, None) == E_OK
+    assert L.tern_quantize_i8(None, 0, 128, None, None, None) == E_OK
+
+
+def test_null_and_alignment_errors():
+    L = tw.lib()
+    p, m = ALIGNED, MISALIGNED
+    assert L.tern_gemv(None, 16, 128, p, 1, p, None) == E_NULL
+    assert L.tern_gemv(p, 16, 128, None, 1, p, None) == E_NULL
+    assert L.tern_gemv(p, 16, 128, p, 1, None, None) == E_NULL
+    assert L.tern_gemv(m, 16, 128, p, 1, p, None) == E_ALIGN
+    assert L.tern_gemv(p, 16, 128, m, 1, p, None) == E_ALIGN
+    assert L.tern_gemv_i8(p, 16, 128, p, None, 1, p, None, None) == E_NULL
+    assert L.tern_gemv_i8(p, 16, 128, m, p, 1, p, None, None) == E_ALIGN
+    assert L.i8_head_gemv(p, None, 16, 128, p, 1, p, None) == E_NULL
+    assert L.i8_head_gemv(m, p, 16, 128, p, 1, p, None) == E_ALIGN
+    assert L.i8_head_gemv_i8(p, p, 16, 128, p, None, 1, p, None, None) == E_NULL
+    assert L.tern_gemm_prefill(p, 16, 128, None, p, 64, p, None, None) == E_NULL
+    assert L.tern_gemm_prefill(p, 16, 128, m, p, 64, p, None, None) == E_ALIGN
+    assert L.tern_pack(None, p, 16, 128, p, None) == E_NULL
+    assert L.tern_pack(p, p, 16, 128, m, None) == E_ALIGN
+    assert L.tern_stats(p, 16, 128, None, None) == E_NULL
+    assert L.tern_quantize_i8(p, 2, 128, p, None, None) == E_NULL
+    assert L.tern_quantize_i8(m, 2, 128, p, p, None) == E_ALIGN
+
+
+def test_binding_raises_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(tw, "_lib", None)
+    monkeypatch.setattr(tw, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="not built"):
+        tw.lib()

@@ -1,0 +1,265 @@
+"""GPU parity: every call of the C ABI against the CPU oracle on the same
+seeded inputs.  Integer results (packed bytes, statistics, int8 codes, int32
+block accumulators) must match bit for bit; float outputs within a relative
+L2 error of 1e-5 of the fp64 oracle (fp32 accumulation gives ~1e-7), or bit
+for bit where the result is exact by construction."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import brute
+from ternary_weight_decode_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def tw():
+    import torch
+    import ternary_weight_decode_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def dev(a):
+    import torch
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda()
+    return torch.from_numpy(a).cuda()
+
+
+def host(t):
+    import torch
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gen(n, k, m=1, seed=0, p0=synth.P_ZERO, pp=synth.P_PLUS):
+    rng = np.random.default_rng(seed)
+    t = synth.gen_ternary(rng, n, k, p0, pp)
+    s = synth.gen_scales(rng, n, k // 128)
+    x = synth.gen_x_bf16(rng, m, k)
+    return t, s, x
+
+
+def gpu_pack(tw, t, s):
+    return tw.tern_pack(dev(t), dev(s))
+
+
+SHAPES = [(16, 128), (20, 640), (3072, 1024), (37, 1536), (100, 2560), (1024, 4096), (48, 12288), (5, 384)]
+
+
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_pack_bit_exact(tw, n, k):
+    t, s, _ = gen(n, k, seed=n + k)
+    p = host(gpu_pack(tw, t, s))
+    assert np.array_equal(p, oracle.pack(t, s))
+    c = host(tw.tern_stats(gpu_pack(tw, t, s), n, k))
+    assert c.tolist() == oracle.stats(oracle.pack(t, s), n, k).astype(np.int64).tolist()
+
+
+def test_pack_golden_examples(tw):
+    from test_oracle import _golden_inputs, _read_golden
+    for name, e in _read_golden().items():
+        t, s, x = _golden_inputs(e)
+        p = host(gpu_pack(tw, t, s))
+        assert p.size == e["total"]
+        for off, val in e["bytes"].items():
+            assert p[off] == val, (name, off)
+        y = host(tw.tern_gemv(gpu_pack(tw, t, s), e["N"], e["K"], dev(x)))
+        want = np.zeros(e["N"], np.float32)
+        for r, v in e["y"].items():
+            want[r] = v
+        assert np.array_equal(y[0], want), name
+
+
+@pytest.mark.parametrize("n,k,m", [(3072, 1024, 1), (16, 128, 1), (20, 640, 3), (37, 1536, 2), (100, 2560, 4),
+                                   (1024, 4096, 7), (1024, 4096, 8), (48, 12288, 1), (48, 12288, 8),
+                                   (64, 4096, 16), (33, 2048, 5), (256, 1152, 1)])
+def test_gemv_bf16(tw, n, k, m):
+    t, s, x = gen(n, k, m, seed=3 * n + k + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert y.shape == (m, n)
+    assert oracle.rel_l2(y, y64) <= TOL, oracle.rel_l2(y, y64)
+    # per-row check too: no single row may be badly off
+    err = np.abs(y - y64).max(axis=1) / np.maximum(np.abs(y64).max(axis=1), 1e-30)
+    assert err.max() < 1e-4
+
+
+def test_gemv_config0(tw):
+    """Config 0: one 3072x1024 ternary linear, M=1, seed 0."""
+    t, s, x = synth.config0_inputs()
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), 3072, 1024, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), 3072, 1024, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+
+
+def test_gemv_exact_cases(tw):
+    n, k = 300, 1536
+    t, s, x = gen(n, k, 2, seed=5)
+    p = gpu_pack(tw, t, s)
+    # all-zero weights -> exactly zero
+    z = host(tw.tern_gemv(gpu_pack(tw, np.zeros_like(t), s), n, k, dev(x)))
+    assert not z.any()
+    # negated weights -> bit-exact negation (fixed summation order)
+    ya = host(tw.tern_gemv(p, n, k, dev(x)))
+    yb = host(tw.tern_gemv(gpu_pack(tw, -t, s), n, k, dev(x)))
+    assert np.array_equal(ya, -yb)
+    # deterministic: same inputs, same bytes
+    assert np.array_equal(ya, host(tw.tern_gemv(p, n, k, dev(x))))
+    # one-hot activation -> t[n,k] * scale exactly
+    for kk in (0, 517, 1535):
+        e = np.zeros((1, k), np.float32)
+        e[0, kk] = 1.0
+        y = host(tw.tern_gemv(p, n, k, dev(synth.f32_to_bf16_bits(e))))
+        want = (t[:, kk] * s[:, kk // 128].view(np.float16).astype(np.float64)).astype(np.float32)
+        assert np.array_equal(y[0], want)
+    # scales 2^-6 and small-integer activations: exact binary fractions
+    s6 = np.full_like(s, 0x2400)
+    xi = synth.f32_to_bf16_bits(np.random.default_rng(1).integers(-8, 9, size=(3, k)).astype(np.float32))
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s6), n, k, dev(xi)))
+    want = (synth.bf16_bits_to_f32(xi).astype(np.int64) @ t.T.astype(np.int64)) / 64.0
+    assert np.array_equal(y, want.astype(np.float32))
+
+
+def test_gemv_k_zero_and_empty(tw):
+    import torch
+    y = torch.full((2, 16), 7.0, device="cuda")
+    p = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    x = torch.zeros((2, 16), dtype=torch.bfloat16, device="cuda")
+    tw.tern_gemv(p, 16, 0, x, y=y)
+    assert not host(y).any()
+
+
+@pytest.mark.parametrize("m,k", [(1, 1024), (3, 4096), (8, 12288), (2, 128), (16, 2048)])
+def test_quantize_bit_exact(tw, m, k):
+    x = synth.gen_x_bf16(np.random.default_rng(m * k), m, k)
+    x[0, 5] = synth.f32_to_bf16_bits(np.array([9.5], np.float32))[0]
+    q, sx = tw.tern_quantize_i8(dev(x))
+    q0, s0 = oracle.quantize_i8(x)
+    assert np.array_equal(host(q), q0)
+    assert np.array_equal(host(sx).view(np.uint32), s0.view(np.uint32))
+
+
+def test_quantize_edge_rows(tw):
+    rows = np.zeros((4, 256), np.float32)
+    rows[1, :10] = [127.0, 2.5, 3.5, -2.5, 0.5, -0.5, 1.5, 126.5, -127.0, 0.0]
+    rows[2, :5] = [254.0, 5.0, 7.0, -5.0, -254.0]
+    rows[3, 7] = -3.0e-3
+    x = synth.f32_to_bf16_bits(rows)
+    q, sx = tw.tern_quantize_i8(dev(x))
+    q0, s0 = oracle.quantize_i8(x)
+    assert np.array_equal(host(q), q0) and np.array_equal(host(sx), s0)
+    assert host(q)[1, :10].tolist() == [127, 2, 4, -2, 0, 0, 2, 126, -127, 0]
+    assert host(sx)[0] == 0.0 and host(q)[3, 7] == -127
+
+
+@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (37, 640, 3), (300, 1536, 8), (1024, 4096, 7), (48, 12288, 2),
+                                   (64, 2048, 16)])
+def test_gemv_i8(tw, n, k, m):
+    t, s, x = gen(n, k, m, seed=n * 7 + m)
+    q, sx = tw.tern_quantize_i8(dev(x))
+    q0, s0 = oracle.quantize_i8(x)
+    assert np.array_equal(host(q), q0)
+    p = gpu_pack(tw, t, s)
+    import torch
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemv_i8(p, n, k, q, sx, acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
+
+
+def test_gemv_i8_unit_scale_full_shape(tw):
+    """Scales 1.0 and s_x = 1: y is an exact integer (< 2^24), so bit-exact y
+    proves the int32 block accumulators through the production path at a
+    full 8B gate shape."""
+    n, k = 12288, 4096
+    rng = np.random.default_rng(21)
+    t = synth.gen_ternary(rng, n, k)
+    s1 = np.full((n, k // 128), 0x3C00, np.uint16)
+    q = rng.integers(-127, 128, size=(2, k)).astype(np.int8)
+    y = host(tw.tern_gemv_i8(gpu_pack(tw, t, s1), n, k, dev(q), dev(np.ones(2, np.float32))))
+    want = (q.astype(np.int64) @ t.T.astype(np.int64)).astype(np.float32)
+    assert np.array_equal(y, want)
+
+
+@pytest.mark.parametrize("v,k,m", [(300, 512, 1), (151936 // 64, 1024, 3), (1000, 4096, 8), (77, 128, 16)])
+def test_head(tw, v, k, m):
+    rng = np.random.default_rng(v + k)
+    w, rs = synth.gen_head(rng, rng, v, k)
+    x = synth.gen_x_bf16(rng, m, k)
+    y = host(tw.i8_head_gemv(dev(w), dev(rs), dev(x)))
+    y64, _ = oracle.head_bf16(w, rs, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    q, sx = oracle.quantize_i8(x)
+    import torch
+    acc = torch.empty((m, v), dtype=torch.int32, device="cuda")
+    yi = host(tw.i8_head_gemv_i8(dev(w), dev(rs), dev(q), dev(sx), acc=acc))
+    acc0, yi64, _ = oracle.head_i8(w, rs, q, sx)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(yi, yi64) <= TOL
+
+
+def test_head_one_hot_exact(tw):
+    rng = np.random.default_rng(2)
+    v, k = 500, 1024
+    w, rs = synth.gen_head(rng, rng, v, k)
+    e = np.zeros((1, k), np.float32)
+    e[0, 333] = 1.0
+    y = host(tw.i8_head_gemv(dev(w), dev(rs), dev(synth.f32_to_bf16_bits(e))))
+    assert np.array_equal(y[0], (rs.astype(np.float64) * w[:, 333]).astype(np.float32))
+
+
+@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (40, 640, 64), (256, 1536, 130), (200, 2048, 300)])
+def test_prefill_small(tw, n, k, m):
+    t, s, x = gen(n, k, m, seed=n + m)
+    q0, s0 = oracle.quantize_i8(x)
+    import torch
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(gpu_pack(tw, t, s), n, k, dev(q0), dev(s0), acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_prefill_full_shape_sampled(tw, proj):
+    """8B gate / down shape at M=512: sampled output rows against the oracle,
+    plus the GEMV-i8 kernel on the same rows (same arithmetic)."""
+    n, k = synth.SHAPES_8B[proj]
+    m = 512
+    t, s, x = gen(n, k, m, seed=42)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
+    rows = np.random.default_rng(1).choice(n, 64, replace=False)
+    _, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0[:64], s0[:64], rows=rows, want_acc=False)
+    assert oracle.rel_l2(y[:64, rows], y64) <= TOL
+    # the remaining rows agree with the small-M kernel
+    y8 = host(tw.tern_gemv_i8(p, n, k, dev(q0[500:508]), dev(s0[500:508])))
+    assert oracle.rel_l2(y[500:508], y8) <= TOL
+
+
+@pytest.mark.parametrize("proj", list(synth.PROJ))
+def test_full_8b_shapes_sampled(tw, proj):
+    """Every 8B linear shape at M=1 (the decode configuration) in the launch
+    configuration the benchmark uses: all rows vs brute force over a sampled
+    set computed by the oracle."""
+    n, k = synth.SHAPES_8B[proj]
+    lin = synth.Linear(2, 1, proj, n, k, synth.P_ZERO_SPARSE if proj in ("gate", "down") else synth.P_ZERO,
+                       synth.P_PLUS_SPARSE if proj in ("gate", "down") else synth.P_PLUS)
+    t, s, x = synth.linear_inputs(lin)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemv(p, n, k, dev(x)))
+    rows = np.random.default_rng(0).choice(n, 256, replace=False)
+    y64, _ = oracle.gemv_bf16(oracle.pack(t[rows], s[rows]), 256, k, x)
+    assert oracle.rel_l2(y[0, rows], y64[0]) <= TOL
+    # occupancy of the packed blob matches the drawn states
+    c = host(tw.tern_stats(p, n, k))
+    assert c[0] == np.count_nonzero(t) and c[1] == np.count_nonzero(t < 0) and c[2] == 0
