@@ -1,0 +1,273 @@
+"""Benchmark of the ternary decode hot path on one MI355X.
+
+One step = one token-equivalent of single-stream decode at the Qwen3-8B
+shapes: the 252 ternary linears of 36 layers (q, k, v, o, gate, up, down;
+M = 1, bf16 activations, fp32 outputs) followed by the untied int8 output
+head 151936 x 4096.  Every linear has its own packed weights and its own
+activation vector, all resident in HBM before timing (2.47 GB per step, ten
+times the 256 MB last-level cache, so every step streams from HBM).
+
+Prints one JSON line: whole-step throughput in GB/s of algorithmic bytes
+(packed weights + scales + activations + outputs), the token-equivalent time,
+the roofline of the dominant kernel (the M=1 ternary GEMV) from HIP events
+around each of its launches, and the CPU oracle timed on a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--compose separate|fused] [--no-graph]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "ternary GEMV GB/s and % HBM peak, 8B shapes M=1; us/token-equiv"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2], help="1 = 0.6B shapes, 2 = 8B shapes")
+    ap.add_argument("--compose", default="separate", choices=["separate", "fused"],
+                    help="separate: one launch per linear (252 + head); fused: q|k|v and gate|up share a launch")
+    ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of replaying a hipGraph")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Step:
+    """Device-resident inputs of one token-equivalent and the launch list."""
+
+    def __init__(self, tw, synth, config: int, compose: str):
+        import torch
+        self.torch = torch
+        self.tw = tw
+        lins = synth.model_linears(config)
+        self.launches = []          # (kind, packed/W, n, k, x, y, bytes, label)
+        t0 = time.time()
+
+        def gen(lin):
+            return synth.linear_inputs(lin)
+
+        # generate on host threads a layer at a time, pack on the GPU
+        per_layer = 7
+        groups = [lins[i:i + per_layer] for i in range(0, len(lins), per_layer)]
+        for gi, group in enumerate(groups):
+            data = synth.parallel_map(gen, group)
+            by = {lin.proj: (lin, d) for lin, d in zip(group, data)}
+            if compose == "fused":
+                units = [("qkv", ["q", "k", "v"]), ("o", ["o"]), ("gateup", ["gate", "up"]), ("down", ["down"])]
+            else:
+                units = [(p, [p]) for p in synth.PROJ]
+            for label, projs in units:
+                ts = np.concatenate([by[p][1][0] for p in projs], axis=0)
+                ss = np.concatenate([by[p][1][1] for p in projs], axis=0)
+                x = by[projs[0]][1][2]
+                n, k = ts.shape
+                t_dev = torch.from_numpy(ts).cuda()
+                s_dev = torch.from_numpy(ss.view(np.int16)).cuda()
+                packed = tw.tern_pack(t_dev, s_dev)
+                del t_dev, s_dev
+                x_dev = torch.from_numpy(x.view(np.int16)).cuda()
+                y_dev = torch.empty((1, n), dtype=torch.float32, device="cuda")
+                nbytes = tw.tern_packed_bytes(n, k) + 2 * k + 4 * n
+                self.launches.append(("tern", packed, n, k, x_dev, y_dev, nbytes, label))
+            if gi % 6 == 5:
+                log(f"generated and packed {gi + 1}/{len(groups)} layers ({time.time() - t0:.1f}s)")
+        w, rs, xh = synth.head_inputs(config)
+        v, k = w.shape
+        self.head = (torch.from_numpy(w).cuda(), torch.from_numpy(rs).cuda(),
+                     torch.from_numpy(xh.view(np.int16)).cuda(), torch.empty((1, v), dtype=torch.float32,
+                                                                             device="cuda"))
+        self.head_bytes = v * k + 4 * v + 2 * k + 4 * v
+        self.tern_bytes = sum(l[6] for l in self.launches)
+        self.bytes = self.tern_bytes + self.head_bytes
+        torch.cuda.synchronize()
+        log(f"inputs resident: {self.bytes / 1e9:.3f} GB algorithmic per step, "
+            f"{len(self.launches)} ternary launches + head ({time.time() - t0:.1f}s)")
+
+    def run_tern(self, label=None):
+        tw = self.tw
+        for (_, p, n, k, x, y, _, lab) in self.launches:
+            if label is None or lab == label:
+                tw.tern_gemv(p, n, k, x, y=y)
+
+    def run_head(self):
+        w, rs, xh, yh = self.head
+        self.tw.i8_head_gemv(w, rs, xh, y=yh)
+
+    def run(self):
+        self.run_tern()
+        self.run_head()
+
+
+def capture(torch, fn):
+    """Capture fn's launches (on a side stream, as torch requires) into a hipGraph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+def time_replays(torch, g, reps: int) -> float:
+    """Mean milliseconds per replay from HIP events on the replay stream."""
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def cpu_baseline(synth, oracle, target_s: float):
+    """The fp64 oracle's bf16 GEMV over the seven linears of one 8B layer (the
+    same generated inputs as the GPU step's layer 0, packed by the oracle),
+    repeated until target_s of CPU time is spent."""
+    lins = [l for l in synth.model_linears(2) if l.layer == 0]
+    work = []
+    for lin in lins:
+        t, s, x = synth.linear_inputs(lin)
+        work.append((oracle.pack(t, s), lin.n, lin.k, x))
+    done_bytes, t_used, reps = 0, 0.0, 0
+    while t_used < target_s:
+        for (p, n, k, x) in work:
+            t0 = time.perf_counter()
+            oracle.gemv_bf16(p, n, k, x)
+            t_used += time.perf_counter() - t0
+            done_bytes += p.size + 2 * k + 4 * n
+        reps += 1
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle bf16 GEMV over the 7 linears of one 8B layer, {reps} pass(es), "
+                      f"{done_bytes / 1e6:.1f} MB algorithmic in {t_used:.1f} s",
+            "seconds": round(t_used, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
+              f"MI355X; see the design notes for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import torch
+    import ternary_weight_decode_amd as tw
+    from ternary_weight_decode_amd import synth
+    assert torch.cuda.is_available(), "no GPU"
+    tw.lib()
+
+    step = Step(tw, synth, args.config, args.compose)
+
+    # ---- timed region: exactly K whole steps, hipGraph replay unless --no-graph
+    graph = None if args.no_graph else capture(torch, step.run)
+
+    def one():
+        if graph is not None:
+            graph.replay()
+        else:
+            step.run()
+
+    for _ in range(args.warmup):
+        one()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        one()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall / args.steps * 1e3
+    value = step.bytes * args.steps / wall / 1e9
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+
+    # ---- dominant kernel (the M=1 ternary GEMV): HIP events around graph
+    # replays of only its launches, on the stream they run on.  The per-launch
+    # time includes the in-graph gap between consecutive kernels, so it is an
+    # upper bound on the kernel's own duration.
+    reps = max(5, min(args.steps, 20))
+    g_tern = capture(torch, step.run_tern)
+    tern_ms = time_replays(torch, g_tern, reps)
+    n_tern = len(step.launches)
+    achieved = step.tern_bytes / (tern_ms * 1e-3) / 1e9
+    g_head = capture(torch, step.run_head)
+    head_ms = time_replays(torch, g_head, reps)
+    shapes = {}
+    for label in dict.fromkeys(l[7] for l in step.launches):
+        ls = [l for l in step.launches if l[7] == label]
+        gl = capture(torch, lambda lab=label: step.run_tern(lab))
+        ms = time_replays(torch, gl, reps) / len(ls)
+        b = ls[0][6]
+        shapes[label] = {"n_k": [ls[0][2], ls[0][3]], "launches": len(ls), "us": round(ms * 1e3, 2),
+                         "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                         "pct_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
+        del gl
+    layer_us = tern_ms / (n_tern / (4 if args.compose == "fused" else 7)) * 1e3
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        oracle.lib()
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(synth, oracle, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": ("qwen3-8b-shapes token-equivalent: 252 ternary GEMVs (36 layers x q,k,v,o,gate,up,"
+                                "down) + int8 head 151936x4096, M=1" if args.config == 2 else
+                                "qwen3-0.6b-shapes token-equivalent: 196 ternary GEMVs + tied int8 head "
+                                "151936x1024, M=1"),
+                   "compose": args.compose, "graph": graph is not None,
+                   "bytes_per_step": int(step.bytes)},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "us_per_token_equiv": round(ms_per_step * 1e3, 2),
+        "ternary_us_per_token_equiv": round(tern_ms * 1e3, 2),
+        "us_per_layer": round(layer_us, 2),
+        "head": {"us": round(head_ms * 1e3, 2),
+                 "GB/s": round(step.head_bytes / (head_ms * 1e-3) / 1e9, 1)},
+        "per_shape": shapes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "gemv_bf16_fast_kernel<1,*> (tern_gemv, M=1)",
+                     "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
+                     "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
+                     "launches_per_step": n_tern,
+                     "timing": "HIP events around hipGraph replays of the step's ternary GEMV launches"},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -28,13 +28,13 @@ struct PlaneTile {
 // Load the plane words and scales a lane (row r, word g) needs from k-tile kt
 // of row tile rt.  nbq = blocks in this k-tile (4 except a narrower last tile).
 __device__ __forceinline__ PlaneTile load_plane_tile(const uint32_t* __restrict__ words,
-                                                     const uint16_t* __restrict__ scales, int64_t rt, int64_t kt,
-                                                     int64_t nb, int r, int g)
+                                                     const uint16_t* __restrict__ scales, int64_t rt, int kt,
+                                                     int nb, int r, int g)
 {
     PlaneTile p;
     const int64_t wb = tile_word_base(rt, kt, nb);
     const int64_t sb = tile_scale_base(rt, kt, nb);
-    const int nbq = (int)(nb - 4 * kt < 4 ? nb - 4 * kt : 4);
+    const int nbq = nb - 4 * kt < 4 ? nb - 4 * kt : 4;
     if (nbq == 4) {
         p.nz = ld_nt16(words + wb + (int64_t)((0 * 4 + g) * 16 + r) * 4);
         p.sg = ld_nt16(words + wb + (int64_t)((1 * 4 + g) * 16 + r) * 4);
@@ -174,6 +174,156 @@ __global__ __launch_bounds__(512) void gemv_bf16_kernel(const uint8_t* __restric
     }
 }
 
+// Decode with 64-bit shifts: c2 rotated right by one bit puts both code words'
+// pairs at even bit positions, so one 64-bit shift of {c2', c1} aligns pair j
+// of both words at bits (14, 15) / (30, 31): 7 shifts + 16 masks per 32
+// weights instead of 15 rotates + 16 masks.
+__device__ __forceinline__ void decode_bf16_x2(uint32_t N, uint32_t S, u32x4 (&B)[4])
+{
+    const CodeWords c = interleave(N, S);
+    const uint32_t c2r = __builtin_amdgcn_alignbit(c.c2, c.c2, 1);
+    const uint64_t d = ((uint64_t)c2r << 32) | c.c1;
+    uint32_t o[16];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+        const uint64_t sh = d << (14 - 2 * p);
+        o[2 * p] = (uint32_t)sh & 0xC000C000u;          // weights (4p, 4p+1)
+        o[2 * p + 1] = (uint32_t)(sh >> 32) & 0xC000C000u;  // weights (4p+2, 4p+3)
+    }
+    B[0] = u32x4{o[0], o[1], o[2], o[3]};
+    B[1] = u32x4{o[4], o[5], o[6], o[7]};
+    B[2] = u32x4{o[8], o[9], o[10], o[11]};
+    B[3] = u32x4{o[12], o[13], o[14], o[15]};
+}
+
+// Two blocks of one k-tile with their MFMA chains interleaved.  xa points at
+// the staged activations of this lane's row at the first block's k + 32*g.
+template <int MT>
+__device__ __forceinline__ void bf16_block_pair(uint32_t n0, uint32_t s0, uint32_t n1, uint32_t s1, float sc0,
+                                                float sc1, const uint16_t* xa, f32x4& acc)
+{
+    u32x4 B0[4], B1[4];
+    decode_bf16_x2(n0, s0, B0);
+    decode_bf16_x2(n1, s1, B1);
+    f32x4 d0 = {0.f, 0.f, 0.f, 0.f}, d1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        d0 = mfma_bf16(*(const u32x4*)(xa + 8 * c), B0[c], d0);
+        d1 = mfma_bf16(*(const u32x4*)(xa + kBlockK + 8 * c), B1[c], d1);
+    }
+#pragma unroll
+    for (int i = 0; i < (MT < 4 ? MT : 4); ++i) {
+        acc[i] = __builtin_fmaf(sc0, d0[i], acc[i]);
+        acc[i] = __builtin_fmaf(sc1, d1[i], acc[i]);
+    }
+}
+
+template <int MT>
+__device__ __forceinline__ void bf16_block(uint32_t n0, uint32_t s0, float sc0, const uint16_t* xa, f32x4& acc)
+{
+    u32x4 B0[4];
+    decode_bf16_x2(n0, s0, B0);
+    f32x4 d0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) d0 = mfma_bf16(*(const u32x4*)(xa + 8 * c), B0[c], d0);
+#pragma unroll
+    for (int i = 0; i < (MT < 4 ? MT : 4); ++i) acc[i] = __builtin_fmaf(sc0, d0[i], acc[i]);
+}
+
+// One k-tile of a lane's row: xt points at the staged activations of this
+// lane's row at k = 512*kt + 32*g.  Scales are halved because decoded
+// weights are 2*t.
+template <int MT>
+__device__ __forceinline__ void bf16_tile(const PlaneTile& t, const uint16_t* xt, int nbq, f32x4& acc)
+{
+    if (nbq == 4) {
+        bf16_block_pair<MT>(t.nz[0], t.sg[0], t.nz[1], t.sg[1], 0.5f * tile_scale(t, 0), 0.5f * tile_scale(t, 1),
+                            xt, acc);
+        bf16_block_pair<MT>(t.nz[2], t.sg[2], t.nz[3], t.sg[3], 0.5f * tile_scale(t, 2), 0.5f * tile_scale(t, 3),
+                            xt + 2 * kBlockK, acc);
+    } else {
+        for (int bq = 0; bq < nbq; ++bq)
+            bf16_block<MT>(t.nz[bq], t.sg[bq], 0.5f * tile_scale(t, bq), xt + bq * kBlockK, acc);
+    }
+}
+
+// Fast path: all of x[0..M)[0..K) fits in LDS.  A workgroup owns one 16-row
+// tile; wave w takes k-tiles w, w+nw, ...  Each wave keeps TPW k-tiles in
+// flight (a register ring refilled as tiles are consumed), and the first TPW
+// loads are issued before the activation staging so HBM latency overlaps it.
+// Index arithmetic stays in 32 bits inside the loops (64-bit divisions are
+// emulated and cost microseconds at these sizes).
+template <int MT, int TPW>
+__global__ __launch_bounds__(512) void gemv_bf16_fast_kernel(const uint8_t* __restrict__ packed, int64_t N,
+                                                             int64_t K, const uint16_t* __restrict__ x, int M,
+                                                             float* __restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int nw = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int64_t rt = blockIdx.x;
+    const int nb = (int)(K / kBlockK), nkt = (nb + 3) >> 2;
+    const uint32_t* words = (const uint32_t*)packed;
+    const uint16_t* scales = (const uint16_t*)(packed + scale_region_offset(N, K));
+    const int xstride = (int)K + 8;
+    uint16_t* xs = (uint16_t*)smem;
+    float* red = (float*)(smem + (size_t)M * xstride * 2);
+    const int mrow = r < M ? r : M - 1;
+
+    // this wave's k-tiles: kt_j = wave + j*nw, j < J
+    const int J = wave < nkt ? (nkt - 1 - wave) / nw + 1 : 0;
+    PlaneTile slot[TPW];
+#pragma unroll
+    for (int s = 0; s < TPW; ++s)
+        if (s < J) slot[s] = load_plane_tile(words, scales, rt, wave + s * nw, nb, r, g);
+
+    {
+        const int per_row = (int)(K >> 3);
+        const int units = M * per_row;
+        for (int u = threadIdx.x; u < units; u += blockDim.x) {
+            const int m = u / per_row, c8 = u - m * per_row;
+            *(u32x4*)(xs + m * xstride + 8 * c8) = *(const u32x4*)(x + (int64_t)m * K + 8 * c8);
+        }
+    }
+    __syncthreads();
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const uint16_t* xrow = xs + mrow * xstride + 32 * g;
+    for (int j0 = 0; j0 < J; j0 += TPW) {
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int j = j0 + s;
+            if (j < J) {
+                const int kt = wave + j * nw;
+                const int nbq = nb - 4 * kt < 4 ? nb - 4 * kt : 4;
+                bf16_tile<MT>(slot[s], xrow + kt * kTileK, nbq, acc);
+                if (j + TPW < J) slot[s] = load_plane_tile(words, scales, rt, kt + TPW * nw, nb, r, g);
+            }
+        }
+    }
+
+    // cross-wave sum of the rows that exist: element (i, lane) holds output
+    // (m = 4*(lane/16) + i, n = lane % 16)
+    constexpr int NI = MT < 4 ? MT : 4;
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+    if (lane < lanes_used) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) red[(wave * NI + i) * 64 + lane] = acc[i];
+    }
+    __syncthreads();
+    const int64_t n0 = rt * kTileRows;
+    for (int e = threadIdx.x; e < NI * 64; e += blockDim.x) {
+        const int i = e >> 6, l = e & 63;
+        const int m = 4 * (l >> 4) + i, n = l & 15;
+        if (l < lanes_used && m < M && n0 + n < N) {
+            float sum = 0.f;
+            for (int w = 0; w < nw; ++w) sum += red[(w * NI + i) * 64 + l];
+            y[(int64_t)m * N + n0 + n] = sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ int8
 
 template <int MT>
@@ -290,14 +440,47 @@ static int pick_chunk(int64_t K, int64_t M, int64_t bytes_per_elem)
     return (int)(kr < cap ? kr : cap);
 }
 
+static constexpr int64_t kFastLds = 64 * 1024;      // LDS budget of the fast path
+
+// waves per workgroup and k-tiles in flight per wave for the fast path
+static void pick_fast(int64_t N, int64_t nkt, int& nw, int& tpw)
+{
+    (void)N;
+    nw = nkt >= 8 ? 8 : (nkt >= 4 ? 4 : (int)(nkt < 1 ? 1 : nkt));
+    const int64_t per = (nkt + nw - 1) / nw;
+    tpw = per >= 3 ? 3 : (int)(per < 1 ? 1 : per);
+}
+
+template <int MT>
+static void launch_fast_mt(int tpw, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const uint8_t* packed,
+                           int64_t N, int64_t K, const uint16_t* x, int M, float* y)
+{
+    if (tpw == 1) gemv_bf16_fast_kernel<MT, 1><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
+    else if (tpw == 2) gemv_bf16_fast_kernel<MT, 2><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
+    else gemv_bf16_fast_kernel<MT, 3><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
+}
+
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
     const int64_t nkt = (K / kBlockK + 3) / 4;
-    const int nw = pick_waves(nkt);
+    const dim3 grid((unsigned)((N + 15) / 16));
+    int nw, tpw;
+    pick_fast(N, nkt, nw, tpw);
+    const size_t fast_lds = (size_t)M * (K + 8) * 2 + (size_t)nw * 4 * 64 * 4;
+    if (fast_lds <= (size_t)kFastLds) {
+        const dim3 block(64 * nw);
+        if (M == 1) launch_fast_mt<1>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
+        else if (M == 2) launch_fast_mt<2>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
+        else if (M <= 4) launch_fast_mt<4>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
+        else launch_fast_mt<16>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
+        return hipGetLastError();
+    }
+    // general path: activations staged in k-chunks
+    const int nwc = pick_waves(nkt);
     const int kc = pick_chunk(K, M, 2);
-    const size_t lds = (size_t)M * (kc + 8) * 2 + (size_t)nw * 256 * 4;
-    const dim3 grid((unsigned)((N + 15) / 16)), block(64 * nw);
+    const size_t lds = (size_t)M * (kc + 8) * 2 + (size_t)nwc * 256 * 4;
+    const dim3 block(64 * nwc);
     if (M == 1) gemv_bf16_kernel<1><<<grid, block, lds, stream>>>(packed, N, K, x, (int)M, y, kc);
     else if (M == 2) gemv_bf16_kernel<2><<<grid, block, lds, stream>>>(packed, N, K, x, (int)M, y, kc);
     else if (M <= 4) gemv_bf16_kernel<4><<<grid, block, lds, stream>>>(packed, N, K, x, (int)M, y, kc);
