@@ -34,11 +34,15 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", type=int, default=2, choices=[1, 2], help="1 = 0.6B shapes, 2 = 8B shapes")
-    ap.add_argument("--compose", default="separate", choices=["separate", "fused"],
+    ap.add_argument("--compose", default="fused", choices=["separate", "fused"],
                     help="separate: one launch per linear (252 + head); fused: q|k|v and gate|up share a launch")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of replaying a hipGraph")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "copy"],
+                    help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
+                         "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
+                         "copy: plain 256 MiB device copies (reference for memory-counter scaling)")
     return ap.parse_args()
 
 
@@ -140,6 +144,29 @@ def time_replays(torch, g, reps: int) -> float:
     return e0.elapsed_time(e1) / reps
 
 
+TRAFFIC_PROFILE = "profiles/tern_gemv_m1_8b_token_fused_hbm_traffic.txt"
+
+
+def measured_traffic(root: str, compose: str):
+    """HBM bytes per ternary-GEMV launch from the committed memory-counter
+    summary, or None when it does not apply: other composition, or the GEMV
+    kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    if compose != "fused":
+        return None
+    try:
+        text = open(os.path.join(root, TRAFFIC_PROFILE)).read()
+        src = open(os.path.join(root, "ternary_weight_decode_amd", "csrc", "tern_gemv.hip"), "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"ternary GEMV per launch .*?: HBM ([0-9.]+) MB", text)
+    h = re.search(r"sha256 \(tern_gemv.hip\) at measurement: ([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(float(m.group(1)) * 1e6)
+
+
 def cpu_baseline(synth, oracle, target_s: float):
     """The fp64 oracle's bf16 GEMV over the seven linears of one 8B layer (the
     same generated inputs as the GPU step's layer 0, packed by the oracle),
@@ -164,6 +191,77 @@ def cpu_baseline(synth, oracle, target_s: float):
             "seconds": round(t_used, 2)}
 
 
+INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
+
+
+def shape_inputs(tw, synth, torch, proj, m, seed=7):
+    """Packed weights of one 8B-shape linear (layer 0) and m bf16 activation rows."""
+    n, k = synth.SHAPES_8B[proj]
+    lin = synth.Linear(2, 0, proj, n, k, synth.P_ZERO, synth.P_PLUS)
+    t, s, _ = synth.linear_inputs(lin)
+    x = synth.gen_x_bf16(np.random.default_rng(seed), m, k)
+    packed = tw.tern_pack(torch.from_numpy(t).cuda(), torch.from_numpy(s.view(np.int16)).cuda())
+    return n, k, packed, torch.from_numpy(x.view(np.int16)).cuda()
+
+
+def rotate_copies(torch, packed, total_bytes=1 << 30):
+    """Distinct copies of a packed matrix so consecutive launches stream from HBM."""
+    reps = max(1, min(256, total_bytes // max(1, packed.numel())))
+    return [packed] + [packed.clone() for _ in range(reps - 1)]
+
+
+def mode_smallm(args, tw, synth, torch):
+    """Speculative-verify sweep: every 8B shape at M in {1,2,4,7,8}, bf16 and int8 activations;
+    weights rotate over >= 1 GB of copies so each launch reads HBM."""
+    out = []
+    for proj in synth.PROJ:
+        n, k, packed, x8 = shape_inputs(tw, synth, torch, proj, 8)
+        copies = rotate_copies(torch, packed)
+        for m in (1, 2, 4, 7, 8):
+            x = x8[:m].contiguous()
+            q, sx = tw.tern_quantize_i8(x)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            for variant in ("bf16", "int8"):
+                def run():
+                    for p in copies:
+                        if variant == "bf16":
+                            tw.tern_gemv(p, n, k, x, y=y)
+                        else:
+                            tw.tern_gemv_i8(p, n, k, q, sx, y=y)
+                g = capture(torch, run)
+                ms = time_replays(torch, g, 5) / len(copies)
+                act = m * (2 * k if variant == "bf16" else k + 4)
+                nbytes = tw.tern_packed_bytes(n, k) + act + 4 * m * n
+                out.append({"proj": proj, "n_k": [n, k], "M": m, "act": variant, "us": round(ms * 1e3, 2),
+                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+                del g
+        del copies
+    print(json.dumps({"mode": "smallm", "unit": "GB/s of weights+activations+outputs per launch, cold HBM",
+                      "rows": out}), flush=True)
+
+
+def mode_prefill(args, tw, synth, torch):
+    """int8-MFMA prefill at M in {64, 512, 2048} on the 8B gate/up/down shapes: TOP/s counting
+    2*M*N*K dense operations (the matrix cores execute the zero weights too)."""
+    out = []
+    for proj in ("gate", "up", "down"):
+        n, k, packed, _ = shape_inputs(tw, synth, torch, proj, 1)
+        for m in (64, 512, 2048):
+            x = torch.from_numpy(synth.gen_x_bf16(np.random.default_rng(m), m, k).view(np.int16)).cuda()
+            q, sx = tw.tern_quantize_i8(x)
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            g = capture(torch, lambda: [tw.tern_gemm_prefill(packed, n, k, q, sx, y=y) for _ in range(10)])
+            ms = time_replays(torch, g, 5) / 10
+            ops = 2.0 * m * n * k
+            tops = ops / (ms * 1e-3) / 1e12
+            nbytes = tw.tern_packed_bytes(n, k) + m * (k + 4) + 4 * m * n
+            out.append({"proj": proj, "n_k": [n, k], "M": m, "us": round(ms * 1e3, 2), "TOP/s": round(tops, 1),
+                        "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1),
+                        "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+            del g
+    print(json.dumps({"mode": "prefill", "peak_tops": INT8_PEAK_TOPS, "rows": out}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -177,6 +275,19 @@ def main():
     from ternary_weight_decode_amd import synth
     assert torch.cuda.is_available(), "no GPU"
     tw.lib()
+    if args.mode == "smallm":
+        return mode_smallm(args, tw, synth, torch)
+    if args.mode == "prefill":
+        return mode_prefill(args, tw, synth, torch)
+    if args.mode == "copy":
+        src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"mode": "copy", "bytes_read_per_copy": src.numel(), "bytes_written_per_copy": dst.numel(),
+                          "copies": 4}), flush=True)
+        return
 
     step = Step(tw, synth, args.config, args.compose)
 
@@ -258,7 +369,8 @@ def main():
                  "GB/s": round(step.head_bytes / (head_ms * 1e-3) / 1e9, 1)},
         "per_shape": shapes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(root, args.compose),
                      "kernel": "gemv_bf16_fast_kernel<1,*> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),

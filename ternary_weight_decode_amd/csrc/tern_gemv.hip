@@ -247,36 +247,50 @@ __device__ __forceinline__ void bf16_tile(const PlaneTile& t, const uint16_t* xt
     }
 }
 
-// Fast path: all of x[0..M)[0..K) fits in LDS.  A workgroup owns one 16-row
-// tile; wave w takes k-tiles w, w+nw, ...  Each wave keeps TPW k-tiles in
-// flight (a register ring refilled as tiles are consumed), and the first TPW
-// loads are issued before the activation staging so HBM latency overlaps it.
-// Index arithmetic stays in 32 bits inside the loops (64-bit divisions are
-// emulated and cost microseconds at these sizes).
+// Fast path: all of x[0..M)[0..K) fits in LDS.  Persistent workgroups: the
+// grid is sized to what stays resident, and workgroup b handles row tiles
+// b, b + G, b + 2G, ...  Within a row tile, wave w takes k-tiles w, w+nw, ...
+// (nw <= number of k-tiles, so every wave has work in every row tile).  Each
+// wave runs a ring of TPW plane tiles over its whole (row tile, k-tile)
+// sequence, so loads for the next row tile are in flight while the current
+// one is reduced.  Activations are staged once per workgroup after the first
+// loads are issued.  Per row tile the waves' fp32 partials meet in LDS
+// (double-buffered, one barrier per row tile) and are summed in wave order.
+// Index arithmetic stays in 32 bits (64-bit divisions are emulated).
 template <int MT, int TPW>
 __global__ __launch_bounds__(512) void gemv_bf16_fast_kernel(const uint8_t* __restrict__ packed, int64_t N,
                                                              int64_t K, const uint16_t* __restrict__ x, int M,
                                                              float* __restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = MT < 4 ? MT : 4;            // accumulator rows in use per lane
     const int nw = blockDim.x >> 6;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t rt = blockIdx.x;
     const int nb = (int)(K / kBlockK), nkt = (nb + 3) >> 2;
+    const int nrt = (int)((N + 15) >> 4);
     const uint32_t* words = (const uint32_t*)packed;
     const uint16_t* scales = (const uint16_t*)(packed + scale_region_offset(N, K));
     const int xstride = (int)K + 8;
     uint16_t* xs = (uint16_t*)smem;
-    float* red = (float*)(smem + (size_t)M * xstride * 2);
+    float* red = (float*)(smem + (size_t)M * xstride * 2);   // [2][nw][NI][64]
     const int mrow = r < M ? r : M - 1;
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
 
-    // this wave's k-tiles: kt_j = wave + j*nw, j < J
-    const int J = wave < nkt ? (nkt - 1 - wave) / nw + 1 : 0;
+    const int rt0 = blockIdx.x, rstep = gridDim.x;
+    const int nmy = rt0 < nrt ? (nrt - 1 - rt0) / rstep + 1 : 0;
+    const int Jw = (nkt - 1 - wave) / nw + 1;                 // k-tiles per row tile for this wave
+    const int U = nmy * Jw;
+
     PlaneTile slot[TPW];
+    int li = 0, lj = 0;                                       // next (row tile, k-tile) to load
 #pragma unroll
-    for (int s = 0; s < TPW; ++s)
-        if (s < J) slot[s] = load_plane_tile(words, scales, rt, wave + s * nw, nb, r, g);
+    for (int s = 0; s < TPW; ++s) {
+        if (s < U) {
+            slot[s] = load_plane_tile(words, scales, rt0 + li * rstep, wave + lj * nw, nb, r, g);
+            if (++lj == Jw) { lj = 0; ++li; }
+        }
+    }
 
     {
         const int per_row = (int)(K >> 3);
@@ -290,36 +304,40 @@ __global__ __launch_bounds__(512) void gemv_bf16_fast_kernel(const uint8_t* __re
 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const uint16_t* xrow = xs + mrow * xstride + 32 * g;
-    for (int j0 = 0; j0 < J; j0 += TPW) {
+    int pi = 0, pj = 0;                                       // (row tile, k-tile) being processed
+    for (int u0 = 0; u0 < U; u0 += TPW) {
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
-            const int j = j0 + s;
-            if (j < J) {
-                const int kt = wave + j * nw;
+            if (u0 + s < U) {
+                const int kt = wave + pj * nw;
                 const int nbq = nb - 4 * kt < 4 ? nb - 4 * kt : 4;
                 bf16_tile<MT>(slot[s], xrow + kt * kTileK, nbq, acc);
-                if (j + TPW < J) slot[s] = load_plane_tile(words, scales, rt, kt + TPW * nw, nb, r, g);
-            }
-        }
-    }
-
-    // cross-wave sum of the rows that exist: element (i, lane) holds output
-    // (m = 4*(lane/16) + i, n = lane % 16)
-    constexpr int NI = MT < 4 ? MT : 4;
-    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
-    if (lane < lanes_used) {
+                if (u0 + s + TPW < U) {
+                    slot[s] = load_plane_tile(words, scales, rt0 + li * rstep, wave + lj * nw, nb, r, g);
+                    if (++lj == Jw) { lj = 0; ++li; }
+                }
+                if (++pj == Jw) {                             // row tile pi complete in this wave
+                    float* rb = red + (pi & 1) * nw * NI * 64;
+                    if (lane < lanes_used) {
 #pragma unroll
-        for (int i = 0; i < NI; ++i) red[(wave * NI + i) * 64 + lane] = acc[i];
-    }
-    __syncthreads();
-    const int64_t n0 = rt * kTileRows;
-    for (int e = threadIdx.x; e < NI * 64; e += blockDim.x) {
-        const int i = e >> 6, l = e & 63;
-        const int m = 4 * (l >> 4) + i, n = l & 15;
-        if (l < lanes_used && m < M && n0 + n < N) {
-            float sum = 0.f;
-            for (int w = 0; w < nw; ++w) sum += red[(w * NI + i) * 64 + l];
-            y[(int64_t)m * N + n0 + n] = sum;
+                        for (int i = 0; i < NI; ++i) rb[(wave * NI + i) * 64 + lane] = acc[i];
+                    }
+                    __syncthreads();
+                    const int64_t n0 = (int64_t)(rt0 + pi * rstep) * kTileRows;
+                    for (int e = threadIdx.x; e < NI * 64; e += blockDim.x) {
+                        const int i = e >> 6, l = e & 63;
+                        const int m = 4 * (l >> 4) + i, n = l & 15;
+                        if (l < lanes_used && m < M && n0 + n < N) {
+                            float sum = 0.f;
+                            for (int w = 0; w < nw; ++w) sum += rb[(w * NI + i) * 64 + l];
+                            y[(int64_t)m * N + n0 + n] = sum;
+                        }
+                    }
+                    acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                    pj = 0;
+                    ++pi;
+                }
+            }
         }
     }
 }
@@ -443,40 +461,70 @@ static int pick_chunk(int64_t K, int64_t M, int64_t bytes_per_elem)
 static constexpr int64_t kFastLds = 64 * 1024;      // LDS budget of the fast path
 
 // waves per workgroup and k-tiles in flight per wave for the fast path
-static void pick_fast(int64_t N, int64_t nkt, int& nw, int& tpw)
+// (nw never exceeds the number of k-tiles, so every wave works on every row tile)
+static void pick_fast(int64_t nkt, int& nw, int& tpw)
 {
-    (void)N;
     nw = nkt >= 8 ? 8 : (nkt >= 4 ? 4 : (int)(nkt < 1 ? 1 : nkt));
     const int64_t per = (nkt + nw - 1) / nw;
     tpw = per >= 3 ? 3 : (int)(per < 1 ? 1 : per);
 }
 
-template <int MT>
-static void launch_fast_mt(int tpw, dim3 grid, dim3 block, size_t lds, hipStream_t stream, const uint8_t* packed,
-                           int64_t N, int64_t K, const uint16_t* x, int M, float* y)
+static int device_cus()
 {
-    if (tpw == 1) gemv_bf16_fast_kernel<MT, 1><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
-    else if (tpw == 2) gemv_bf16_fast_kernel<MT, 2><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
-    else gemv_bf16_fast_kernel<MT, 3><<<grid, block, lds, stream>>>(packed, N, K, x, M, y);
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    return cus;
+}
+
+// Workgroups that stay resident at once for this kernel instance (the grid of
+// the persistent fast path); falls back to one per row tile on any error.
+template <typename F>
+static int64_t resident_grid(F kern, int block, size_t lds, int64_t nrt)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, block, lds) != hipSuccess || per_cu <= 0)
+        return nrt;
+    const int64_t cap = (int64_t)per_cu * device_cus();
+    return nrt < cap ? nrt : cap;
+}
+
+template <int MT, int TPW>
+static hipError_t launch_fast(int nw, size_t lds, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
+                              const uint16_t* x, int M, float* y)
+{
+    const int64_t nrt = (N + 15) / 16;
+    const int block = 64 * nw;
+    const int64_t grid = resident_grid(gemv_bf16_fast_kernel<MT, TPW>, block, lds, nrt);
+    gemv_bf16_fast_kernel<MT, TPW><<<dim3((unsigned)grid), dim3(block), lds, stream>>>(packed, N, K, x, M, y);
+    return hipGetLastError();
+}
+
+template <int MT>
+static hipError_t launch_fast_mt(int tpw, int nw, size_t lds, hipStream_t stream, const uint8_t* packed, int64_t N,
+                                 int64_t K, const uint16_t* x, int M, float* y)
+{
+    if (tpw == 1) return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
+    if (tpw == 2) return launch_fast<MT, 2>(nw, lds, stream, packed, N, K, x, M, y);
+    return launch_fast<MT, 3>(nw, lds, stream, packed, N, K, x, M, y);
 }
 
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
     const int64_t nkt = (K / kBlockK + 3) / 4;
-    const dim3 grid((unsigned)((N + 15) / 16));
     int nw, tpw;
-    pick_fast(N, nkt, nw, tpw);
-    const size_t fast_lds = (size_t)M * (K + 8) * 2 + (size_t)nw * 4 * 64 * 4;
+    pick_fast(nkt, nw, tpw);
+    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);   // accumulator rows of the instance (NI)
+    const size_t fast_lds = (size_t)M * (K + 8) * 2 + (size_t)2 * nw * ni * 64 * 4;
     if (fast_lds <= (size_t)kFastLds) {
-        const dim3 block(64 * nw);
-        if (M == 1) launch_fast_mt<1>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
-        else if (M == 2) launch_fast_mt<2>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
-        else if (M <= 4) launch_fast_mt<4>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
-        else launch_fast_mt<16>(tpw, grid, block, fast_lds, stream, packed, N, K, x, (int)M, y);
-        return hipGetLastError();
+        if (M == 1) return launch_fast_mt<1>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
+        if (M == 2) return launch_fast_mt<2>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
+        if (M <= 4) return launch_fast_mt<4>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
+        return launch_fast_mt<16>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
     }
     // general path: activations staged in k-chunks
+    const dim3 grid((unsigned)((N + 15) / 16));
     const int nwc = pick_waves(nkt);
     const int kc = pick_chunk(K, M, 2);
     const size_t lds = (size_t)M * (kc + 8) * 2 + (size_t)nwc * 256 * 4;

@@ -6,6 +6,7 @@
 //
 // One wave owns a 16-row tile of W over the whole K (no cross-wave
 // reduction); a workgroup of 4 waves shares the activations staged in LDS.
+// Each wave keeps a ring of loads in flight (depth chosen by the launcher).
 // Each lane streams 32 contiguous bytes of its row per 128-k unit, so a
 // wave's load pair covers 16 full 128-byte lines.  bf16 path: int8 -> f32 via
 // the byte-select convert (exact) -> bf16 pair by taking the high halves
@@ -38,7 +39,12 @@ __device__ __forceinline__ void head_decode_bf16(const u32x4& lo, const u32x4& h
     }
 }
 
-template <bool kInt8>
+// Head kernel: wave q of the grid owns row tiles q, q + Q, q + 2Q, ...
+// (Q = total waves; the launcher gives every wave one row tile) over the
+// whole K and keeps a ring of TPW 128-k units (32 bytes per lane each) in
+// flight, across row-tile boundaries when a wave has several.  Activations (all of K, or a chunk of it when
+// M*K is large) are staged in LDS once per workgroup.
+template <bool kInt8, int TPW>
 __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W, const float* __restrict__ rs,
                                                    int64_t V, int64_t K, const void* __restrict__ act,
                                                    const float* __restrict__ s_x, int M, float* __restrict__ y,
@@ -47,74 +53,93 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
     extern __shared__ __align__(16) uint8_t smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
-    const int64_t v0 = ((int64_t)blockIdx.x * kHeadWaves + wave) * kTileRows;
-    const int64_t vrow = v0 + r < V ? v0 + r : V - 1;       // rows past V re-read the last row (dropped)
     const int ebytes = kInt8 ? 1 : 2;
     const int astride = kc * ebytes + 16;                  // bytes per staged activation row
     const int mrow = r < M ? r : M - 1;
-    const int8_t* wrow = W + vrow * K + 32 * g;
-    const int64_t nunit = K / kBlockK;
-    const int64_t upc = kc / kBlockK;                      // 128-k units per chunk
+    const int nunit = (int)(K / kBlockK);                  // 128-k units per row
+    const int upc = kc / kBlockK;                          // units per staged chunk
+    const int nchunks = (nunit + upc - 1) / upc;
+    const int64_t nrt = (V + 15) >> 4;
+    const int64_t q0 = (int64_t)blockIdx.x * kHeadWaves + wave, qstep = (int64_t)gridDim.x * kHeadWaves;
+    const int nmy = q0 < nrt ? (int)((nrt - 1 - q0) / qstep + 1) : 0;
 
-    f32x4 accf = {0.f, 0.f, 0.f, 0.f};
-    i32x4 acci = {0, 0, 0, 0};
-    u32x4 cl, ch, nl, nh;
-    const bool active = v0 < V;
-    if (active) {
-        cl = ld_nt16(wrow);
-        ch = ld_nt16(wrow + 16);
-    }
-    int64_t u = 0;
-    const int64_t nchunks = (nunit + upc - 1) / upc;
-    for (int64_t c = 0; c < nchunks; ++c) {
-        const int64_t k0 = c * kc;
-        const int64_t kcl = (K - k0) < kc ? (K - k0) : kc;
-        if (c > 0) __syncthreads();
+    // units of this wave in order: (row tile i, unit j), j fastest; chunk c covers units [c*upc, (c+1)*upc)
+    // With one chunk (kc >= K) the ring spans row tiles; with several chunks the
+    // chunk loop is outermost and every row tile is revisited per chunk.
+    for (int c = 0; c < nchunks; ++c) {
+        const int j_lo = c * upc, j_hi = (c + 1) * upc < nunit ? (c + 1) * upc : nunit;
+        const int Jc = j_hi - j_lo;
+        const int U = nmy * Jc;
+        u32x4 lo[TPW], hi[TPW];
+        int li = 0, lj = 0;
+        auto load = [&](int s) {
+            int64_t v = (q0 + li * qstep) * kTileRows + r;
+            v = v < V ? v : V - 1;                         // rows past V re-read the last row (outputs dropped)
+            const int8_t* p = W + v * K + (int64_t)(j_lo + lj) * kBlockK + 32 * g;
+            lo[s] = ld_nt16(p);
+            hi[s] = ld_nt16(p + 16);
+            if (++lj == Jc) { lj = 0; ++li; }
+        };
+#pragma unroll
+        for (int s = 0; s < TPW; ++s)
+            if (s < U) load(s);
+
+        if (c > 0) __syncthreads();                        // previous chunk's activations no longer read
         {
-            const int64_t per_row = kcl * ebytes / 16;
-            const int64_t units = (int64_t)M * per_row;
+            const int64_t k0 = (int64_t)j_lo * kBlockK;
+            const int per_row = Jc * kBlockK * ebytes / 16;
+            const int units = M * per_row;
             const uint8_t* src = (const uint8_t*)act;
-            for (int64_t i = threadIdx.x; i < units; i += blockDim.x) {
-                const int64_t m = i / per_row, c16 = i % per_row;
-                *(u32x4*)(smem + m * astride + 16 * c16) = *(const u32x4*)(src + (m * K + k0) * ebytes + 16 * c16);
+            for (int i = threadIdx.x; i < units; i += blockDim.x) {
+                const int m = i / per_row, c16 = i - m * per_row;
+                *(u32x4*)(smem + m * astride + 16 * c16) = *(const u32x4*)(src + ((int64_t)m * K + k0) * ebytes + 16 * c16);
             }
         }
         __syncthreads();
-        const int64_t u_end = (c + 1) * upc < nunit ? (c + 1) * upc : nunit;
-        if (active) {
-            for (; u < u_end; ++u) {
-                if (u + 1 < nunit) {
-                    nl = ld_nt16(wrow + (u + 1) * kBlockK);
-                    nh = ld_nt16(wrow + (u + 1) * kBlockK + 16);
-                }
-                const uint8_t* arow = smem + mrow * astride + ((u * kBlockK - k0) + 32 * g) * ebytes;
-                if constexpr (kInt8) {
-                    acci = mfma_i8(*(const u32x4*)(arow), cl, acci);
-                    acci = mfma_i8(*(const u32x4*)(arow + 16), ch, acci);
-                } else {
-                    u32x4 B[4];
-                    head_decode_bf16(cl, ch, B);
+
+        f32x4 accf = {0.f, 0.f, 0.f, 0.f};
+        i32x4 acci = {0, 0, 0, 0};
+        int pi = 0, pj = 0;
+        for (int u0 = 0; u0 < U; u0 += TPW) {
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) accf = mfma_bf16(*(const u32x4*)(arow + 16 * s), B[s], accf);
-                }
-                cl = nl;
-                ch = nh;
-            }
-        }
-    }
-    if (!active) return;
-    const int64_t v = v0 + r;
-    if (v >= V) return;
-    const float sv = rs[v];
+            for (int s = 0; s < TPW; ++s) {
+                if (u0 + s < U) {
+                    const uint8_t* arow = smem + mrow * astride + (pj * kBlockK + 32 * g) * ebytes;
+                    if constexpr (kInt8) {
+                        acci = mfma_i8(*(const u32x4*)(arow), lo[s], acci);
+                        acci = mfma_i8(*(const u32x4*)(arow + 16), hi[s], acci);
+                    } else {
+                        u32x4 B[4];
+                        head_decode_bf16(lo[s], hi[s], B);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int m = 4 * g + i;
-        if (m < M) {
-            if constexpr (kInt8) {
-                y[(int64_t)m * V + v] = sv * s_x[m] * (float)acci[i];
-                if (acc_dbg) acc_dbg[(int64_t)m * V + v] = acci[i];
-            } else {
-                y[(int64_t)m * V + v] = sv * accf[i];
+                        for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(arow + 16 * t), B[t], accf);
+                    }
+                    if (u0 + s + TPW < U) load(s);
+                    if (++pj == Jc) {                      // row tile pi: this chunk's part is complete
+                        const int64_t v = (q0 + pi * qstep) * kTileRows + r;
+                        if (v < V) {
+                            const float sv = rs[v];
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const int m = 4 * g + i;
+                                if (m < M) {
+                                    float* yp = y + (int64_t)m * V + v;
+                                    if constexpr (kInt8) {
+                                        // with several chunks, logits add per-chunk products; acc_dbg adds exactly
+                                        *yp = (c == 0 ? 0.0f : *yp) + sv * s_x[m] * (float)acci[i];
+                                        if (acc_dbg) acc_dbg[(int64_t)m * V + v] = (c == 0 ? 0 : acc_dbg[(int64_t)m * V + v]) + acci[i];
+                                    } else {
+                                        *yp = (c == 0 ? 0.0f : *yp) + sv * accf[i];
+                                    }
+                                }
+                            }
+                        }
+                        accf = f32x4{0.f, 0.f, 0.f, 0.f};
+                        acci = i32x4{0, 0, 0, 0};
+                        pj = 0;
+                        ++pi;
+                    }
+                }
             }
         }
     }
@@ -127,24 +152,32 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
     return (int)(K < cap ? K : cap);
 }
 
+template <bool kInt8>
+static hipError_t launch_head(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
+                              const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    constexpr int kTpw = 1;   // deeper rings cost more VGPRs than they win (measured: 1 -> 137 us, 2 -> 152, 4 -> 198 on the 8B head)
+    const int kc = head_chunk(K, M, kInt8 ? 1 : 2);
+    const size_t lds = (size_t)M * (kc * (kInt8 ? 1 : 2) + 16);
+    // one row tile per wave: a row tile is 16 x K bytes (64 KB at K = 4096), so
+    // a static multi-tile assignment leaves a serial tail; retiring workgroups
+    // balance the load instead
+    const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
+    head_kernel<kInt8, kTpw><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(W, rs, V, K, act, s_x,
+                                                                                             (int)M, y, acc, kc);
+    return hipGetLastError();
+}
+
 hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x, int64_t M,
                             float* y, hipStream_t stream)
 {
-    const int kc = head_chunk(K, M, 2);
-    const size_t lds = (size_t)M * (kc * 2 + 16);
-    const unsigned grid = (unsigned)((V + 16 * kHeadWaves - 1) / (16 * kHeadWaves));
-    head_kernel<false><<<grid, 64 * kHeadWaves, lds, stream>>>(W, rs, V, K, x, nullptr, (int)M, y, nullptr, kc);
-    return hipGetLastError();
+    return launch_head<false>(W, rs, V, K, x, nullptr, M, y, nullptr, stream);
 }
 
 hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                           const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
-    const int kc = head_chunk(K, M, 1);
-    const size_t lds = (size_t)M * (kc + 16);
-    const unsigned grid = (unsigned)((V + 16 * kHeadWaves - 1) / (16 * kHeadWaves));
-    head_kernel<true><<<grid, 64 * kHeadWaves, lds, stream>>>(W, rs, V, K, q, s_x, (int)M, y, acc, kc);
-    return hipGetLastError();
+    return launch_head<true>(W, rs, V, K, q, s_x, M, y, acc, stream);
 }
 
 }  // namespace tern
