@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 1
+#define TERN_ABI_VERSION 2
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -158,6 +158,56 @@ int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t 
  *   acc_dbg NULL or int32 [M][N][K/128] (debug; small shapes). */
 int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
                       float* y, int32_t* acc_dbg, void* stream);
+
+/* ---- dependent GEMV chain (single-stream decode in one launch) ----
+ *
+ * A token runs its linears one after another, each reading an activation
+ * that the previous ones produced; per token the time above the pure DRAM
+ * bound sits at the roughly one hundred kernel boundaries and in the
+ * dependency chain inside each small kernel ([P2] section "뉴트리노 엔진:
+ * 토큰 하나의 시간은 어디로 가는가").  tern_gemv_chain runs a whole chain
+ * of M = 1 ternary GEMVs in one persistent launch, with a device-wide barrier
+ * between steps and the next step's weights streaming in during it.
+ *
+ * Step p computes, with the arithmetic of tern_gemv at M = 1:
+ *   y[n] = sum_b scale[n][b] * sum_{k in block b} t[n][k] * x[k]
+ *   y_bf16[n] = y[n] rounded to bf16, nearest-even (when y_bf16 != NULL)
+ * x of a step may be (part of) y_bf16 of an earlier step: the chain orders
+ * the steps.  It must not overlap the step's own outputs. */
+typedef struct tern_chain_step {
+    const void* packed;   /* tern_pack blob of W [N][K], 16-byte aligned     */
+    int64_t N;            /* output rows, >= 1                                */
+    int64_t K;            /* input features, 512 <= K <= 16384, K % 512 == 0  */
+    const uint16_t* x;    /* bf16 bits [K], 16-byte aligned                   */
+    float* y;             /* fp32 [N], 4-byte aligned                         */
+    uint16_t* y_bf16;     /* bf16 bits [N], 2-byte aligned, or NULL           */
+} tern_chain_step;
+
+/* Workspace bytes for a chain of nsteps steps (-1 if nsteps < 0).  The
+ * workspace holds the grid-barrier counters and the device copy of the
+ * plan.  The caller allocates it (256-byte aligned), fills it with zeros once
+ * before its first use, and then leaves it to the library; it may be reused
+ * for any number of plans and runs.  Runs that share a workspace must not
+ * overlap in time.  A 32-bit count of aborted waits sits at byte offset 1544
+ * (0 in normal operation; a workspace with a nonzero count runs nothing until
+ * it is zero-filled again). */
+int64_t tern_chain_workspace_bytes(int64_t nsteps);
+
+/* Validate nsteps host-side step descriptors and enqueue the write of their
+ * device plan into the workspace.  Errors: TERN_E_NULL / TERN_E_ALIGN /
+ * TERN_E_SHAPE for a bad step, a step whose x overlaps its own outputs, a
+ * workspace smaller than tern_chain_workspace_bytes(nsteps), or a step with
+ * more than 256 (row tile, 512-k tile) units per CU.  The steps array is
+ * read before the call returns. */
+int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspace, int64_t workspace_bytes,
+                    void* stream);
+
+/* Run the first nsteps steps of the plan in the workspace (no more than were
+ * planned).  One workgroup per CU stays resident for the whole launch
+ * (cooperative launch); the call fails with TERN_E_HIP if the device cannot
+ * hold them.  Every wait inside is bounded (a stalled run ends after seconds
+ * and counts an error, see tern_chain_workspace_bytes). */
+int tern_gemv_chain(void* workspace, int64_t nsteps, void* stream);
 
 #ifdef __cplusplus
 }

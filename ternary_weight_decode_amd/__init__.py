@@ -10,7 +10,8 @@ fails to load, every call raises.
 
 Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 ``tern_gemv``, ``tern_gemv_i8``, ``i8_head_gemv``, ``i8_head_gemv_i8``,
-``tern_gemm_prefill``, ``tern_packed_bytes``.
+``tern_gemm_prefill``, ``tern_packed_bytes``, and the dependent-GEMV chain
+``tern_chain_workspace_bytes``, ``tern_chain_plan``, ``tern_gemv_chain``.
 """
 from __future__ import annotations
 
@@ -20,11 +21,19 @@ import os
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtern.so")
 MAX_M_GEMV = 16
 SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
-           "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill")
+           "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
+           "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain")
+_INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
+               "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain")
 
 _lib = None
 _i64 = ctypes.c_int64
 _p = ctypes.c_void_p
+
+
+class TernChainStep(ctypes.Structure):
+    """struct tern_chain_step of include/tern.h."""
+    _fields_ = [("packed", _p), ("N", _i64), ("K", _i64), ("x", _p), ("y", _p), ("y_bf16", _p)]
 
 
 def lib():
@@ -48,7 +57,11 @@ def lib():
         L.i8_head_gemv.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
         L.i8_head_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.tern_gemm_prefill.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
-        for name in SYMBOLS[4:]:
+        L.tern_chain_workspace_bytes.restype = _i64
+        L.tern_chain_workspace_bytes.argtypes = [_i64]
+        L.tern_chain_plan.argtypes = [ctypes.POINTER(TernChainStep), _i64, _p, _i64, _p]
+        L.tern_gemv_chain.argtypes = [_p, _i64, _p]
+        for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -182,3 +195,48 @@ def tern_gemm_prefill(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=N
     _check("tern_gemm_prefill", lib().tern_gemm_prefill(_ptr(packed), n, k, _ptr(q), _ptr(s_x), m, _ptr(y),
                                                         _ptr(acc), _stream(stream)))
     return y
+
+
+def tern_chain_workspace_bytes(nsteps: int) -> int:
+    return int(lib().tern_chain_workspace_bytes(nsteps))
+
+
+def tern_chain_workspace(nsteps: int, device="cuda"):
+    """A zero-filled workspace for chains of up to nsteps steps."""
+    import torch
+    nbytes = tern_chain_workspace_bytes(nsteps)
+    if nbytes < 0:
+        _check("tern_chain_workspace_bytes", 2)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
+def tern_chain_plan(steps, workspace, stream=None):
+    """steps: sequence of (packed, N, K, x, y, y_bf16 or None); x bf16 bits [K],
+    y fp32 [N], y_bf16 bf16 bits [N].  Writes the device plan into workspace."""
+    import torch
+    arr = (TernChainStep * max(1, len(steps)))()
+    for i, (packed, n, k, x, y, yb) in enumerate(steps):
+        _need(packed, "packed", (torch.uint8,))
+        _need(x, "x", (torch.int16, torch.uint16, torch.bfloat16))
+        _need(y, "y", (torch.float32,))
+        if yb is not None:
+            _need(yb, "y_bf16", (torch.int16, torch.uint16, torch.bfloat16))
+        if x.numel() != k or y.numel() != n or (yb is not None and yb.numel() != n):
+            raise RuntimeError(f"tern_chain_plan: step {i} tensor sizes do not match N={n}, K={k}")
+        arr[i] = TernChainStep(packed.data_ptr(), n, k, x.data_ptr(), y.data_ptr(),
+                               None if yb is None else yb.data_ptr())
+    _need(workspace, "workspace", (torch.uint8,), 1)
+    _check("tern_chain_plan", lib().tern_chain_plan(arr, len(steps), _ptr(workspace), workspace.numel(),
+                                                    _stream(stream)))
+
+
+def tern_gemv_chain(workspace, nsteps: int, stream=None):
+    import torch
+    _need(workspace, "workspace", (torch.uint8,), 1)
+    _check("tern_gemv_chain", lib().tern_gemv_chain(_ptr(workspace), nsteps, _stream(stream)))
+
+
+def tern_chain_errors(workspace) -> int:
+    """Count of aborted waits recorded in a chain workspace (0 in normal operation)."""
+    import torch
+    return int(workspace[1544:1548].view(torch.int32).item())

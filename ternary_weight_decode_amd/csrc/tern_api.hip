@@ -10,6 +10,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "../../include/tern.h"
 #include "tern_launch.h"
@@ -186,6 +187,69 @@ int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q,
     if (rc) return rc;
     if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
     return finish(tern::launch_prefill((const uint8_t*)packed, N, K, q, s_x, M, y, acc_dbg, (hipStream_t)stream));
+}
+
+int64_t tern_chain_workspace_bytes(int64_t nsteps)
+{
+    if (nsteps < 0) return -1;
+    return tern::kChainPlanOffset + nsteps * (int64_t)sizeof(tern::ChainStep);
+}
+
+int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspace, int64_t workspace_bytes,
+                    void* stream)
+{
+    if (nsteps < 0 || nsteps > (int64_t)1 << 24) return TERN_E_SHAPE;
+    if (!workspace || (nsteps > 0 && !steps)) return TERN_E_NULL;
+    if (((uintptr_t)workspace & 255u) != 0) return TERN_E_ALIGN;
+    if (workspace_bytes < tern_chain_workspace_bytes(nsteps)) return TERN_E_SHAPE;
+    std::vector<tern::ChainStep> plan((size_t)nsteps);
+    for (int64_t p = 0; p < nsteps; ++p) {
+        const tern_chain_step& st = steps[p];
+        if (st.N < 1 || st.K < 512 || st.K % 512 != 0 || st.K > tern::kChainMaxK) return TERN_E_SHAPE;
+        if (!st.packed || !st.x || !st.y) return TERN_E_NULL;
+        if (!aligned16(st.packed) || !aligned16(st.x) || !aligned4(st.y) || ((uintptr_t)st.y_bf16 & 1u))
+            return TERN_E_ALIGN;
+        const uintptr_t x0 = (uintptr_t)st.x, x1 = x0 + (uintptr_t)st.K * 2;
+        auto overlaps = [&](const void* a, int64_t bytes) {
+            const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)bytes;
+            return a && a0 < x1 && x0 < a1;
+        };
+        if (overlaps(st.y, st.N * 4) || overlaps(st.y_bf16, st.N * 2)) return TERN_E_SHAPE;
+        bool coherent = false;
+        for (int64_t q = 0; q < p && !coherent; ++q)
+            coherent = overlaps(steps[q].y, steps[q].N * 4) || overlaps(steps[q].y_bf16, steps[q].N * 2);
+        tern::ChainStep& d = plan[(size_t)p];
+        d = tern::ChainStep{};
+        d.packed = (const uint8_t*)st.packed;
+        d.x = st.x;
+        d.y = st.y;
+        d.y_bf16 = st.y_bf16;
+        d.N = st.N;
+        d.K = st.K;
+        d.x_coherent = coherent ? 1u : 0u;
+    }
+    int rc = check_device();
+    if (rc) return rc;
+    int grid = 0;
+    hipError_t e = tern::chain_grid(&grid);
+    if (e != hipSuccess) return hip_fail(e);
+    for (const tern::ChainStep& d : plan) {
+        const int64_t nrt = (d.N + 15) / 16, nkt = (d.K / 128 + 3) / 4;
+        const int64_t per_cu = (nrt + grid - 1) / grid;
+        if (per_cu * nkt * 16 > tern::kChainRedMax) return TERN_E_SHAPE;
+    }
+    return finish(tern::launch_chain_plan(plan.data(), (int)nsteps, (uint8_t*)workspace, (hipStream_t)stream));
+}
+
+int tern_gemv_chain(void* workspace, int64_t nsteps, void* stream)
+{
+    if (nsteps < 0 || nsteps > (int64_t)1 << 24) return TERN_E_SHAPE;
+    if (!workspace) return TERN_E_NULL;
+    if (((uintptr_t)workspace & 255u) != 0) return TERN_E_ALIGN;
+    if (nsteps == 0) return TERN_OK;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_chain((uint8_t*)workspace, (int)nsteps, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -60,16 +60,6 @@ __device__ __forceinline__ CodeWords interleave(uint32_t N, uint32_t S)
     return c;
 }
 
-// bf16 pair j (j = 0..15) of a 32-weight word: low half = weight 2j, high
-// half = weight 2j+1, each equal to 2*t as bf16 (0x4000 = +2, 0xC000 = -2,
-// 0 = 0; a non-canonical sign bit without a nonzero bit gives -0).
-template <int J>
-__device__ __forceinline__ uint32_t bf16_pair(const CodeWords& c)
-{
-    const uint32_t src = (J & 1) ? c.c2 : c.c1;
-    return rotl32(src, 14 - J) & 0xC000C000u;
-}
-
 // int8 quad d (d = 0..7) of a 32-weight word: bytes are 64*t of weights
 // (2d, 2d+16, 2d+1, 2d+17).  Requires canonical planes.
 template <int D>
@@ -126,6 +116,21 @@ __device__ __forceinline__ u32x4 ld_nt16(const void* p)
 __device__ __forceinline__ u32x2 ld_nt8(const void* p)
 {
     return __builtin_nontemporal_load((const u32x2*)p);
+}
+
+// Pointers known to address global memory.  Loads through them compile to
+// global (not flat) instructions, which count only against the vector-memory
+// counter, so waiting for LDS traffic never waits for them.
+#define TERN_GLOBAL __attribute__((address_space(1)))
+
+__device__ __forceinline__ u32x4 ld_nt16(const TERN_GLOBAL void* p)
+{
+    return __builtin_nontemporal_load((const TERN_GLOBAL u32x4*)p);
+}
+
+__device__ __forceinline__ u32x2 ld_nt8(const TERN_GLOBAL void* p)
+{
+    return __builtin_nontemporal_load((const TERN_GLOBAL u32x2*)p);
 }
 
 }  // namespace tern

@@ -25,6 +25,32 @@ hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t
                             float* y, hipStream_t stream);
 hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                           const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
+// ---- dependent GEMV chain (persistent, one workgroup per CU) ----
+// Workspace layout: grid-barrier counters at 0, header (magic, planned step
+// count, error count) at kChainHeaderOffset, plan entries at kChainPlanOffset.
+constexpr int kChainWaves = 16;                   // 1 control + 15 compute waves
+constexpr int kChainMaxK = 16384;                 // activation elements staged per step
+constexpr int kChainRedMax = 4096;                // unit partial floats per workgroup and step
+constexpr size_t kChainLds = 96 * 1024;           // more than half the CU's LDS: one workgroup per CU
+constexpr int64_t kChainHeaderOffset = 1536;
+constexpr int64_t kChainPlanOffset = 4096;
+constexpr uint32_t kChainMagic = 0x7E4C3A11u;
+constexpr int kChainPlanBatch = 16;
+
+struct ChainStep {                                // 64 bytes
+    const uint8_t* packed;
+    const uint16_t* x;
+    float* y;
+    uint16_t* y_bf16;
+    int64_t N, K;
+    uint32_t x_coherent;                          // x overlaps an output of an earlier step
+    uint32_t pad[3];
+};
+
+hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, hipStream_t stream);
+hipError_t launch_chain(uint8_t* ws, int nsteps, hipStream_t stream);
+hipError_t chain_grid(int* grid);
+
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream);
 

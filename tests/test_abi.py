@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 1
+    assert L.tern_abi_version() == 2
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -105,3 +105,52 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(tw, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         tw.lib()
+
+
+def _steps(*specs):
+    """ctypes array of tern_chain_step from (packed, N, K, x, y, y_bf16) tuples of ints/None."""
+    arr = (tw.TernChainStep * len(specs))()
+    for i, sp in enumerate(specs):
+        arr[i] = tw.TernChainStep(*sp)
+    return arr
+
+
+def test_chain_workspace_bytes():
+    assert tw.tern_chain_workspace_bytes(0) == 4096
+    assert tw.tern_chain_workspace_bytes(144) == 4096 + 144 * 64
+    assert tw.tern_chain_workspace_bytes(-1) == -1
+
+
+def test_chain_plan_rejects_bad_steps_before_any_device_call():
+    L = tw.lib()
+    ws, nb = ctypes.c_void_p(0x100000), 1 << 20
+    good = (0x10000, 4096, 4096, 0x20000, 0x30000, 0x40000)
+    assert L.tern_chain_plan(_steps(good), 1, None, nb, None) == E_NULL
+    assert L.tern_chain_plan(None, 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps(good), 1, ctypes.c_void_p(0x100010), nb, None) == E_ALIGN   # 256-byte
+    assert L.tern_chain_plan(_steps(good), 1, ws, 4096 + 63, None) == E_SHAPE                   # too small
+    assert L.tern_chain_plan(_steps(good), -1, ws, nb, None) == E_SHAPE
+    bad_k = [(0x10000, 4096, 640, 0x20000, 0x30000, None),      # K % 512
+             (0x10000, 4096, 256, 0x20000, 0x30000, None),      # K < 512
+             (0x10000, 4096, 16896, 0x20000, 0x30000, None),    # K > 16384
+             (0x10000, 0, 4096, 0x20000, 0x30000, None)]        # N < 1
+    for st in bad_k:
+        assert L.tern_chain_plan(_steps(good, st), 2, ws, nb, None) == E_SHAPE, st
+    assert L.tern_chain_plan(_steps((None, 16, 512, 0x20000, 0x30000, None)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, None, 0x30000, None)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, None, None)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10008, 16, 512, 0x20000, 0x30000, None)), 1, ws, nb, None) == E_ALIGN
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20008, 0x30000, None)), 1, ws, nb, None) == E_ALIGN
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30002, None)), 1, ws, nb, None) == E_ALIGN
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30000, 0x40001)), 1, ws, nb, None) == E_ALIGN
+    # a step's x may not overlap its own outputs (y at x + 16 bytes, y_bf16 ending inside x)
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x20010, None)), 1, ws, nb, None) == E_SHAPE
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30000, 0x1FFF0)), 1, ws, nb, None) == E_SHAPE
+
+
+def test_chain_run_argument_errors():
+    L = tw.lib()
+    assert L.tern_gemv_chain(None, 1, None) == E_NULL
+    assert L.tern_gemv_chain(ctypes.c_void_p(0x100010), 1, None) == E_ALIGN
+    assert L.tern_gemv_chain(ctypes.c_void_p(0x100000), -1, None) == E_SHAPE
+    assert L.tern_gemv_chain(ctypes.c_void_p(0x100000), 0, None) == E_OK
