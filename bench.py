@@ -12,7 +12,13 @@ Prints one JSON line: whole-step throughput in GB/s of algorithmic bytes
 the roofline of the dominant kernel (the M=1 ternary GEMV) from HIP events
 around each of its launches, and the CPU oracle timed on a bounded sample.
 
-    python bench.py [--steps K] [--warmup W] [--compose separate|fused] [--no-graph]
+    python bench.py [--steps K] [--warmup W] [--engine graph|chain] [--compose separate|fused] [--no-graph]
+
+Engines: "chain" runs the step's ternary linears as one persistent launch of
+tern_gemv_chain, each linear reading an earlier one's output and waiting only
+for it, the next weights streaming meanwhile, and then the head; "graph"
+replays a hipGraph of one tern_gemv launch per linear (each with its own
+input vector) and the head.
 """
 from __future__ import annotations
 
@@ -37,6 +43,8 @@ def parse():
     ap.add_argument("--compose", default="fused", choices=["separate", "fused"],
                     help="separate: one launch per linear (252 + head); fused: q|k|v and gate|up share a launch")
     ap.add_argument("--no-graph", action="store_true", help="launch the step eagerly instead of replaying a hipGraph")
+    ap.add_argument("--engine", default="graph", choices=["graph", "chain"],
+                    help="chain: one persistent tern_gemv_chain launch per step; graph: one launch per linear")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "copy"],
@@ -115,6 +123,25 @@ class Step:
         self.run_tern()
         self.run_head()
 
+    # ---- persistent-chain engine: the same linears, in order, as one launch.
+    # Each linear after the first reads the output of the nearest earlier one
+    # with at least K outputs (its first K values, rounded to bf16), the way
+    # decode feeds one linear into the next (attention and the gated
+    # activation, which sit between them in the model, are not part of this
+    # path), so every step truly waits for its input.
+    def plan_chain(self):
+        tw = self.tw
+        specs = []
+        for i, (_, p, n, k, x, y, _, _) in enumerate(self.launches):
+            src = next((j for j in range(i - 1, -1, -1) if self.launches[j][2] >= k), -1)
+            specs.append((p, n, k, x.view(-1) if src < 0 else None, src, y.view(-1)))
+        ws = tw.tern_chain_workspace(specs)
+        tw.tern_chain_plan(specs, ws)
+        return ws, len(specs)
+
+    def run_chain(self, ws, n):
+        self.tw.tern_gemv_chain(ws, n)
+
 
 def capture(torch, fn):
     """Capture fn's launches (on a side stream, as torch requires) into a hipGraph."""
@@ -162,6 +189,62 @@ def measured_traffic(root: str, compose: str):
         return None
     m = re.search(r"ternary GEMV per launch .*?: HBM ([0-9.]+) MB", text)
     h = re.search(r"sha256 \(tern_gemv.hip\) at measurement: ([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return int(float(m.group(1)) * 1e6)
+
+
+def time_calls(torch, fn, reps: int) -> float:
+    """Mean milliseconds per call of fn (launches only) from HIP events on the current stream."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def roofline(root, args, achieved, tern_ms, n_tern, step):
+    base = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    if args.engine == "chain":
+        base.update({"traffic": measured_chain_traffic(root, args.compose),
+                     "kernel": f"chain_kernel (tern_gemv_chain, M=1, {n_tern} dependent steps per launch)",
+                     "avg_launch_us": round(tern_ms * 1e3, 3),
+                     "avg_bytes_per_launch": int(step.tern_bytes),
+                     "launches_per_step": 1,
+                     "us_per_linear_step": round(tern_ms / n_tern * 1e3, 3),
+                     "timing": "HIP events around back-to-back launches of the step's ternary chain"})
+    else:
+        base.update({"traffic": measured_traffic(root, args.compose),
+                     "kernel": "gemv_bf16_fast_kernel<1,*> (tern_gemv, M=1)",
+                     "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
+                     "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
+                     "launches_per_step": n_tern,
+                     "timing": "HIP events around hipGraph replays of the step's ternary GEMV launches"})
+    return base
+
+
+CHAIN_TRAFFIC_PROFILE = "profiles/tern_chain_8b_token_fused_hbm_traffic.txt"
+
+
+def measured_chain_traffic(root: str, compose: str):
+    """HBM bytes per chain launch from the committed memory-counter summary, or
+    None when the chain kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    if compose != "fused":
+        return None
+    try:
+        text = open(os.path.join(root, CHAIN_TRAFFIC_PROFILE)).read()
+        src = open(os.path.join(root, "ternary_weight_decode_amd", "csrc", "tern_chain.hip"), "rb").read()
+    except OSError:
+        return None
+    m = re.search(r"chain per launch .*?: HBM ([0-9.]+) MB", text)
+    h = re.search(r"sha256 \(tern_chain.hip\) at measurement: ([0-9a-f]{64})", text)
     if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
         return None
     return int(float(m.group(1)) * 1e6)
@@ -290,12 +373,20 @@ def main():
         return
 
     step = Step(tw, synth, args.config, args.compose)
+    chain = args.engine == "chain"
+    if chain:
+        ws, n_chain = step.plan_chain()
 
-    # ---- timed region: exactly K whole steps, hipGraph replay unless --no-graph
-    graph = None if args.no_graph else capture(torch, step.run)
+    # ---- timed region: exactly K whole steps
+    graph = None
+    if not chain and not args.no_graph:
+        graph = capture(torch, step.run)
 
     def one():
-        if graph is not None:
+        if chain:
+            step.run_chain(ws, n_chain)
+            step.run_head()
+        elif graph is not None:
             graph.replay()
         else:
             step.run()
@@ -311,28 +402,37 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     value = step.bytes * args.steps / wall / 1e9
     log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step, {value:.1f} GB/s")
+    if chain:
+        errs = tw.tern_chain_errors(ws)
+        assert errs == 0, f"chain workspace recorded {errs} aborted waits"
 
-    # ---- dominant kernel (the M=1 ternary GEMV): HIP events around graph
-    # replays of only its launches, on the stream they run on.  The per-launch
-    # time includes the in-graph gap between consecutive kernels, so it is an
-    # upper bound on the kernel's own duration.
+    # ---- dominant kernel: HIP events on the stream it runs on.  Graph engine:
+    # graph replays of only the ternary GEMV launches (the per-launch time
+    # includes the in-graph gap, an upper bound on the kernel's duration).
+    # Chain engine: back-to-back launches of the whole chain.
     reps = max(5, min(args.steps, 20))
-    g_tern = capture(torch, step.run_tern)
-    tern_ms = time_replays(torch, g_tern, reps)
     n_tern = len(step.launches)
+    if chain:
+        tern_ms = time_calls(torch, lambda: step.run_chain(ws, n_chain), reps)
+    else:
+        g_tern = capture(torch, step.run_tern)
+        tern_ms = time_replays(torch, g_tern, reps)
     achieved = step.tern_bytes / (tern_ms * 1e-3) / 1e9
     g_head = capture(torch, step.run_head)
     head_ms = time_replays(torch, g_head, reps)
-    shapes = {}
-    for label in dict.fromkeys(l[7] for l in step.launches):
-        ls = [l for l in step.launches if l[7] == label]
-        gl = capture(torch, lambda lab=label: step.run_tern(lab))
-        ms = time_replays(torch, gl, reps) / len(ls)
-        b = ls[0][6]
-        shapes[label] = {"n_k": [ls[0][2], ls[0][3]], "launches": len(ls), "us": round(ms * 1e3, 2),
-                         "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
-                         "pct_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
-        del gl
+    # per launch kind (graph engine only: inside the chain the kinds overlap)
+    shapes = None
+    if not chain:
+        shapes = {}
+        for label in dict.fromkeys(l[7] for l in step.launches):
+            ls = [l for l in step.launches if l[7] == label]
+            gl = capture(torch, lambda lab=label: step.run_tern(lab))
+            ms = time_replays(torch, gl, reps) / len(ls)
+            del gl
+            b = ls[0][6]
+            shapes[label] = {"n_k": [ls[0][2], ls[0][3]], "launches": len(ls), "us": round(ms * 1e3, 2),
+                             "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
+                             "pct_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
     layer_us = tern_ms / (n_tern / (4 if args.compose == "fused" else 7)) * 1e3
 
     cpu = None
@@ -359,7 +459,7 @@ def main():
                                 "down) + int8 head 151936x4096, M=1" if args.config == 2 else
                                 "qwen3-0.6b-shapes token-equivalent: 196 ternary GEMVs + tied int8 head "
                                 "151936x1024, M=1"),
-                   "compose": args.compose, "graph": graph is not None,
+                   "engine": args.engine, "compose": args.compose, "graph": graph is not None,
                    "bytes_per_step": int(step.bytes)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_token_equiv": round(ms_per_step * 1e3, 2),
@@ -368,14 +468,7 @@ def main():
         "head": {"us": round(head_ms * 1e3, 2),
                  "GB/s": round(step.head_bytes / (head_ms * 1e-3) / 1e9, 1)},
         "per_shape": shapes,
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(root, args.compose),
-                     "kernel": "gemv_bf16_fast_kernel<1,*> (tern_gemv, M=1)",
-                     "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
-                     "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
-                     "launches_per_step": n_tern,
-                     "timing": "HIP events around hipGraph replays of the step's ternary GEMV launches"},
+        "roofline": roofline(root, args, achieved, tern_ms, n_tern, step),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -159,46 +159,49 @@ int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t 
 int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
                       float* y, int32_t* acc_dbg, void* stream);
 
-/* ---- dependent GEMV chain (single-stream decode in one launch) ----
+/* ---- GEMV chain (single-stream decode in one launch) ----
  *
  * A token runs its linears one after another, each reading an activation
  * that the previous ones produced; per token the time above the pure DRAM
  * bound sits at the roughly one hundred kernel boundaries and in the
  * dependency chain inside each small kernel ([P2] section "뉴트리노 엔진:
  * 토큰 하나의 시간은 어디로 가는가").  tern_gemv_chain runs a whole chain
- * of M = 1 ternary GEMVs in one persistent launch, with a device-wide barrier
- * between steps and the next step's weights streaming in during it.
+ * of M = 1 ternary GEMVs in one persistent launch: each step waits only for
+ * the activations it reads, and later steps' weights stream in meanwhile.
  *
  * Step p computes, with the arithmetic of tern_gemv at M = 1:
  *   y[n] = sum_b scale[n][b] * sum_{k in block b} t[n][k] * x[k]
- *   y_bf16[n] = y[n] rounded to bf16, nearest-even (when y_bf16 != NULL)
- * x of a step may be (part of) y_bf16 of an earlier step: the chain orders
- * the steps.  It must not overlap the step's own outputs. */
+ * where x is either the step's own input vector, or (x_from = q, an earlier
+ * step with N_q >= K) the first K outputs of step q rounded to bf16
+ * (nearest-even); the rounded copy travels through the workspace, y_q itself
+ * is the fp32 result.  Steps without such a link may run concurrently, so no
+ * y may overlap another y, an input vector or a packed blob of the chain. */
 typedef struct tern_chain_step {
-    const void* packed;   /* tern_pack blob of W [N][K], 16-byte aligned     */
-    int64_t N;            /* output rows, >= 1                                */
-    int64_t K;            /* input features, 512 <= K <= 16384, K % 512 == 0  */
-    const uint16_t* x;    /* bf16 bits [K], 16-byte aligned                   */
-    float* y;             /* fp32 [N], 4-byte aligned                         */
-    uint16_t* y_bf16;     /* bf16 bits [N], 2-byte aligned, or NULL           */
+    const void* packed;   /* tern_pack blob of W [N][K], 16-byte aligned              */
+    int64_t N;            /* output rows, >= 1                                         */
+    int64_t K;            /* input features, 512 <= K <= 16384, K % 512 == 0           */
+    const uint16_t* x;    /* bf16 bits [K], 16-byte aligned; unused when x_from >= 0  */
+    int64_t x_from;       /* -1, or the earlier step whose output is x                 */
+    float* y;             /* fp32 [N], 4-byte aligned                                  */
 } tern_chain_step;
 
-/* Workspace bytes for a chain of nsteps steps (-1 if nsteps < 0).  The
- * workspace holds the grid-barrier counters and the device copy of the
- * plan.  The caller allocates it (256-byte aligned), fills it with zeros once
- * before its first use, and then leaves it to the library; it may be reused
- * for any number of plans and runs.  Runs that share a workspace must not
- * overlap in time.  A 32-bit count of aborted waits sits at byte offset 1544
- * (0 in normal operation; a workspace with a nonzero count runs nothing until
- * it is zero-filled again). */
-int64_t tern_chain_workspace_bytes(int64_t nsteps);
+/* Workspace bytes for this chain, or -1 if nsteps is outside [0, 4095], steps
+ * is NULL or an x_from does not name an earlier step.  The workspace holds the
+ * plan and the rounded copies of the outputs that later steps read.  The
+ * caller allocates it (256-byte aligned), fills it with zeros once before its
+ * first use and then leaves it to the library; it may be re-planned (with a
+ * chain that fits) and run any number of times.  Runs that share a workspace
+ * must not overlap in time.  A 32-bit count of aborted waits sits at byte
+ * offset 8 (0 in normal operation; a workspace with a nonzero count runs
+ * nothing until it is zero-filled again). */
+int64_t tern_chain_workspace_bytes(const tern_chain_step* steps, int64_t nsteps);
 
 /* Validate nsteps host-side step descriptors and enqueue the write of their
  * device plan into the workspace.  Errors: TERN_E_NULL / TERN_E_ALIGN /
- * TERN_E_SHAPE for a bad step, a step whose x overlaps its own outputs, a
- * workspace smaller than tern_chain_workspace_bytes(nsteps), or a step with
- * more than 256 (row tile, 512-k tile) units per CU.  The steps array is
- * read before the call returns. */
+ * TERN_E_SHAPE for a bad step or link, overlapping outputs, a workspace
+ * smaller than tern_chain_workspace_bytes, or a step with more than 256 (row
+ * tile, 512-k tile) units per CU.  The steps array is read before the call
+ * returns. */
 int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspace, int64_t workspace_bytes,
                     void* stream);
 

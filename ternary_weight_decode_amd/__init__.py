@@ -33,7 +33,7 @@ _p = ctypes.c_void_p
 
 class TernChainStep(ctypes.Structure):
     """struct tern_chain_step of include/tern.h."""
-    _fields_ = [("packed", _p), ("N", _i64), ("K", _i64), ("x", _p), ("y", _p), ("y_bf16", _p)]
+    _fields_ = [("packed", _p), ("N", _i64), ("K", _i64), ("x", _p), ("x_from", _i64), ("y", _p)]
 
 
 def lib():
@@ -58,7 +58,7 @@ def lib():
         L.i8_head_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.tern_gemm_prefill.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.tern_chain_workspace_bytes.restype = _i64
-        L.tern_chain_workspace_bytes.argtypes = [_i64]
+        L.tern_chain_workspace_bytes.argtypes = [ctypes.POINTER(TernChainStep), _i64]
         L.tern_chain_plan.argtypes = [ctypes.POINTER(TernChainStep), _i64, _p, _i64, _p]
         L.tern_gemv_chain.argtypes = [_p, _i64, _p]
         for name in _INT_STATUS:
@@ -197,34 +197,42 @@ def tern_gemm_prefill(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=N
     return y
 
 
-def tern_chain_workspace_bytes(nsteps: int) -> int:
-    return int(lib().tern_chain_workspace_bytes(nsteps))
-
-
-def tern_chain_workspace(nsteps: int, device="cuda"):
-    """A zero-filled workspace for chains of up to nsteps steps."""
+def _chain_array(steps):
+    """ctypes tern_chain_step array from (packed, N, K, x or None, x_from, y) tuples of tensors."""
     import torch
-    nbytes = tern_chain_workspace_bytes(nsteps)
+    arr = (TernChainStep * max(1, len(steps)))()
+    for i, (packed, n, k, x, x_from, y) in enumerate(steps):
+        _need(packed, "packed", (torch.uint8,))
+        _need(y, "y", (torch.float32,))
+        if y.numel() != n:
+            raise RuntimeError(f"tern_chain: step {i} y has {y.numel()} elements, N = {n}")
+        if x is not None:
+            _need(x, "x", (torch.int16, torch.uint16, torch.bfloat16))
+            if x.numel() != k:
+                raise RuntimeError(f"tern_chain: step {i} x has {x.numel()} elements, K = {k}")
+        arr[i] = TernChainStep(packed.data_ptr(), n, k, None if x is None else x.data_ptr(), x_from, y.data_ptr())
+    return arr
+
+
+def tern_chain_workspace_bytes(steps) -> int:
+    return int(lib().tern_chain_workspace_bytes(_chain_array(steps), len(steps)))
+
+
+def tern_chain_workspace(steps, device="cuda"):
+    """A zero-filled workspace sized for this chain."""
+    import torch
+    nbytes = tern_chain_workspace_bytes(steps)
     if nbytes < 0:
         _check("tern_chain_workspace_bytes", 2)
     return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 def tern_chain_plan(steps, workspace, stream=None):
-    """steps: sequence of (packed, N, K, x, y, y_bf16 or None); x bf16 bits [K],
-    y fp32 [N], y_bf16 bf16 bits [N].  Writes the device plan into workspace."""
+    """steps: sequence of (packed, N, K, x, x_from, y): x bf16 bits [K] (None when
+    x_from >= 0), x_from -1 or an earlier step whose first K outputs, rounded
+    to bf16, are x; y fp32 [N].  Writes the device plan into workspace."""
     import torch
-    arr = (TernChainStep * max(1, len(steps)))()
-    for i, (packed, n, k, x, y, yb) in enumerate(steps):
-        _need(packed, "packed", (torch.uint8,))
-        _need(x, "x", (torch.int16, torch.uint16, torch.bfloat16))
-        _need(y, "y", (torch.float32,))
-        if yb is not None:
-            _need(yb, "y_bf16", (torch.int16, torch.uint16, torch.bfloat16))
-        if x.numel() != k or y.numel() != n or (yb is not None and yb.numel() != n):
-            raise RuntimeError(f"tern_chain_plan: step {i} tensor sizes do not match N={n}, K={k}")
-        arr[i] = TernChainStep(packed.data_ptr(), n, k, x.data_ptr(), y.data_ptr(),
-                               None if yb is None else yb.data_ptr())
+    arr = _chain_array(steps)
     _need(workspace, "workspace", (torch.uint8,), 1)
     _check("tern_chain_plan", lib().tern_chain_plan(arr, len(steps), _ptr(workspace), workspace.numel(),
                                                     _stream(stream)))
@@ -239,4 +247,4 @@ def tern_gemv_chain(workspace, nsteps: int, stream=None):
 def tern_chain_errors(workspace) -> int:
     """Count of aborted waits recorded in a chain workspace (0 in normal operation)."""
     import torch
-    return int(workspace[1544:1548].view(torch.int32).item())
+    return int(workspace[8:12].view(torch.int32).item())

@@ -189,44 +189,90 @@ int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q,
     return finish(tern::launch_prefill((const uint8_t*)packed, N, K, q, s_x, M, y, acc_dbg, (hipStream_t)stream));
 }
 
-int64_t tern_chain_workspace_bytes(int64_t nsteps)
+namespace {
+
+// Byte offsets of the hand-off buffers of a chain (0 for steps that feed no
+// later step) and the workspace size; -1 if the step links are invalid.
+int64_t chain_layout(const tern_chain_step* steps, int64_t nsteps, std::vector<int64_t>* offs,
+                     std::vector<char>* feeds, int64_t* begin)
 {
-    if (nsteps < 0) return -1;
-    return tern::kChainPlanOffset + nsteps * (int64_t)sizeof(tern::ChainStep);
+    if (nsteps < 0 || nsteps >= tern::kChainMaxSteps || (nsteps > 0 && !steps)) return -1;
+    std::vector<char> f((size_t)nsteps, 0);
+    for (int64_t p = 0; p < nsteps; ++p) {
+        const int64_t q = steps[p].x_from;
+        if (q < -1 || q >= p) return -1;
+        if (q >= 0) f[(size_t)q] = 1;
+    }
+    int64_t at = tern::align256(tern::kChainPlanOffset + nsteps * (int64_t)sizeof(tern::ChainStep));
+    if (begin) *begin = at;
+    if (offs) offs->assign((size_t)nsteps, 0);
+    for (int64_t p = 0; p < nsteps; ++p) {
+        if (!f[(size_t)p]) continue;
+        if (steps[p].N < 1) return -1;
+        if (offs) (*offs)[(size_t)p] = at;
+        at += tern::align256((steps[p].N + 1) / 2 * 8);
+    }
+    if (feeds) *feeds = f;
+    return at;
+}
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb)
+{
+    const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+    return a && b && na > 0 && nb > 0 && a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+}  // namespace
+
+int64_t tern_chain_workspace_bytes(const tern_chain_step* steps, int64_t nsteps)
+{
+    return chain_layout(steps, nsteps, nullptr, nullptr, nullptr);
 }
 
 int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspace, int64_t workspace_bytes,
                     void* stream)
 {
-    if (nsteps < 0 || nsteps > (int64_t)1 << 24) return TERN_E_SHAPE;
+    if (nsteps < 0 || nsteps >= tern::kChainMaxSteps) return TERN_E_SHAPE;
     if (!workspace || (nsteps > 0 && !steps)) return TERN_E_NULL;
     if (((uintptr_t)workspace & 255u) != 0) return TERN_E_ALIGN;
-    if (workspace_bytes < tern_chain_workspace_bytes(nsteps)) return TERN_E_SHAPE;
-    std::vector<tern::ChainStep> plan((size_t)nsteps);
     for (int64_t p = 0; p < nsteps; ++p) {
         const tern_chain_step& st = steps[p];
         if (st.N < 1 || st.K < 512 || st.K % 512 != 0 || st.K > tern::kChainMaxK) return TERN_E_SHAPE;
-        if (!st.packed || !st.x || !st.y) return TERN_E_NULL;
-        if (!aligned16(st.packed) || !aligned16(st.x) || !aligned4(st.y) || ((uintptr_t)st.y_bf16 & 1u))
-            return TERN_E_ALIGN;
-        const uintptr_t x0 = (uintptr_t)st.x, x1 = x0 + (uintptr_t)st.K * 2;
-        auto overlaps = [&](const void* a, int64_t bytes) {
-            const uintptr_t a0 = (uintptr_t)a, a1 = a0 + (uintptr_t)bytes;
-            return a && a0 < x1 && x0 < a1;
-        };
-        if (overlaps(st.y, st.N * 4) || overlaps(st.y_bf16, st.N * 2)) return TERN_E_SHAPE;
-        bool coherent = false;
-        for (int64_t q = 0; q < p && !coherent; ++q)
-            coherent = overlaps(steps[q].y, steps[q].N * 4) || overlaps(steps[q].y_bf16, steps[q].N * 2);
+        if (st.x_from < -1 || st.x_from >= p) return TERN_E_SHAPE;
+        if (st.x_from >= 0 && st.K > steps[st.x_from].N) return TERN_E_SHAPE;
+        if (!st.packed || !st.y || (st.x_from < 0 && !st.x)) return TERN_E_NULL;
+        if (!aligned16(st.packed) || !aligned4(st.y) || (st.x_from < 0 && !aligned16(st.x))) return TERN_E_ALIGN;
+    }
+    // steps without a hand-off between them may run at the same time, so no
+    // output may overlap another output, an input vector or packed weights
+    for (int64_t p = 0; p < nsteps; ++p) {
+        const tern_chain_step& a = steps[p];
+        for (int64_t q = 0; q < nsteps; ++q) {
+            const tern_chain_step& c = steps[q];
+            if (q != p && overlap(a.y, a.N * 4, c.y, c.N * 4)) return TERN_E_SHAPE;
+            if (c.x_from < 0 && overlap(a.y, a.N * 4, c.x, c.K * 2)) return TERN_E_SHAPE;
+            if (overlap(a.y, a.N * 4, c.packed, tern_packed_bytes(c.N, c.K))) return TERN_E_SHAPE;
+        }
+    }
+    std::vector<int64_t> offs;
+    std::vector<char> feeds;
+    int64_t begin = 0;
+    const int64_t need = chain_layout(steps, nsteps, &offs, &feeds, &begin);
+    if (need < 0 || workspace_bytes < need) return TERN_E_SHAPE;
+    std::vector<tern::ChainStep> plan((size_t)nsteps);
+    for (int64_t p = 0; p < nsteps; ++p) {
+        const tern_chain_step& st = steps[p];
         tern::ChainStep& d = plan[(size_t)p];
         d = tern::ChainStep{};
         d.packed = (const uint8_t*)st.packed;
-        d.x = st.x;
+        d.x = st.x_from < 0 ? st.x : nullptr;
         d.y = st.y;
-        d.y_bf16 = st.y_bf16;
         d.N = st.N;
         d.K = st.K;
-        d.x_coherent = coherent ? 1u : 0u;
+        d.x_from = (int32_t)st.x_from;
+        d.feeds = feeds[(size_t)p] ? 1u : 0u;
+        d.hand_off = offs[(size_t)p];
+        d.x_hand_off = st.x_from >= 0 ? offs[(size_t)st.x_from] : 0;
     }
     int rc = check_device();
     if (rc) return rc;
@@ -234,16 +280,17 @@ int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspac
     hipError_t e = tern::chain_grid(&grid);
     if (e != hipSuccess) return hip_fail(e);
     for (const tern::ChainStep& d : plan) {
-        const int64_t nrt = (d.N + 15) / 16, nkt = (d.K / 128 + 3) / 4;
+        const int64_t nrt = (d.N + 15) / 16, nkt = d.K / 512;
         const int64_t per_cu = (nrt + grid - 1) / grid;
         if (per_cu * nkt * 16 > tern::kChainRedMax) return TERN_E_SHAPE;
     }
-    return finish(tern::launch_chain_plan(plan.data(), (int)nsteps, (uint8_t*)workspace, (hipStream_t)stream));
+    return finish(tern::launch_chain_plan(plan.data(), (int)nsteps, (uint8_t*)workspace, begin, need,
+                                          (hipStream_t)stream));
 }
 
 int tern_gemv_chain(void* workspace, int64_t nsteps, void* stream)
 {
-    if (nsteps < 0 || nsteps > (int64_t)1 << 24) return TERN_E_SHAPE;
+    if (nsteps < 0 || nsteps >= tern::kChainMaxSteps) return TERN_E_SHAPE;
     if (!workspace) return TERN_E_NULL;
     if (((uintptr_t)workspace & 255u) != 0) return TERN_E_ALIGN;
     if (nsteps == 0) return TERN_OK;

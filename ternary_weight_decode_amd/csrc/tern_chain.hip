@@ -1,49 +1,50 @@
-// tern_chain.hip — a chain of dependent ternary GEMVs (M = 1) in one
-// persistent launch.
+// tern_chain.hip — a chain of ternary GEMVs (M = 1) in one persistent launch,
+// the steps linked by their activations.
 //
 //   step p:  y_p[n] = sum_b scale_p[n][b] * sum_{k in b} t_p[n][k] * x_p[k]
-//            y_bf16_p = y_p rounded to bf16 (nearest-even), when requested
+//            x_p = an input vector, or bf16(y_q[0:K_p]) of an earlier step q
 //
-// x_p may be the bf16 output of an earlier step of the same chain.  This is
-// single-stream decode with its dependent launches folded into one: on this
-// chip a kernel boundary costs a few microseconds of launch, ramp and drain,
-// and a token has one boundary per dependent linear.
+// This is single-stream decode with its dependent launches folded into one:
+// on this chip a kernel boundary costs a few microseconds of launch, ramp and
+// drain, and a token has one boundary per dependent linear.
 //
 // Work split.  One workgroup per CU stays resident for the whole chain (the
 // launch is cooperative).  Workgroup b owns row tiles b, b+G, b+2G, ... of
 // every step; its 15 compute waves split the step's (row tile, k-tile) units
 // round-robin.  Each compute wave keeps a ring of plane tiles in registers
 // whose loads run ahead of its compute, across step boundaries, so the next
-// step's weights stream in while the workgroups synchronise.  Each unit's
-// fp32 partial (16 rows) goes to LDS.
+// steps' weights stream in while the workgroup waits for its activations.
+// Each unit's fp32 partial (16 rows) goes to LDS; a control wave sums them
+// per output in fixed k-tile order (deterministic) and stores y.  All threads
+// fetch the next activations.
 //
-// Step boundary.  A control wave per workgroup sums the unit partials of each
-// output in fixed k-tile order (deterministic), stores y (and y_bf16) with
-// device-coherent stores, waits for them to complete, joins a grid-wide
-// barrier, then loads the next step's activations (device-coherent loads when
-// they were written earlier in the chain) into LDS.  Compute waves only wait
-// on workgroup barriers, so their weight loads stay in flight meanwhile.
-//
-// Grid barrier: monotonic 64-bit counters, never reset, so the workspace needs
-// no clearing between launches: eight group counters (workgroup b joins group
-// b % 8), a top counter bumped by the last arrival of each group, and a
-// generation counter bumped by the last top arrival.  Arrival number a in a
-// group of size s belongs to barrier a / s; a waiter leaves when the
-// generation exceeds that.  All spins are bounded: a wait past the bound
-// counts an error in the workspace, and every workgroup leaves at the next
-// step boundary; a workspace with a nonzero error count runs nothing until it
-// is cleared.
+// Hand-off.  A step whose output feeds a later step also writes it as 64-bit
+// words {bf16 y[2i], bf16 y[2i+1], 32-bit tag} with device-coherent atomic
+// stores, where the tag names the launch (an epoch counter in the workspace,
+// bumped by the last workgroup to finish) and the step.  A consumer loads
+// the words it needs (device-coherent) until every tag matches, so it waits
+// for exactly the data it reads: no grid-wide barrier, no store
+// acknowledgement on the producer's path.  Steps with an input vector do not
+// wait for anything.  Every spin is bounded: a wait past the bound counts an
+// error in the workspace and the workgroup leaves at the next step boundary;
+// a workspace with a nonzero error count runs nothing until it is cleared.
 #include "tern_device.h"
 #include "tern_launch.h"
 #include "tern_tile.h"
 
 namespace tern {
 
-constexpr int kChainCompute = kChainWaves - 1;
+constexpr int kChainIo = 1;                     // control wave: partial sums and outputs
+constexpr int kChainCompute = kChainWaves - kChainIo;
 constexpr int kChainTpw = 3;                    // plane tiles in flight per compute wave
-constexpr unsigned kChainMaxPolls = 1u << 22;   // bound on every spin (seconds of polling)
+constexpr unsigned kChainMaxPolls = 1u << 21;   // bound on every spin (seconds of polling)
 constexpr int kBufferRsrcWord3 = 0x00020000;    // raw buffer resource, 32-bit data format
 constexpr int kCachePolicySc1 = 16;             // sc1: device-coherent access
+constexpr int kThreads = 64 * kChainWaves;
+constexpr int kWordsPerThread = kChainMaxK / 2 / kThreads;      // hand-off words a thread polls at most
+constexpr int kLoadsPerThread = kChainMaxK * 2 / 16 / kThreads;   // 16-byte input loads per thread
+static_assert(kWordsPerThread == 8, "hand-off polling covers kChainMaxK with 8 words per thread");
+static_assert(kLoadsPerThread == 2, "input staging covers kChainMaxK with 2 loads per thread");
 
 struct ChainStepBatch {
     ChainStep s[kChainPlanBatch];
@@ -57,47 +58,20 @@ __global__ void chain_plan_kernel(ChainStepBatch batch, int first, int count, in
     const int i = threadIdx.x;
     if (i < count) plan[first + i] = batch.s[i];
     if (i == 0 && first + count == total) {
-        uint32_t* hdr = (uint32_t*)(ws + kChainHeaderOffset);
-        hdr[0] = kChainMagic;
-        hdr[1] = (uint32_t)total;
+        ChainHeader* h = (ChainHeader*)ws;
+        h->magic = kChainMagic;
+        h->nsteps = (uint32_t)total;
     }
 }
 
-struct ChainCounters {
-    unsigned long long grp[8][16];   // one 128-byte line per group
-    unsigned long long top[16];
-    unsigned long long gen[16];
-};
-
-__device__ __forceinline__ void compiler_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
-
-// Grid-wide barrier among G workgroups (lane 0 of the control wave of each).
-// Returns false when a spin exceeded its bound.
-__device__ bool chain_grid_barrier(ChainCounters* c, uint32_t* errors, unsigned G)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
 {
-    const unsigned grp = blockIdx.x & 7u;
-    const unsigned gsize = G / 8 + (grp < (G & 7u) ? 1u : 0u);
-    const unsigned ngroups = G < 8 ? G : 8;
-    const unsigned long long a = __hip_atomic_fetch_add(&c->grp[grp][0], 1ull, __ATOMIC_RELAXED,
-                                                        __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned long long done = a / gsize;   // barriers completed before this one
-    if (a % gsize == gsize - 1) {
-        const unsigned long long t = __hip_atomic_fetch_add(&c->top[0], 1ull, __ATOMIC_RELAXED,
-                                                            __HIP_MEMORY_SCOPE_AGENT);
-        if (t % ngroups == ngroups - 1)
-            __hip_atomic_fetch_add(&c->gen[0], 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    unsigned polls = 0;
-    while (__hip_atomic_load(&c->gen[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= done) {
-        if (++polls > kChainMaxPolls) {
-            __hip_atomic_fetch_add(errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return false;
-        }
-    }
-    return true;
+    const uint32_t u = __builtin_bit_cast(uint32_t, f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Geometry of one step as seen by workgroup b and compute wave cw.
+// Geometry of one step as seen by workgroup b.
 struct StepGeo {
     const TERN_GLOBAL uint32_t* words;
     const TERN_GLOBAL uint16_t* scales;
@@ -105,13 +79,11 @@ struct StepGeo {
     int qd, qr;         // kChainCompute / nkt and kChainCompute % nkt (cursor stride)
 };
 
-// Plan entries are read with a wave-uniform index (scalar loads), and their
-// device pointers are global-memory pointers.
+// Plan entries are read with a wave-uniform index (scalar loads).
 __device__ __forceinline__ ChainStep plan_entry(const ChainStep* __restrict__ plan, int p)
 {
     return plan[__builtin_amdgcn_readfirstlane(p)];
 }
-
 
 __device__ __forceinline__ StepGeo step_geo(const ChainStep& st, int b, int G)
 {
@@ -158,21 +130,14 @@ __device__ __forceinline__ void cursor_next(Cursor& c, const ChainStep* plan, in
     cursor_skip_empty(c, plan, nsteps, b, G, cw);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
-{
-    const uint32_t u = __builtin_bit_cast(uint32_t, f);
-    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-__global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainStep* __restrict__ plan,
-                                                                ChainCounters* __restrict__ ctr,
-                                                                uint32_t* __restrict__ hdr, int nsteps_arg)
+__global__ __launch_bounds__(kThreads) void chain_kernel(const ChainStep* __restrict__ plan,
+                                                         ChainHeader* __restrict__ hdr, uint8_t* __restrict__ ws,
+                                                         int nsteps_arg)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     uint16_t* xs = (uint16_t*)smem;                                    // [kChainMaxK] activations
     float* red = (float*)(smem + kChainMaxK * 2);                      // [kChainRedMax] unit partials
-    int* abort_flag = (int*)(smem + kChainMaxK * 2 + kChainRedMax * 4);
+    int* flags = (int*)(smem + kChainMaxK * 2 + kChainRedMax * 4);     // abort, nsteps, epoch
 
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -180,56 +145,86 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainStep
 
     // one thread reads the header for the workgroup: a workspace that was never
     // planned, or that holds an aborted run, runs nothing
-    int* nsteps_lds = abort_flag + 1;
     if (threadIdx.x == 0) {
-        const bool ok = hdr[0] == kChainMagic && hdr[2] == 0;
-        *nsteps_lds = ok ? (nsteps_arg < (int)hdr[1] ? nsteps_arg : (int)hdr[1]) : 0;
-        *abort_flag = 0;
+        const bool ok = hdr->magic == kChainMagic && hdr->errors == 0;
+        flags[0] = 0;
+        flags[1] = ok ? (nsteps_arg < (int)hdr->nsteps ? nsteps_arg : (int)hdr->nsteps) : 0;
+        flags[2] = (int)hdr->epoch;
     }
     __syncthreads();
-    const int nsteps = __builtin_amdgcn_readfirstlane(*nsteps_lds);
+    const int nsteps = __builtin_amdgcn_readfirstlane(flags[1]);
     if (nsteps <= 0) return;
+    const uint32_t epoch = (uint32_t)__builtin_amdgcn_readfirstlane(flags[2]);
+    auto tag_of = [&](int p) -> uint32_t { return epoch * (uint32_t)kChainMaxSteps + (uint32_t)(p + 1); };
 
-    // Activations of a step into LDS: all threads, two 16-byte loads each
-    // (K <= 16384).  Buffer loads past K return zeros and the LDS array holds
-    // kChainMaxK elements, so loads and stores need no guards (and the
-    // compiler's wait counts stay exact).  Loads of an x written earlier in
-    // this chain bypass the non-coherent caches (sc1), as the stores did.
-    auto load_x = [&](const ChainStep& st, u32x4 (&v)[2]) {
+    // Activations of step p into LDS, by all threads (t = threadIdx.x).
+    // An input vector: 16-byte buffer loads (loads past K return zeros, and
+    // the LDS array holds kChainMaxK elements, so nothing needs a guard).  A
+    // hand-off: each thread polls its words until their tags name (this
+    // launch, step q).
+    auto acquire_x = [&](int p, int t) {
+        const ChainStep st = plan_entry(plan, p);
+        if (st.x_from < 0) {
+            const __amdgpu_buffer_rsrc_t rs =
+                __builtin_amdgcn_make_buffer_rsrc((void*)st.x, (short)0, (int)(st.K * 2), kBufferRsrcWord3);
+            u32x4 v[kLoadsPerThread];
+#pragma unroll
+            for (int j = 0; j < kLoadsPerThread; ++j)
+                v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (t + j * kThreads) * 16, 0, 0);
+#pragma unroll
+            for (int j = 0; j < kLoadsPerThread; ++j) ((u32x4*)xs)[t + j * kThreads] = v[j];
+            return;
+        }
+        // 8-byte device-coherent buffer loads (one access each, so a word's tag
+        // and values come from the same store); loads past K/2 words return 0
+        const int nw = (int)(st.K >> 1);
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)st.x, (short)0, (int)(st.K * 2), kBufferRsrcWord3);
-        const int i0 = (int)threadIdx.x * 16, i1 = i0 + 64 * kChainWaves * 16;
-        if (st.x_coherent) {
-            v[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, i0, 0, kCachePolicySc1);
-            v[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, i1, 0, kCachePolicySc1);
-        } else {
-            v[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, i0, 0, 0);
-            v[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, i1, 0, 0);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(ws + st.x_hand_off), (short)0, nw * 8, kBufferRsrcWord3);
+        const uint32_t want = tag_of((int)st.x_from);
+        unsigned pend = 0;
+#pragma unroll
+        for (int j = 0; j < kWordsPerThread; ++j)
+            if (t + j * kThreads < nw) pend |= 1u << j;
+        unsigned polls = 0;
+        while (pend) {
+            // issue every pending word's load, then check them
+            u32x2 v[kWordsPerThread];
+#pragma unroll
+            for (int j = 0; j < kWordsPerThread; ++j) {
+                v[j] = u32x2{0, 0};
+                if (pend & (1u << j))
+                    v[j] = __builtin_amdgcn_raw_buffer_load_b64(rs, (t + j * kThreads) * 8, 0, kCachePolicySc1);
+            }
+#pragma unroll
+            for (int j = 0; j < kWordsPerThread; ++j) {
+                if ((pend & (1u << j)) && v[j][1] == want) {
+                    ((uint32_t*)xs)[t + j * kThreads] = v[j][0];
+                    pend &= ~(1u << j);
+                }
+            }
+            if (pend && ++polls > kChainMaxPolls) {
+                __hip_atomic_fetch_add(&hdr->errors, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                flags[0] = 1;
+                break;
+            }
         }
     };
-    auto store_x = [&](const u32x4 (&v)[2]) {
-        ((u32x4*)xs)[threadIdx.x] = v[0];
-        ((u32x4*)xs)[threadIdx.x + 64 * kChainWaves] = v[1];
-    };
-    static_assert(kChainMaxK == 2 * 64 * kChainWaves * 8, "x staging covers kChainMaxK with two loads per thread");
 
-    if (wave == 0) {
+    const int t = (int)threadIdx.x;
+    if (wave < kChainIo) {
         // ------------------------------------------------------ control wave
-        {
-            u32x4 v[2];
-            const ChainStep st = plan_entry(plan, 0);
-            load_x(st, v);
-            store_x(v);
-        }
-        __syncthreads();                                               // B_0
+        acquire_x(0, t);
+        __syncthreads();                                               // B_0: x_0 in LDS
+        if (flags[0]) return;
         for (int p = 0; p < nsteps; ++p) {
             __syncthreads();                                           // A_p: partials of step p in LDS
             const ChainStep st = plan_entry(plan, p);
             const StepGeo geo = step_geo(st, b, G);
-            // outputs in pairs (n, n+1) of row tile i: sum the k-tile partials in order
             TERN_GLOBAL float* y = (TERN_GLOBAL float*)st.y;
-            TERN_GLOBAL uint16_t* yb = (TERN_GLOBAL uint16_t*)st.y_bf16;
-            for (int o = lane; o < geo.nmy * 8; o += 64) {
+            TERN_GLOBAL unsigned long long* ho = (TERN_GLOBAL unsigned long long*)(ws + st.hand_off);
+            const unsigned long long tag = (unsigned long long)tag_of(p) << 32;
+            // outputs in pairs (n, n+1) of row tile i: sum the k-tile partials in order
+            for (int o = t; o < geo.nmy * 8; o += 64 * kChainIo) {
                 const int i = o >> 3, n = 2 * (o & 7);
                 const float2* rp = (const float2*)(red + (i * geo.nkt) * 16 + n);
                 float s0 = 0.f, s1 = 0.f;
@@ -239,42 +234,32 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainStep
                     s1 += v.y;
                 }
                 const int64_t row = ((int64_t)(b + i * G) << 4) + n;
-                if (row < st.N) {
-                    __hip_atomic_store(&y[row], s0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (st.y_bf16)
-                        __hip_atomic_store(&yb[row], (uint16_t)f32_to_bf16_rne(s0), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-                }
-                if (row + 1 < st.N) {
-                    __hip_atomic_store(&y[row + 1], s1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    if (st.y_bf16)
-                        __hip_atomic_store(&yb[row + 1], (uint16_t)f32_to_bf16_rne(s1), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
+                if (row < st.N) y[row] = s0;
+                if (row + 1 < st.N) y[row + 1] = s1;
+                if (st.feeds && row < st.N) {
+                    const unsigned long long lo = f32_to_bf16_rne(s0);
+                    const unsigned long long hi = row + 1 < st.N ? f32_to_bf16_rne(s1) : 0u;
+                    __hip_atomic_store(&ho[row >> 1], tag | (hi << 16) | lo, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
                 }
             }
             if (p + 1 == nsteps) break;
-            // this workgroup's outputs are complete at the device's coherence point
-            compiler_fence();
-            __builtin_amdgcn_s_waitcnt(0);
-            compiler_fence();
-            bool ok = true;
-            if (lane == 0) ok = chain_grid_barrier(ctr, hdr + 2, (unsigned)G);
-            ok = __builtin_amdgcn_readfirstlane((int)ok) != 0;
-            if (!ok && lane == 0) *abort_flag = 1;
-            compiler_fence();
-            __syncthreads();                                           // C_p: every step-p output stored
-            if (*abort_flag) return;
-            u32x4 v[2];
-            const ChainStep nx = plan_entry(plan, p + 1);
-            load_x(nx, v);
-            store_x(v);
+            acquire_x(p + 1, t);
             __syncthreads();                                           // B_{p+1}
+            if (flags[0]) return;
+        }
+        // the last workgroup to finish moves the workspace to the next epoch
+        if (t == 0) {
+            const unsigned long long d = __hip_atomic_fetch_add(&hdr->done, 1ull, __ATOMIC_RELAXED,
+                                                                __HIP_MEMORY_SCOPE_AGENT);
+            if (d % (unsigned long long)G == (unsigned long long)(G - 1))
+                __hip_atomic_fetch_add(&hdr->epoch, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
         return;
     }
 
     // ---------------------------------------------------------- compute waves
-    const int cw = wave - 1;
+    const int cw = wave - kChainIo;
     Cursor ld, cu;
     ld.p = 0;
     ld.geo = step_geo(plan_entry(plan, 0), b, G);
@@ -307,30 +292,20 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainStep
     };
 
     PlaneTile slot[kChainTpw];
-    {
-        // x of step 0 is requested before the first weight tiles, so waiting
-        // for it does not wait for them
-        u32x4 v[2];
-        load_x(st0, v);
 #pragma unroll
-        for (int s = 0; s < kChainTpw; ++s) refill(slot[s]);
-        store_x(v);
-    }
+    for (int s = 0; s < kChainTpw; ++s) refill(slot[s]);
+    acquire_x(0, t);
 
     int passed = 0;                                                    // step whose activations are staged
     __syncthreads();                                                   // B_0
-    // step boundary: A (partials stored), C (outputs stored device-wide), B (next x staged)
+    if (flags[0]) return;
+    // step boundary: A (partials stored), the next activations, B
     auto next_step = [&]() -> bool {
         __syncthreads();                                               // A_passed
-        __syncthreads();                                               // C_passed
-        if (*abort_flag) return false;
         ++passed;
-        u32x4 v[2];
-        const ChainStep nx = plan_entry(plan, passed);
-        load_x(nx, v);
-        store_x(v);
+        acquire_x(passed, t);
         __syncthreads();                                               // B_passed
-        return true;
+        return flags[0] == 0;
     };
     while (cu.p < nsteps) {
 #pragma unroll
@@ -351,8 +326,24 @@ __global__ __launch_bounds__(64 * kChainWaves) void chain_kernel(const ChainStep
     __syncthreads();                                                   // A_last
 }
 
-hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, hipStream_t stream)
+__global__ void chain_clear_kernel(unsigned long long* p, int64_t n)
 {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0ull;
+}
+
+hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, int64_t hand_off_begin,
+                             int64_t hand_off_end, hipStream_t stream)
+{
+    // stale hand-off words from an earlier plan must never carry a live tag
+    const int64_t nclear = (hand_off_end - hand_off_begin) / 8;
+    if (nclear > 0) {
+        const int64_t blocks = (nclear + 255) / 256 < 1024 ? (nclear + 255) / 256 : 1024;
+        chain_clear_kernel<<<(unsigned)blocks, 256, 0, stream>>>((unsigned long long*)(ws + hand_off_begin),
+                                                                 nclear);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     for (int first = 0; first < nsteps; first += kChainPlanBatch) {
         const int count = nsteps - first < kChainPlanBatch ? nsteps - first : kChainPlanBatch;
         ChainStepBatch batch;
@@ -372,7 +363,7 @@ hipError_t chain_grid(int* grid)
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, 64 * kChainWaves, kChainLds);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, chain_kernel, kThreads, kChainLds);
     if (e != hipSuccess) return e;
     if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
     *grid = cus;   // exactly one workgroup per CU (the LDS request admits no second one)
@@ -385,10 +376,9 @@ hipError_t launch_chain(uint8_t* ws, int nsteps, hipStream_t stream)
     hipError_t e = chain_grid(&grid);
     if (e != hipSuccess) return e;
     const ChainStep* plan = (const ChainStep*)(ws + kChainPlanOffset);
-    ChainCounters* ctr = (ChainCounters*)ws;
-    uint32_t* hdr = (uint32_t*)(ws + kChainHeaderOffset);
-    void* args[] = {&plan, &ctr, &hdr, &nsteps};
-    return hipLaunchCooperativeKernel((const void*)chain_kernel, dim3((unsigned)grid), dim3(64 * kChainWaves), args,
+    ChainHeader* hdr = (ChainHeader*)ws;
+    void* args[] = {&plan, &hdr, &ws, &nsteps};
+    return hipLaunchCooperativeKernel((const void*)chain_kernel, dim3((unsigned)grid), dim3(kThreads), args,
                                       kChainLds, stream);
 }
 

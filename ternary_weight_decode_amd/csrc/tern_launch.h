@@ -25,29 +25,40 @@ hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t
                             float* y, hipStream_t stream);
 hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                           const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
-// ---- dependent GEMV chain (persistent, one workgroup per CU) ----
-// Workspace layout: grid-barrier counters at 0, header (magic, planned step
-// count, error count) at kChainHeaderOffset, plan entries at kChainPlanOffset.
+// ---- GEMV chain (persistent, one workgroup per CU) ----
+// Workspace layout: header at 0, plan entries at kChainPlanOffset, then the
+// hand-off words of every step that feeds a later one (offsets in the plan).
 constexpr int kChainWaves = 16;                   // 1 control + 15 compute waves
 constexpr int kChainMaxK = 16384;                 // activation elements staged per step
 constexpr int kChainRedMax = 4096;                // unit partial floats per workgroup and step
+constexpr int kChainMaxSteps = 4096;              // steps per chain (the hand-off tag counts them)
 constexpr size_t kChainLds = 96 * 1024;           // more than half the CU's LDS: one workgroup per CU
-constexpr int64_t kChainHeaderOffset = 1536;
 constexpr int64_t kChainPlanOffset = 4096;
-constexpr uint32_t kChainMagic = 0x7E4C3A11u;
+constexpr uint32_t kChainMagic = 0x7E4C3A12u;
 constexpr int kChainPlanBatch = 16;
+
+struct ChainHeader {
+    uint32_t magic;                               // kChainMagic once a plan is written
+    uint32_t nsteps;                              // planned steps
+    uint32_t errors;                              // aborted waits (byte offset 8)
+    uint32_t epoch;                               // launches completed on this workspace
+    unsigned long long done;                      // workgroups that finished, over all launches
+};
 
 struct ChainStep {                                // 64 bytes
     const uint8_t* packed;
-    const uint16_t* x;
+    const uint16_t* x;                            // input vector when x_from < 0
     float* y;
-    uint16_t* y_bf16;
     int64_t N, K;
-    uint32_t x_coherent;                          // x overlaps an output of an earlier step
-    uint32_t pad[3];
+    int32_t x_from;                               // -1, or the step whose output is x
+    uint32_t feeds;                               // a later step reads this step's output
+    int64_t hand_off;                             // workspace offset of this step's hand-off words
+    int64_t x_hand_off;                           // workspace offset of the producer's words
 };
+static_assert(sizeof(ChainStep) == 64, "plan entry layout");
 
-hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, hipStream_t stream);
+hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, int64_t hand_off_begin,
+                             int64_t hand_off_end, hipStream_t stream);
 hipError_t launch_chain(uint8_t* ws, int nsteps, hipStream_t stream);
 hipError_t chain_grid(int* grid);
 

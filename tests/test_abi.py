@@ -108,7 +108,7 @@ def test_binding_raises_without_library(monkeypatch, tmp_path):
 
 
 def _steps(*specs):
-    """ctypes array of tern_chain_step from (packed, N, K, x, y, y_bf16) tuples of ints/None."""
+    """ctypes array of tern_chain_step from (packed, N, K, x, x_from, y) tuples of ints/None."""
     arr = (tw.TernChainStep * len(specs))()
     for i, sp in enumerate(specs):
         arr[i] = tw.TernChainStep(*sp)
@@ -116,36 +116,49 @@ def _steps(*specs):
 
 
 def test_chain_workspace_bytes():
-    assert tw.tern_chain_workspace_bytes(0) == 4096
-    assert tw.tern_chain_workspace_bytes(144) == 4096 + 144 * 64
-    assert tw.tern_chain_workspace_bytes(-1) == -1
+    L = tw.lib()
+    a = (0x10000, 4096, 4096, 0x20000, -1, 0x30000)
+    b = (0x10000, 6144, 4096, None, 0, 0x40000)          # reads step 0's output
+    c = (0x10000, 1000, 4096, None, 1, 0x50000)          # reads step 1's output
+    assert L.tern_chain_workspace_bytes(_steps(a), 1) == 4096 + 256            # plan only
+    # plan 3 x 64 B -> 4352; hand-off of step 0: 2048 words x 8 B; of step 1: 3072 x 8 B
+    assert L.tern_chain_workspace_bytes(_steps(a, b, c), 3) == 4352 + 16384 + 24576
+    assert L.tern_chain_workspace_bytes(_steps(a, b), 0) == 4096
+    assert L.tern_chain_workspace_bytes(_steps(a, (0x10000, 16, 512, None, 1, 0x40000)), 2) == -1  # not earlier
+    assert L.tern_chain_workspace_bytes(_steps(a), -1) == -1
+    assert L.tern_chain_workspace_bytes(None, 1) == -1
 
 
 def test_chain_plan_rejects_bad_steps_before_any_device_call():
     L = tw.lib()
-    ws, nb = ctypes.c_void_p(0x100000), 1 << 20
-    good = (0x10000, 4096, 4096, 0x20000, 0x30000, 0x40000)
+    ws, nb = ctypes.c_void_p(0x1000000), 1 << 22
+    good = (0x10000, 4096, 4096, 0x20000, -1, 0x30000)
     assert L.tern_chain_plan(_steps(good), 1, None, nb, None) == E_NULL
     assert L.tern_chain_plan(None, 1, ws, nb, None) == E_NULL
-    assert L.tern_chain_plan(_steps(good), 1, ctypes.c_void_p(0x100010), nb, None) == E_ALIGN   # 256-byte
-    assert L.tern_chain_plan(_steps(good), 1, ws, 4096 + 63, None) == E_SHAPE                   # too small
+    assert L.tern_chain_plan(_steps(good), 1, ctypes.c_void_p(0x1000010), nb, None) == E_ALIGN   # 256-byte
+    assert L.tern_chain_plan(_steps(good), 1, ws, 4096 + 255, None) == E_SHAPE                   # too small
     assert L.tern_chain_plan(_steps(good), -1, ws, nb, None) == E_SHAPE
-    bad_k = [(0x10000, 4096, 640, 0x20000, 0x30000, None),      # K % 512
-             (0x10000, 4096, 256, 0x20000, 0x30000, None),      # K < 512
-             (0x10000, 4096, 16896, 0x20000, 0x30000, None),    # K > 16384
-             (0x10000, 0, 4096, 0x20000, 0x30000, None)]        # N < 1
-    for st in bad_k:
+    assert L.tern_chain_plan(_steps(good), 4096, ws, nb, None) == E_SHAPE
+    bad = [(0x10000, 4096, 640, 0x20000, -1, 0x30000),       # K % 512
+           (0x10000, 4096, 256, 0x20000, -1, 0x30000),       # K < 512
+           (0x10000, 4096, 16896, 0x20000, -1, 0x30000),     # K > 16384
+           (0x10000, 0, 4096, 0x20000, -1, 0x30000),         # N < 1
+           (0x10000, 64, 4096, None, 1, 0x70000),            # x_from not earlier
+           (0x10000, 64, 8192, None, 0, 0x70000),            # K > N of the producer
+           (0x10000, 64, 4096, None, -2, 0x70000)]
+    for st in bad:
         assert L.tern_chain_plan(_steps(good, st), 2, ws, nb, None) == E_SHAPE, st
-    assert L.tern_chain_plan(_steps((None, 16, 512, 0x20000, 0x30000, None)), 1, ws, nb, None) == E_NULL
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, None, 0x30000, None)), 1, ws, nb, None) == E_NULL
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, None, None)), 1, ws, nb, None) == E_NULL
-    assert L.tern_chain_plan(_steps((0x10008, 16, 512, 0x20000, 0x30000, None)), 1, ws, nb, None) == E_ALIGN
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20008, 0x30000, None)), 1, ws, nb, None) == E_ALIGN
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30002, None)), 1, ws, nb, None) == E_ALIGN
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30000, 0x40001)), 1, ws, nb, None) == E_ALIGN
-    # a step's x may not overlap its own outputs (y at x + 16 bytes, y_bf16 ending inside x)
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x20010, None)), 1, ws, nb, None) == E_SHAPE
-    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, 0x30000, 0x1FFF0)), 1, ws, nb, None) == E_SHAPE
+    assert L.tern_chain_plan(_steps((None, 16, 512, 0x20000, -1, 0x30000)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, None, -1, 0x30000)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, -1, None)), 1, ws, nb, None) == E_NULL
+    assert L.tern_chain_plan(_steps((0x10008, 16, 512, 0x20000, -1, 0x30000)), 1, ws, nb, None) == E_ALIGN
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20008, -1, 0x30000)), 1, ws, nb, None) == E_ALIGN
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, -1, 0x30002)), 1, ws, nb, None) == E_ALIGN
+    # outputs may not overlap inputs, packed weights or each other
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, -1, 0x20010)), 1, ws, nb, None) == E_SHAPE
+    assert L.tern_chain_plan(_steps((0x10000, 16, 512, 0x20000, -1, 0x10100)), 1, ws, nb, None) == E_SHAPE
+    assert L.tern_chain_plan(_steps(good, (0x10000, 16, 512, 0x60000, -1, 0x30020)), 2, ws, nb, None) == E_SHAPE
+    assert L.tern_chain_plan(_steps(good, (0x10000, 16, 512, 0x30000, -1, 0x60000)), 2, ws, nb, None) == E_SHAPE
 
 
 def test_chain_run_argument_errors():
