@@ -125,7 +125,7 @@ __global__ __launch_bounds__(512) void gemv_bf16_kernel(const uint8_t* __restric
 // (double-buffered, one barrier per row tile) and are summed in wave order.
 // Index arithmetic stays in 32 bits (64-bit divisions are emulated).
 template <int MT, int TPW>
-__global__ __launch_bounds__(512) void gemv_bf16_fast_kernel(const uint8_t* __restrict__ packed, int64_t N,
+__global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __restrict__ packed, int64_t N,
                                                              int64_t K, const uint16_t* __restrict__ x, int M,
                                                              float* __restrict__ y)
 {
@@ -325,15 +325,18 @@ static int pick_chunk(int64_t K, int64_t M, int64_t bytes_per_elem)
     return (int)(kr < cap ? kr : cap);
 }
 
-static constexpr int64_t kFastLds = 64 * 1024;      // LDS budget of the fast path
+static constexpr int64_t kFastLds = 160 * 1024;     // LDS budget of the fast path (all of a CU's LDS)
 
 // waves per workgroup and k-tiles in flight per wave for the fast path
-// (nw never exceeds the number of k-tiles, so every wave works on every row tile)
+// (nw never exceeds the number of k-tiles, so every wave works on every row
+// tile).  Measured on the 8B shapes at M = 1 (hipGraph of 36 launches, cold
+// weights): one tile in flight per wave beats deeper rings (fewer registers,
+// more resident waves), and 16 waves per row tile beat 8 and 12 on the
+// 24-k-tile down projection (6.4 us vs 6.9 / 7.5 us).
 static void pick_fast(int64_t nkt, int& nw, int& tpw)
 {
-    nw = nkt >= 8 ? 8 : (nkt >= 4 ? 4 : (int)(nkt < 1 ? 1 : nkt));
-    const int64_t per = (nkt + nw - 1) / nw;
-    tpw = per >= 3 ? 3 : (int)(per < 1 ? 1 : per);
+    nw = nkt >= 16 ? 16 : (nkt >= 8 ? 8 : (nkt >= 4 ? 4 : (int)(nkt < 1 ? 1 : nkt)));
+    tpw = 1;
 }
 
 static int device_cus()
@@ -371,9 +374,8 @@ template <int MT>
 static hipError_t launch_fast_mt(int tpw, int nw, size_t lds, hipStream_t stream, const uint8_t* packed, int64_t N,
                                  int64_t K, const uint16_t* x, int M, float* y)
 {
-    if (tpw == 1) return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
-    if (tpw == 2) return launch_fast<MT, 2>(nw, lds, stream, packed, N, K, x, M, y);
-    return launch_fast<MT, 3>(nw, lds, stream, packed, N, K, x, M, y);
+    (void)tpw;   // one tile in flight per wave (pick_fast)
+    return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
 }
 
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
