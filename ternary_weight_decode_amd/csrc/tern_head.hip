@@ -18,6 +18,10 @@
 namespace tern {
 
 constexpr int kHeadWaves = 4;
+#ifndef TERN_HEAD_TPW
+#define TERN_HEAD_TPW 4
+#endif
+constexpr int kHeadTpw = TERN_HEAD_TPW;   // 128-k units in flight per wave (single-chunk path)
 
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int lo_byte)
 {
@@ -145,6 +149,92 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
     }
 }
 
+// Head kernel when all of x fits in LDS: one 16-row tile per wave over the
+// whole K, a ring of TPW 128-k units per wave.  Every ring slot is refilled
+// with the same two loads whether or not a unit is left (past the end they
+// read 16 bytes at the start of W, unused), so the compiler can count the
+// loads in flight exactly instead of waiting for all of them.
+template <bool kInt8, int TPW>
+__global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict__ W, const float* __restrict__ rs,
+                                                        int64_t V, int64_t K, const void* __restrict__ act,
+                                                        const float* __restrict__ s_x, int M, float* __restrict__ y,
+                                                        int32_t* __restrict__ acc_dbg)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int ebytes = kInt8 ? 1 : 2;
+    const int astride = (int)K * ebytes + 16;              // bytes per staged activation row
+    const int mrow = r < M ? r : M - 1;
+    const int nunit = (int)(K / kBlockK);                  // 128-k units per row
+    const int64_t nrt = (V + 15) >> 4;
+    const int64_t q = (int64_t)blockIdx.x * kHeadWaves + wave;
+    const bool has = q < nrt;
+    int64_t v = q * kTileRows + r;
+    v = v < V ? v : V - 1;                                 // rows past V re-read the last row (outputs dropped)
+    const int8_t* row = W + (has ? v : 0) * K + 32 * g;
+
+    u32x4 lo[TPW], hi[TPW];
+    auto load = [&](int s, int j) {
+        const bool valid = has && j < nunit;
+        const int8_t* p = valid ? row + (int64_t)j * kBlockK : W;
+        lo[s] = ld_nt16(p);
+        hi[s] = ld_nt16(valid ? p + 16 : W);
+    };
+#pragma unroll
+    for (int s = 0; s < TPW; ++s) load(s, s);
+
+    {
+        const int per_row = (int)(K * ebytes / 16);
+        const uint8_t* src = (const uint8_t*)act;
+        for (int i = threadIdx.x; i < M * per_row; i += blockDim.x) {
+            const int m = i / per_row, c16 = i - m * per_row;
+            *(u32x4*)(smem + m * astride + 16 * c16) = *(const u32x4*)(src + (int64_t)m * K * ebytes + 16 * c16);
+        }
+    }
+    __syncthreads();
+    if (!has) return;
+
+    f32x4 accf = {0.f, 0.f, 0.f, 0.f};
+    i32x4 acci = {0, 0, 0, 0};
+    const uint8_t* arow = smem + mrow * astride + 32 * g * ebytes;
+    for (int u0 = 0; u0 < nunit; u0 += TPW) {
+#pragma unroll
+        for (int s = 0; s < TPW; ++s) {
+            const int j = u0 + s;
+            if (j < nunit) {
+                const uint8_t* a = arow + j * kBlockK * ebytes;
+                if constexpr (kInt8) {
+                    acci = mfma_i8(*(const u32x4*)(a), lo[s], acci);
+                    acci = mfma_i8(*(const u32x4*)(a + 16), hi[s], acci);
+                } else {
+                    u32x4 B[4];
+                    head_decode_bf16(lo[s], hi[s], B);
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(a + 16 * t), B[t], accf);
+                }
+            }
+            load(s, j + TPW);
+        }
+    }
+    const int64_t vo = q * kTileRows + r;
+    if (vo < V) {
+        const float sv = rs[vo];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 4 * g + i;
+            if (m < M) {
+                if constexpr (kInt8) {
+                    y[(int64_t)m * V + vo] = sv * s_x[m] * (float)acci[i];
+                    if (acc_dbg) acc_dbg[(int64_t)m * V + vo] = acci[i];
+                } else {
+                    y[(int64_t)m * V + vo] = sv * accf[i];
+                }
+            }
+        }
+    }
+}
+
 static int head_chunk(int64_t K, int64_t M, int ebytes)
 {
     int64_t cap = (48 * 1024) / (M * ebytes) / kBlockK * kBlockK;
@@ -152,12 +242,24 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
     return (int)(K < cap ? K : cap);
 }
 
+template <bool kInt8, int TPW>
+static hipError_t launch_head_fast(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
+                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    const size_t lds = (size_t)M * (K * (kInt8 ? 1 : 2) + 16);
+    const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
+    head_fast_kernel<kInt8, TPW><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(W, rs, V, K, act, s_x,
+                                                                                               (int)M, y, acc);
+    return hipGetLastError();
+}
+
 template <bool kInt8>
 static hipError_t launch_head(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                               const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
-    constexpr int kTpw = 1;   // deeper rings cost more VGPRs than they win (measured: 1 -> 137 us, 2 -> 152, 4 -> 198 on the 8B head)
     const int kc = head_chunk(K, M, kInt8 ? 1 : 2);
+    if (kc == K) return launch_head_fast<kInt8, kHeadTpw>(W, rs, V, K, act, s_x, M, y, acc, stream);
+    constexpr int kTpw = 1;   // deeper rings cost more VGPRs than they win here
     const size_t lds = (size_t)M * (kc * (kInt8 ? 1 : 2) + 16);
     // one row tile per wave: a row tile is 16 x K bytes (64 KB at K = 4096), so
     // a static multi-tile assignment leaves a serial tail; retiring workgroups
