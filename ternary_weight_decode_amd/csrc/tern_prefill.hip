@@ -199,6 +199,236 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void prefill_kernel(const uint8_t* _
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M kernel: each weight block is decoded once per workgroup into LDS and
+// shared by all of its waves.
+//
+// Workgroup = 8 waves in a WGM (m) x WGN (n) grid, wave tile 16*TM x 16*TN, so
+// a workgroup covers BM = 16*TM*WGM rows of M and BN = 16*TN*WGN rows of N.
+// Per 128-k block, every thread decodes one plane word pair (32 weights of one
+// row) into the two int8 B operands of its (row, word) lane and stores them in
+// LDS in MFMA lane order, and stages part of the activation block (permuted to
+// the decoded byte order); each wave then runs 2*TM*TN MFMAs from LDS and folds
+// each block's int32 result into fp32 with that block's scale.  Two LDS stages:
+// block b is computed while block b+1 is written.  Plane words are loaded a
+// k-tile (4 blocks) ahead and activations two blocks ahead, all from fixed
+// positions of a loop unrolled over two k-tiles, so the loads in flight are
+// counted exactly.  Requires K % 512 == 0.
+template <int TM, int TN, int WGM, int WGN>
+struct Pf2 {
+    static constexpr int kWaves = WGM * WGN;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int BM = 16 * TM * WGM;
+    static constexpr int BN = 16 * TN * WGN;
+    static constexpr int NRT = BN / 16;                     // row tiles per workgroup
+    static constexpr int kAStride = kBlockK + 16;           // bytes per staged activation row
+    static constexpr int kWBytes = NRT * 2 * 64 * 16;       // decoded B operands per block
+    static constexpr int kABytes = BM * kAStride;
+    static constexpr int kStage = kWBytes + kABytes + BN * 4;
+    static constexpr int kActPerThread = BM * kBlockK / 16 / kThreads;   // 16-byte activation loads
+    static constexpr size_t kLds = 2 * (size_t)kStage;
+    static_assert(NRT * 64 == kThreads, "one plane word pair per thread and block");
+    static_assert(kActPerThread >= 2 && kActPerThread % 2 == 0, "activations staged in 32-byte words");
+};
+
+template <int TM, int TN, int WGM, int WGN, bool kDbg>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void prefill2_kernel(
+    const uint8_t* __restrict__ packed, int64_t N, int64_t K, const int8_t* __restrict__ q,
+    const float* __restrict__ s_x, int64_t M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
+{
+    using C = Pf2<TM, TN, WGM, WGN>;
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int64_t m0 = (int64_t)blockIdx.y * C::BM;
+    const int64_t rt0 = (int64_t)blockIdx.x * C::NRT;
+    const int nb = (int)(K / kBlockK), nkt = nb >> 2;
+    const int64_t nrt = (N + 15) >> 4;
+    const uint32_t* words = (const uint32_t*)packed;
+    const uint16_t* scales = (const uint16_t*)(packed + scale_region_offset(N, K));
+
+    // this thread's decode assignment: row tile dt, lane (r, g) within it
+    const int dt = tid >> 6;
+    const int64_t drt = rt0 + dt;
+    const bool drow_ok = drt < nrt;
+    // this thread's activation staging assignment: row am, 32-byte words aw0 ..
+    constexpr int kWordsPerThread = C::kActPerThread / 2;
+    constexpr int kThreadsPerRow = (kBlockK / 32) / kWordsPerThread;
+    const int am = tid / kThreadsPerRow, aw0 = (tid % kThreadsPerRow) * kWordsPerThread;
+    const int64_t arow = m0 + am < M ? m0 + am : M - 1;
+    const int8_t* asrc = q + arow * K + 32 * aw0;
+
+    auto stage_w = [&](int st) { return smem + st * C::kStage; };
+    auto stage_a = [&](int st) { return smem + st * C::kStage + C::kWBytes; };
+    auto stage_s = [&](int st) { return (float*)(smem + st * C::kStage + C::kWBytes + C::kABytes); };
+
+    // plane words of k-tile kt for this thread's (row tile, r, g); rows past N read tile 0 (outputs dropped)
+    auto load_planes = [&](int kt, PfPlanes<1>& P) {
+        const int ktc = kt < nkt ? kt : nkt - 1;
+        const int64_t rt = drow_ok ? drt : 0;
+        const int64_t wb = tile_word_base(rt, ktc, nb);
+        P.nz[0] = ld_nt16(words + wb + ((0 * 4 + g) * 16 + r) * 4);
+        P.sg[0] = ld_nt16(words + wb + ((1 * 4 + g) * 16 + r) * 4);
+        P.sc[0] = ld_nt8(scales + tile_scale_base(rt, ktc, nb) + r * 4);
+    };
+    auto load_act = [&](int b, u32x4 (&v)[C::kActPerThread]) {
+        const int bc = b < nb ? b : nb - 1;
+        const u32x4* src = (const u32x4*)(asrc + (int64_t)bc * kBlockK);
+#pragma unroll
+        for (int i = 0; i < C::kActPerThread; ++i) v[i] = src[i];
+    };
+    // decode block bq of planes P and stage block activations v into stage st
+    auto write_stage = [&](int st, const PfPlanes<1>& P, int bq, const u32x4 (&v)[C::kActPerThread]) {
+        const CodeWords cw = interleave(P.nz[0][bq], P.sg[0][bq]);
+        const u32x4 B0 = u32x4{i8_quad<0>(cw), i8_quad<1>(cw), i8_quad<2>(cw), i8_quad<3>(cw)};
+        const u32x4 B1 = u32x4{i8_quad<4>(cw), i8_quad<5>(cw), i8_quad<6>(cw), i8_quad<7>(cw)};
+        uint8_t* w = stage_w(st) + ((dt * 2 + 0) * 64 + lane) * 16;
+        *(u32x4*)w = B0;
+        *(u32x4*)(w + 64 * 16) = B1;
+        if (g == 0) {
+            const uint32_t sw = P.sc[0][bq >> 1];
+            stage_s(st)[dt * 16 + r] = half_bits_to_float((sw >> (16 * (bq & 1))) & 0xFFFFu) * (1.0f / 64.0f);
+        }
+#pragma unroll
+        for (int u = 0; u < kWordsPerThread; ++u) {
+            const uint32_t Q[8] = {v[2 * u][0], v[2 * u][1], v[2 * u][2], v[2 * u][3],
+                                   v[2 * u + 1][0], v[2 * u + 1][1], v[2 * u + 1][2], v[2 * u + 1][3]};
+            u32x4 o0, o1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o0[d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+            for (int d = 4; d < 8; ++d) o1[d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+            u32x4* dst = (u32x4*)(stage_a(st) + am * C::kAStride + 32 * (aw0 + u));
+            dst[0] = o0;
+            dst[1] = o1;
+        }
+    };
+
+    f32x4 facc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) facc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // The MFMAs of n-tile j are issued before the epilogue of n-tile j-1, so
+    // the conversions never wait on the matrix core's latency.
+    auto compute = [&](int st, int b) {
+        const uint8_t* ab = stage_a(st);
+        const uint8_t* wb = stage_w(st);
+        const float* sb = stage_s(st);
+        u32x4 A[TM][2];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const uint8_t* a = ab + (wm * 16 * TM + 16 * i + r) * C::kAStride + 32 * g;
+            A[i][0] = *(const u32x4*)(a);
+            A[i][1] = *(const u32x4*)(a + 16);
+        }
+        i32x4 dprev[TM], dcur[TM];
+        float scprev = 0.f;
+#pragma unroll
+        for (int j = 0; j <= TN; ++j) {
+            float sc = 0.f;
+            if (j < TN) {
+                const int t = wn * TN + j;
+                const u32x4 B0 = *(const u32x4*)(wb + ((t * 2 + 0) * 64 + lane) * 16);
+                const u32x4 B1 = *(const u32x4*)(wb + ((t * 2 + 1) * 64 + lane) * 16);
+                sc = sb[t * 16 + r];
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+                    dcur[i] = mfma_i8(A[i][0], B0, i32x4{0, 0, 0, 0});
+                    dcur[i] = mfma_i8(A[i][1], B1, dcur[i]);
+                }
+            }
+            if (j > 0) {
+                const int jp = j - 1;
+#pragma unroll
+                for (int i = 0; i < TM; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        facc[i][jp][e] = __builtin_fmaf(scprev, (float)dprev[i][e], facc[i][jp][e]);
+                    if constexpr (kDbg) {
+                        const int64_t n = ((rt0 + wn * TN + jp) << 4) + r;
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int64_t m = m0 + wm * 16 * TM + 16 * i + 4 * g + e;
+                            if (m < M && n < N) acc_dbg[(m * N + n) * nb + b] = dprev[i][e] >> 6;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < TM; ++i) dprev[i] = dcur[i];
+            scprev = sc;
+        }
+    };
+
+    // prologue: planes of k-tiles 0 and 1, activations of blocks 0 and 1; stage 0 = block 0
+    PfPlanes<1> Pa, Pb;
+    u32x4 va[C::kActPerThread], vb[C::kActPerThread];
+    load_planes(0, Pa);
+    load_act(0, va);
+    load_act(1, vb);
+    load_planes(1, Pb);
+    write_stage(0, Pa, 0, va);
+    load_act(2, va);
+    __syncthreads();
+
+    // block b = 4*kt + bq: compute b from stage b&1, write block b+1 into the
+    // other stage (its activations sit in the register set loaded two blocks
+    // earlier), then load block b+3's activations into that set.  Past the
+    // last block, compute and writes are skipped but the (clamped) loads are
+    // still issued, so every pass issues the same loads.
+    auto block = [&](int b, const PfPlanes<1>& Pnext_src, int nbq_src, u32x4 (&vnext)[C::kActPerThread]) {
+        if (b < nb) compute(b & 1, b);
+        if (b + 1 < nb) write_stage((b + 1) & 1, Pnext_src, nbq_src, vnext);
+        load_act(b + 3, vnext);
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nkt; kt += 2) {
+        // k-tile kt has planes Pa, k-tile kt+1 has Pb
+        block(4 * kt + 0, Pa, 1, vb);
+        block(4 * kt + 1, Pa, 2, va);
+        block(4 * kt + 2, Pa, 3, vb);
+        block(4 * kt + 3, Pb, 0, va);
+        load_planes(kt + 2, Pa);
+        block(4 * kt + 4, Pb, 1, vb);
+        block(4 * kt + 5, Pb, 2, va);
+        block(4 * kt + 6, Pb, 3, vb);
+        block(4 * kt + 7, Pa, 0, va);
+        load_planes(kt + 3, Pb);
+    }
+
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+        const int64_t n = ((rt0 + wn * TN + j) << 4) + r;
+        if (n >= N) continue;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int64_t m = m0 + wm * 16 * TM + 16 * i + 4 * g + e;
+                if (m < M) y[m * N + n] = s_x[m] * facc[i][j][e];
+            }
+    }
+}
+
+template <int TM, int TN, int WGM, int WGN>
+static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
+                             int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    using C = Pf2<TM, TN, WGM, WGN>;
+    const dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
+    if (acc)
+        prefill2_kernel<TM, TN, WGM, WGN, true><<<grid, C::kThreads, C::kLds, stream>>>(packed, N, K, q, s_x, M, y,
+                                                                                      acc);
+    else
+        prefill2_kernel<TM, TN, WGM, WGN, false><<<grid, C::kThreads, C::kLds, stream>>>(packed, N, K, q, s_x, M, y,
+                                                                                       acc);
+    return hipGetLastError();
+}
+
 template <int WM, int WN, int NWAVE>
 static hipError_t launch_pf(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
                             float* y, int32_t* acc, hipStream_t stream)
@@ -215,6 +445,14 @@ static hipError_t launch_pf(const uint8_t* packed, int64_t N, int64_t K, const i
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
+    if (K % 512 == 0 && M >= 128) {
+        // workgroup-shared decode: 256 x 128 tiles when they give at least half
+        // the CUs a workgroup (measured: gate M=512, 192 workgroups, 63 us vs
+        // 70 us with 128 x 64 tiles), else 128 x 64 tiles
+        const int64_t big = ((N + 127) / 128) * ((M + 255) / 256);
+        if (M >= 256 && big >= 128) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+        return launch_pf2<4, 2, 2, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+    }
     // wave tile 64 (m) x 16 (n), two workgroups per CU: measured best among the
     // tile shapes that fit 256 VGPRs without spills (8B gate, M = 2048: 259 us vs
     // 355-398 us for 32x32 and 64x16 at two waves per workgroup)

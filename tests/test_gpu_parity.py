@@ -228,22 +228,37 @@ def test_prefill_small(tw, n, k, m):
     assert oracle.rel_l2(y, y64) <= TOL
 
 
-@pytest.mark.parametrize("proj", ["gate", "down"])
-def test_prefill_full_shape_sampled(tw, proj):
-    """8B gate / down shape at M=512: sampled output rows against the oracle,
-    plus the GEMV-i8 kernel on the same rows (same arithmetic)."""
+@pytest.mark.parametrize("proj,m", [("gate", 512), ("down", 512), ("gate", 2048), ("down", 2048)])
+def test_prefill_full_shape_sampled(tw, proj, m):
+    """8B gate / down shapes at M=512 (128 x 64 workgroup tiles) and M=2048
+    (256 x 128 tiles): sampled output rows and activation rows against the
+    oracle, plus the GEMV-i8 kernel on other rows (same arithmetic)."""
     n, k = synth.SHAPES_8B[proj]
-    m = 512
     t, s, x = gen(n, k, m, seed=42)
     q0, s0 = oracle.quantize_i8(x)
     p = gpu_pack(tw, t, s)
     y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
-    rows = np.random.default_rng(1).choice(n, 64, replace=False)
-    _, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0[:64], s0[:64], rows=rows, want_acc=False)
-    assert oracle.rel_l2(y[:64, rows], y64) <= TOL
-    # the remaining rows agree with the small-M kernel
-    y8 = host(tw.tern_gemv_i8(p, n, k, dev(q0[500:508]), dev(s0[500:508])))
-    assert oracle.rel_l2(y[500:508], y8) <= TOL
+    rng = np.random.default_rng(1)
+    rows = rng.choice(n, 64, replace=False)
+    mrows = np.unique(np.concatenate([rng.choice(m, 62, replace=False), [0, m - 1]]))
+    _, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0[mrows], s0[mrows], rows=rows, want_acc=False)
+    assert oracle.rel_l2(y[np.ix_(mrows, rows)], y64) <= TOL
+    y8 = host(tw.tern_gemv_i8(p, n, k, dev(q0[m - 12:m - 4]), dev(s0[m - 12:m - 4])))
+    assert oracle.rel_l2(y[m - 12:m - 4], y8) <= TOL
+
+
+def test_prefill_large_tiles_exact(tw):
+    """A shape that takes the 256 x 128 workgroup tiles (a grid of 256 of
+    them), ragged in M: int32 block accumulators bit for bit."""
+    n, k, m = 8192, 512, 1000
+    t, s, x = gen(n, k, m, seed=77)
+    q0, s0 = oracle.quantize_i8(x)
+    import torch
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(gpu_pack(tw, t, s), n, k, dev(q0), dev(s0), acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
 
 
 @pytest.mark.parametrize("proj", list(synth.PROJ))
