@@ -7,8 +7,10 @@
 // One wave owns a 16-row tile of W over the whole K (no cross-wave
 // reduction); a workgroup of 4 waves shares the activations staged in LDS.
 // Each wave keeps a ring of loads in flight (depth chosen by the launcher).
-// Each lane streams 32 contiguous bytes of its row per 128-k unit, so a
-// wave's load pair covers 16 full 128-byte lines.  bf16 path: int8 -> f32 via
+// Per 128-k unit, lane (row r, group g) loads bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of its row, so each of a wave's two loads covers whole
+// 64-byte halves of 16 rows' lines (a line half is never requested twice);
+// the activations are read at the matching k.  bf16 path: int8 -> f32 via
 // the byte-select convert (exact) -> bf16 pair by taking the high halves
 // (exact: |w| <= 127 has 7 significant bits), then MFMA 16x16x32 bf16.
 // int8 path: bytes go straight into MFMA 16x16x64 i8.
@@ -18,10 +20,17 @@
 namespace tern {
 
 constexpr int kHeadWaves = 4;
+// byte offsets, within a lane's k range of a 128-k unit, of the four bf16 MFMA
+// steps' activations: k = 16g + {0, 8} and 64 + 16g + {0, 8} (2 bytes each)
+__device__ constexpr int kHalfOff[4] = {0, 16, 128, 144};
 #ifndef TERN_HEAD_TPW
 #define TERN_HEAD_TPW 4
 #endif
 constexpr int kHeadTpw = TERN_HEAD_TPW;   // 128-k units in flight per wave (single-chunk path)
+// 16-byte load of head weights.  Plain (cached) loads: with non-temporal ones
+// the head fetched about 10% more bytes from HBM than it reads and ran ~13%
+// slower at every ring depth measured (V = 151936, K = 4096).
+__device__ __forceinline__ u32x4 head_ld16(const int8_t* p) { return *(const u32x4*)p; }
 
 __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int lo_byte)
 {
@@ -30,7 +39,7 @@ __device__ __forceinline__ uint32_t i8x2_to_bf16x2(uint32_t w, int lo_byte)
     return __builtin_amdgcn_perm(__builtin_bit_cast(uint32_t, f1), __builtin_bit_cast(uint32_t, f0), 0x07060302u);
 }
 
-// 32 int8 weights (8 dwords) -> 4 bf16 B operands (step c = weights 8c .. 8c+7)
+// 32 int8 weights (lo then hi, 8 dwords) -> 4 bf16 B operands (step c = bytes 8c .. 8c+7 of lo, hi)
 __device__ __forceinline__ void head_decode_bf16(const u32x4& lo, const u32x4& hi, u32x4 (&B)[4])
 {
     const uint32_t d[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -79,9 +88,9 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
         auto load = [&](int s) {
             int64_t v = (q0 + li * qstep) * kTileRows + r;
             v = v < V ? v : V - 1;                         // rows past V re-read the last row (outputs dropped)
-            const int8_t* p = W + v * K + (int64_t)(j_lo + lj) * kBlockK + 32 * g;
-            lo[s] = ld_nt16(p);
-            hi[s] = ld_nt16(p + 16);
+            const int8_t* p = W + v * K + (int64_t)(j_lo + lj) * kBlockK + 16 * g;
+            lo[s] = head_ld16(p);
+            hi[s] = head_ld16(p + 64);
             if (++lj == Jc) { lj = 0; ++li; }
         };
 #pragma unroll
@@ -108,15 +117,15 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
 #pragma unroll
             for (int s = 0; s < TPW; ++s) {
                 if (u0 + s < U) {
-                    const uint8_t* arow = smem + mrow * astride + (pj * kBlockK + 32 * g) * ebytes;
+                    const uint8_t* arow = smem + mrow * astride + (pj * kBlockK + 16 * g) * ebytes;
                     if constexpr (kInt8) {
                         acci = mfma_i8(*(const u32x4*)(arow), lo[s], acci);
-                        acci = mfma_i8(*(const u32x4*)(arow + 16), hi[s], acci);
+                        acci = mfma_i8(*(const u32x4*)(arow + 64), hi[s], acci);
                     } else {
                         u32x4 B[4];
                         head_decode_bf16(lo[s], hi[s], B);
 #pragma unroll
-                        for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(arow + 16 * t), B[t], accf);
+                        for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(arow + kHalfOff[t]), B[t], accf);
                     }
                     if (u0 + s + TPW < U) load(s);
                     if (++pj == Jc) {                      // row tile pi: this chunk's part is complete
@@ -172,14 +181,14 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
     const bool has = q < nrt;
     int64_t v = q * kTileRows + r;
     v = v < V ? v : V - 1;                                 // rows past V re-read the last row (outputs dropped)
-    const int8_t* row = W + (has ? v : 0) * K + 32 * g;
+    const int8_t* row = W + (has ? v : 0) * K + 16 * g;
 
     u32x4 lo[TPW], hi[TPW];
     auto load = [&](int s, int j) {
         const bool valid = has && j < nunit;
         const int8_t* p = valid ? row + (int64_t)j * kBlockK : W;
-        lo[s] = ld_nt16(p);
-        hi[s] = ld_nt16(valid ? p + 16 : W);
+        lo[s] = head_ld16(p);
+        hi[s] = head_ld16(valid ? p + 64 : W);
     };
 #pragma unroll
     for (int s = 0; s < TPW; ++s) load(s, s);
@@ -197,7 +206,7 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
 
     f32x4 accf = {0.f, 0.f, 0.f, 0.f};
     i32x4 acci = {0, 0, 0, 0};
-    const uint8_t* arow = smem + mrow * astride + 32 * g * ebytes;
+    const uint8_t* arow = smem + mrow * astride + 16 * g * ebytes;
     for (int u0 = 0; u0 < nunit; u0 += TPW) {
 #pragma unroll
         for (int s = 0; s < TPW; ++s) {
@@ -206,12 +215,12 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
                 const uint8_t* a = arow + j * kBlockK * ebytes;
                 if constexpr (kInt8) {
                     acci = mfma_i8(*(const u32x4*)(a), lo[s], acci);
-                    acci = mfma_i8(*(const u32x4*)(a + 16), hi[s], acci);
+                    acci = mfma_i8(*(const u32x4*)(a + 64), hi[s], acci);
                 } else {
                     u32x4 B[4];
                     head_decode_bf16(lo[s], hi[s], B);
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(a + 16 * t), B[t], accf);
+                    for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(a + kHalfOff[t]), B[t], accf);
                 }
             }
             load(s, j + TPW);
