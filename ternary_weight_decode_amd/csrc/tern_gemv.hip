@@ -209,6 +209,106 @@ __global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __r
     }
 }
 
+// One-shot path (K a multiple of 512, x in LDS, every workgroup resident at
+// once): workgroup b owns R consecutive row tiles and its waves take the
+// R*nkt (row tile, k-tile) units round-robin, U <= 4 per wave.  A wave
+// issues its activation loads and then the loads of all its units before it
+// waits on any, so no second memory latency is exposed and the unit loads
+// stay in flight while x is staged.  Units are computed in order as they
+// arrive; each leaves its fp32 partial in LDS, and after one barrier every
+// output is the sum of its row tile's partials in k-tile order (the result
+// does not depend on the wave split).  XC = 16-byte activation chunks per
+// thread (the launcher checks M*K/8 <= XC * threads).
+template <int MT, int U, int XC>
+__global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N,
+                                                                int64_t K, const uint16_t* __restrict__ x, int M,
+                                                                float* __restrict__ y, int R)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = MT < 4 ? MT : 4;
+    const int nthreads = blockDim.x, nw = nthreads >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7), nkt = nb >> 2;
+    const int nrt = (int)((N + 15) >> 4);
+    const int rt0 = (int)blockIdx.x * R;
+    const int rn = nrt - rt0 < R ? nrt - rt0 : R;          // row tiles of this workgroup
+    const int units = rn * nkt;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    const int xstride = (int)K + 8;
+    uint16_t* xs = (uint16_t*)smem;
+    float* red = (float*)(smem + (size_t)M * xstride * 2);  // [unit + 1 spare][NI][64]
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+
+    // activations first; a chunk index past the end re-loads the last chunk
+    // and stores it to a dummy slot (the start of the partials, written only
+    // after the barrier), so every load is issued and used unconditionally
+    const int per_row = (int)(K >> 3), chunks = M * per_row;
+    u32x4 xv[XC];
+    int xdst[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int u = threadIdx.x + c * nthreads;
+        const int uc = u < chunks ? u : chunks - 1;
+        const int m = uc / per_row, c8 = uc - m * per_row;
+        xv[c] = xg[(int64_t)m * per_row + c8];
+        xdst[c] = u < chunks ? (m * xstride + 8 * c8) * 2 : M * xstride * 2;
+    }
+    // keep the activation loads ahead of the unit loads: waiting for them
+    // must not wait for the weights
+    __builtin_amdgcn_sched_barrier(0);
+    PlaneTile t[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        int j = wave + i * nw;
+        j = j < units ? j : units - 1;
+        const int lrt = j / nkt, kt = j - lrt * nkt;
+        const int64_t wb = tile_word_base(rt0 + lrt, kt, nb);
+        const int64_t sb = tile_scale_base(rt0 + lrt, kt, nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        t[i].sc = ld_nt8(scales + sb + r * 4);
+        __builtin_amdgcn_sched_barrier(0);   // unit i's loads complete before unit i+1's
+    }
+#pragma unroll
+    for (int c = 0; c < XC; ++c) *(u32x4*)(smem + xdst[c]) = xv[c];
+    __syncthreads();
+
+    const int mrow = r < M ? r : M - 1;
+    const uint16_t* xrow = xs + mrow * xstride + 32 * g;
+    // every unit is computed (a unit past the end repeats the last one and
+    // leaves its partial in the spare slot after the real ones), so no load
+    // is consumed behind a branch
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int j = wave + i * nw;
+        const int jc = j < units ? j : units - 1;
+        const int lrt = jc / nkt, kt = jc - lrt * nkt;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16_tile<MT>(t[i], xrow + kt * kTileK, 4, acc);
+        const int slot = j < units ? j : units;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];   // all lanes: no branch
+        __builtin_amdgcn_sched_barrier(0);   // unit i+1's decode waits for its own loads only
+    }
+    __syncthreads();
+
+    const int nout = rn * NI * 64;
+    for (int e = threadIdx.x; e < nout; e += nthreads) {
+        const int l = e & 63, q = (e >> 6) % NI, lrt = (e >> 6) / NI;
+        const int m = 4 * (l >> 4) + q, n = l & 15;
+        const int64_t row = (int64_t)(rt0 + lrt) * kTileRows + n;
+        if (l < lanes_used && m < M && row < N) {
+            const float* pr = red + ((int64_t)lrt * nkt * NI + q) * 64 + l;
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * NI * 64];
+            y[(int64_t)m * N + row] = sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ int8
 
 template <int MT>
@@ -378,9 +478,85 @@ static hipError_t launch_fast_mt(int tpw, int nw, size_t lds, hipStream_t stream
     return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
 }
 
+// One-shot configuration: R row tiles per workgroup (one workgroup per CU
+// when there are enough row tiles), U <= 4 units per wave, up to 16 waves.
+struct OneShot {
+    int R, nw, U, XC;
+    int64_t grid;
+    size_t lds;
+};
+
+template <int MT, int U, int XC>
+static bool oneshot_fits(const OneShot& c)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_bf16_oneshot_kernel<MT, U, XC>, 64 * c.nw, c.lds) !=
+            hipSuccess ||
+        per_cu <= 0)
+        return false;
+    return c.grid <= (int64_t)per_cu * device_cus();
+}
+
+template <int MT, int U, int XC>
+static hipError_t launch_oneshot(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
+                                 const uint16_t* x, int M, float* y)
+{
+    gemv_bf16_oneshot_kernel<MT, U, XC><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, M,
+                                                                                                  y, c.R);
+    return hipGetLastError();
+}
+
+// Dispatch on (U, XC); returns hipErrorNotSupported when the configuration
+// does not fit (then the persistent path runs).
+template <int MT>
+static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
+                                   const uint16_t* x, int M, float* y)
+{
+#define TERN_ONESHOT_CASE(UU, XX)                                                        \
+    if (c.U == UU && c.XC == XX) {                                                       \
+        if (!oneshot_fits<MT, UU, XX>(c)) return hipErrorNotSupported;                   \
+        return launch_oneshot<MT, UU, XX>(c, stream, packed, N, K, x, M, y);              \
+    }
+    TERN_ONESHOT_CASE(1, 1) TERN_ONESHOT_CASE(2, 1) TERN_ONESHOT_CASE(3, 1) TERN_ONESHOT_CASE(4, 1)
+    TERN_ONESHOT_CASE(1, 2) TERN_ONESHOT_CASE(2, 2) TERN_ONESHOT_CASE(3, 2) TERN_ONESHOT_CASE(4, 2)
+    TERN_ONESHOT_CASE(1, 4) TERN_ONESHOT_CASE(2, 4) TERN_ONESHOT_CASE(3, 4) TERN_ONESHOT_CASE(4, 4)
+#undef TERN_ONESHOT_CASE
+    return hipErrorNotSupported;
+}
+
+static bool pick_oneshot(int64_t N, int64_t K, int64_t M, OneShot& c)
+{
+    if (K % kTileK != 0 || M > 4) return false;
+    const int64_t nkt = K / kTileK, nrt = (N + 15) / 16;
+    const int64_t cus = device_cus();
+    c.R = (int)(nrt / cus < 1 ? 1 : nrt / cus);
+    const int64_t units = c.R * nkt;
+    const int64_t U = (units + 15) / 16;
+    if (U > 4) return false;
+    c.U = (int)U;
+    c.nw = (int)((units + U - 1) / U);
+    c.grid = (nrt + c.R - 1) / c.R;
+    const int64_t xc = (M * (K / 8) + 64 * c.nw - 1) / (64 * c.nw);
+    if (xc > 4) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : 4);
+    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    c.lds = (size_t)M * (K + 8) * 2 + (size_t)(units + 1) * ni * 64 * 4;
+    return c.lds <= (size_t)kFastLds;
+}
+
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
+    {
+        OneShot c;
+        if (pick_oneshot(N, K, M, c)) {
+            hipError_t e = hipErrorNotSupported;
+            if (M == 1) e = oneshot_dispatch<1>(c, stream, packed, N, K, x, (int)M, y);
+            else if (M == 2) e = oneshot_dispatch<2>(c, stream, packed, N, K, x, (int)M, y);
+            else e = oneshot_dispatch<4>(c, stream, packed, N, K, x, (int)M, y);
+            if (e != hipErrorNotSupported) return e;
+        }
+    }
     const int64_t nkt = (K / kBlockK + 3) / 4;
     int nw, tpw;
     pick_fast(nkt, nw, tpw);

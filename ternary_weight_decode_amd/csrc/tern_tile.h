@@ -52,15 +52,19 @@ __device__ __forceinline__ float tile_scale(const PlaneTile& p, int bq)
     return half_bits_to_float((w >> (16 * (bq & 1))) & 0xFFFFu);
 }
 
-// 64-bit left shift by a constant.  Written as one instruction: the compiler
-// otherwise splits it into two 32-bit shifts once it sees that only the masked
-// bits of each half are used, and v_lshlrev_b64 issues at the full VALU rate.
+// 64-bit left shift by S.  The amount reaches the shift through an SGPR the
+// compiler cannot see into: with a constant amount it splits the shift into
+// two 32-bit operations (only the masked bits of each half are used), while
+// v_lshlrev_b64 issues at the full VALU rate.  The shift itself stays a
+// compiler-visible instruction, so the hazard recognizer still inserts the
+// wait states for a destination an in-flight MFMA is about to write (which it
+// cannot do for a hand-written VALU instruction).
 template <int S>
 __device__ __forceinline__ uint64_t shl64(uint64_t v)
 {
-    uint64_t r;
-    asm("v_lshlrev_b64 %0, %1, %2" : "=v"(r) : "n"(S), "v"(v));
-    return r;
+    uint32_t s;
+    asm("s_mov_b32 %0, %1" : "=s"(s) : "i"(S));
+    return v << s;
 }
 
 // Decode word pair (N, S) into the four B operands of the block's four MFMA

@@ -91,6 +91,31 @@ def test_gemv_bf16(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+# Shapes that, on a 256-CU device, take the one-pass kernel (K a multiple of
+# 512, M <= 4) in its different configurations: several row tiles per
+# workgroup with a short last workgroup, 1 to 4 units per wave, activation
+# staging of 1 to 4 chunks per thread.  Rows are sampled (plus every row of
+# the last two workgroups' tiles) and compared with the oracle.
+@pytest.mark.parametrize("n,k,m", [(8813, 1024, 1),     # 551 row tiles: 2 per workgroup, last one short
+                                   (24576, 4096, 1),    # 6 row tiles per workgroup, 3 units per wave
+                                   (53243, 2048, 1),    # 13 row tiles per workgroup, 4 units per wave
+                                   (8813, 1536, 2),     # 3 k-tiles, ragged rows, M = 2
+                                   (24576, 4096, 4),    # M = 4, 2 activation chunks per thread
+                                   (100, 4096, 3)])     # M = 3, 4 chunks per thread, partial row tile
+def test_gemv_bf16_one_pass_configs(tw, n, k, m):
+    t, s, x = gen(n, k, m, seed=n + 7 * k + m)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemv(p, n, k, dev(x)))
+    assert y.shape == (m, n) and np.isfinite(y).all()
+    rng = np.random.default_rng(n)
+    tail = np.arange(max(0, n - 3 * 16 * 13), n)
+    rows = np.unique(np.concatenate([rng.choice(n, min(n, 300), replace=False), tail, [0]]))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t[rows], s[rows]), len(rows), k, x)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL, oracle.rel_l2(y[:, rows], y64)
+    # fixed summation order: a second call gives the same bytes
+    assert np.array_equal(y, host(tw.tern_gemv(p, n, k, dev(x))))
+
+
 def test_gemv_config0(tw):
     """Config 0: one 3072x1024 ternary linear, M=1, seed 0."""
     t, s, x = synth.config0_inputs()
