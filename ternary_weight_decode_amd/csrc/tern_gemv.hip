@@ -210,19 +210,18 @@ __global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __r
 }
 
 // One-shot path (K a multiple of 512, x in LDS, every workgroup resident at
-// once): workgroup b owns R consecutive row tiles and its waves take the
+// once): workgroup b owns R row tiles (b, b + G, ...) and its waves take the
 // R*nkt (row tile, k-tile) units round-robin, U <= 4 per wave.  A wave
-// issues its activation loads and then the loads of all its units before it
-// waits on any, so no second memory latency is exposed and the unit loads
-// stay in flight while x is staged.  Units are computed in order as they
-// arrive; each leaves its fp32 partial in LDS, and after one barrier every
+// requests its activations and its first unit, stages x, and then requests
+// its remaining units before computing any, so no second memory latency is
+// exposed.  Units are computed in order as they arrive; each leaves its fp32 partial in LDS, and after one barrier every
 // output is the sum of its row tile's partials in k-tile order (the result
 // does not depend on the wave split).  XC = 16-byte activation chunks per
 // thread (the launcher checks M*K/8 <= XC * threads).
 template <int MT, int U, int XC>
 __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N,
                                                                 int64_t K, const uint16_t* __restrict__ x, int M,
-                                                                float* __restrict__ y, int R)
+                                                                float* __restrict__ y)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NI = MT < 4 ? MT : 4;
@@ -231,8 +230,10 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     const int r = lane & 15, g = lane >> 4;
     const int nb = (int)(K >> 7), nkt = nb >> 2;
     const int nrt = (int)((N + 15) >> 4);
-    const int rt0 = (int)blockIdx.x * R;
-    const int rn = nrt - rt0 < R ? nrt - rt0 : R;          // row tiles of this workgroup
+    // row tiles b, b + G, b + 2G, ... (G = grid): at any moment the
+    // workgroups read neighbouring tiles, spread over all memory channels
+    const int rt0 = (int)blockIdx.x, G = (int)gridDim.x;
+    const int rn = (nrt - 1 - rt0) / G + 1;                 // row tiles of this workgroup (<= R)
     const int units = rn * nkt;
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
@@ -260,21 +261,31 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     // must not wait for the weights
     __builtin_amdgcn_sched_barrier(0);
     PlaneTile t[U];
-#pragma unroll
-    for (int i = 0; i < U; ++i) {
+    auto load_unit = [&](int i) {
         int j = wave + i * nw;
         j = j < units ? j : units - 1;
         const int lrt = j / nkt, kt = j - lrt * nkt;
-        const int64_t wb = tile_word_base(rt0 + lrt, kt, nb);
-        const int64_t sb = tile_scale_base(rt0 + lrt, kt, nb);
+        const int64_t wb = tile_word_base(rt0 + lrt * G, kt, nb);
+        const int64_t sb = tile_scale_base(rt0 + lrt * G, kt, nb);
         t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
         t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
         t[i].sc = ld_nt8(scales + sb + r * 4);
-        __builtin_amdgcn_sched_barrier(0);   // unit i's loads complete before unit i+1's
-    }
+    };
+    // Only the first unit is requested before the activations are staged:
+    // requests queue in the memory system in issue order, and x (needed by
+    // every unit) would otherwise wait behind all of the weights.  The
+    // other units are requested right after the barrier and stream in while
+    // the first one is computed.
+    load_unit(0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int c = 0; c < XC; ++c) *(u32x4*)(smem + xdst[c]) = xv[c];
     __syncthreads();
+#pragma unroll
+    for (int i = 1; i < U; ++i) {
+        load_unit(i);
+        __builtin_amdgcn_sched_barrier(0);   // unit i's loads complete before unit i+1's
+    }
 
     const int mrow = r < M ? r : M - 1;
     const uint16_t* xrow = xs + mrow * xstride + 32 * g;
@@ -299,7 +310,7 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     for (int e = threadIdx.x; e < nout; e += nthreads) {
         const int l = e & 63, q = (e >> 6) % NI, lrt = (e >> 6) / NI;
         const int m = 4 * (l >> 4) + q, n = l & 15;
-        const int64_t row = (int64_t)(rt0 + lrt) * kTileRows + n;
+        const int64_t row = (int64_t)(rt0 + lrt * G) * kTileRows + n;
         if (l < lanes_used && m < M && row < N) {
             const float* pr = red + ((int64_t)lrt * nkt * NI + q) * 64 + l;
             float sum = 0.f;
@@ -478,8 +489,15 @@ static hipError_t launch_fast_mt(int tpw, int nw, size_t lds, hipStream_t stream
     return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
 }
 
-// One-shot configuration: R row tiles per workgroup (one workgroup per CU
-// when there are enough row tiles), U <= 4 units per wave, up to 16 waves.
+// One-shot configuration.  R row tiles per workgroup is chosen to minimise
+// the largest number of units any CU receives (the critical path), and among
+// equals to bring a workgroup closest to 16 units; waves take 2 units each
+// (1 when a workgroup has at most 8), so the second unit's loads overlap the
+// first unit's compute.  Measured on the 8B shapes at M = 1 (hipGraph of 36
+// launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
+// (R = 3, 12 waves) and 9.17 us (R = 6, 16 waves); 6144x4096 4.58 us with
+// R = 2 vs 4.87 us with R = 1; 4096x12288 5.64 us with 12 waves x 2 units vs
+// 6.16 us with 8 x 3.
 struct OneShot {
     int R, nw, U, XC;
     int64_t grid;
@@ -502,7 +520,7 @@ static hipError_t launch_oneshot(const OneShot& c, hipStream_t stream, const uin
                                  const uint16_t* x, int M, float* y)
 {
     gemv_bf16_oneshot_kernel<MT, U, XC><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, M,
-                                                                                                  y, c.R);
+                                                                                                  y);
     return hipGetLastError();
 }
 
@@ -524,17 +542,41 @@ static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const u
     return hipErrorNotSupported;
 }
 
+// units per wave for a workgroup of `units` units
+static int64_t oneshot_u(int64_t units)
+{
+    return units <= 8 ? 1 : ((units + 15) / 16 > 2 ? (units + 15) / 16 : 2);
+}
+
 static bool pick_oneshot(int64_t N, int64_t K, int64_t M, OneShot& c)
 {
     if (K % kTileK != 0 || M > 4) return false;
     const int64_t nkt = K / kTileK, nrt = (N + 15) / 16;
     const int64_t cus = device_cus();
-    c.R = (int)(nrt / cus < 1 ? 1 : nrt / cus);
+    // waves per SIMD that fit next to each other for U = 1..4 units per wave
+    // (56-65, 62-70, 75-81 and 87-91 VGPRs)
+    static const int64_t kWavesPerSimd[5] = {0, 8, 7, 6, 5};
+    int64_t best_max = -1, best_dist = 0;
+    c.R = 0;
+    for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
+        const int64_t units = R * nkt, U = oneshot_u(units);
+        if (U > 4) break;
+        const int64_t nw = (units + U - 1) / U;
+        const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
+        if (per_cu * nw > 4 * kWavesPerSimd[U]) continue;   // not resident in one round
+        const int64_t max_units = per_cu * units;
+        const int64_t dist = units > 16 ? units - 16 : 16 - units;
+        if (best_max < 0 || max_units < best_max || (max_units == best_max && dist < best_dist)) {
+            best_max = max_units;
+            best_dist = dist;
+            c.R = R;
+        }
+        if (grid == 1) break;
+    }
+    if (c.R == 0) return false;
     const int64_t units = c.R * nkt;
-    const int64_t U = (units + 15) / 16;
-    if (U > 4) return false;
-    c.U = (int)U;
-    c.nw = (int)((units + U - 1) / U);
+    c.U = (int)oneshot_u(units);
+    c.nw = (int)((units + c.U - 1) / c.U);
     c.grid = (nrt + c.R - 1) / c.R;
     const int64_t xc = (M * (K / 8) + 64 * c.nw - 1) / (64 * c.nw);
     if (xc > 4) return false;

@@ -91,17 +91,19 @@ def test_gemv_bf16(tw, n, k, m):
     assert err.max() < 1e-4
 
 
-# Shapes that, on a 256-CU device, take the one-pass kernel (K a multiple of
-# 512, M <= 4) in its different configurations: several row tiles per
-# workgroup with a short last workgroup, 1 to 4 units per wave, activation
-# staging of 1 to 4 chunks per thread.  Rows are sampled (plus every row of
-# the last two workgroups' tiles) and compared with the oracle.
-@pytest.mark.parametrize("n,k,m", [(8813, 1024, 1),     # 551 row tiles: 2 per workgroup, last one short
-                                   (24576, 4096, 1),    # 6 row tiles per workgroup, 3 units per wave
+# Shapes that take the one-pass kernel (K a multiple of 512, M <= 4) in its
+# different configurations on a 256-CU device: several row tiles per
+# workgroup (interleaved across workgroups, the last ones holding fewer),
+# 1 to 4 units per wave, spare unit slots, and activation staging of 1 to 4
+# chunks per thread.  Rows are sampled (plus the last row tiles, which the
+# short workgroups hold) and compared with the oracle.
+@pytest.mark.parametrize("n,k,m", [(8813, 1024, 1),     # 3 row tiles per workgroup, last workgroup short
+                                   (24576, 4096, 1),    # 2 units per wave
+                                   (500, 20480, 1),     # 3 units per wave, 4 activation chunks per thread
                                    (53243, 2048, 1),    # 13 row tiles per workgroup, 4 units per wave
-                                   (8813, 1536, 2),     # 3 k-tiles, ragged rows, M = 2
-                                   (24576, 4096, 4),    # M = 4, 2 activation chunks per thread
-                                   (100, 4096, 3)])     # M = 3, 4 chunks per thread, partial row tile
+                                   (8813, 1536, 2),     # 9 units on 5 waves (one spare slot), M = 2
+                                   (24576, 4096, 4),    # M = 4, 4 activation chunks per thread
+                                   (100, 4096, 3)])     # M = 3, partial row tile
 def test_gemv_bf16_one_pass_configs(tw, n, k, m):
     t, s, x = gen(n, k, m, seed=n + 7 * k + m)
     p = gpu_pack(tw, t, s)
