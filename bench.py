@@ -174,6 +174,9 @@ def time_replays(torch, g, reps: int) -> float:
 TRAFFIC_PROFILE = "profiles/tern_gemv_m1_8b_token_fused_hbm_traffic.txt"
 
 
+GEMV_SOURCES = ("tern_gemv.hip", "tern_tile.h", "tern_device.h")   # the M = 1 GEMV kernel's sources
+
+
 def measured_traffic(root: str, compose: str):
     """HBM bytes per ternary-GEMV launch from the committed memory-counter
     summary, or None when it does not apply: other composition, or the GEMV
@@ -184,11 +187,12 @@ def measured_traffic(root: str, compose: str):
         return None
     try:
         text = open(os.path.join(root, TRAFFIC_PROFILE)).read()
-        src = open(os.path.join(root, "ternary_weight_decode_amd", "csrc", "tern_gemv.hip"), "rb").read()
+        src = b"".join(open(os.path.join(root, "ternary_weight_decode_amd", "csrc", f), "rb").read()
+                       for f in GEMV_SOURCES)
     except OSError:
         return None
     m = re.search(r"ternary GEMV per launch .*?: HBM ([0-9.]+) MB", text)
-    h = re.search(r"sha256 \(tern_gemv.hip\) at measurement: ([0-9a-f]{64})", text)
+    h = re.search(r"sha256 \(tern_gemv.hip, tern_tile.h, tern_device.h\) at measurement: ([0-9a-f]{64})", text)
     if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
         return None
     return int(float(m.group(1)) * 1e6)
@@ -220,7 +224,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
                      "timing": "HIP events around back-to-back launches of the step's ternary chain"})
     else:
         base.update({"traffic": measured_traffic(root, args.compose),
-                     "kernel": "gemv_bf16_fast_kernel<1,*> (tern_gemv, M=1)",
+                     "kernel": "gemv_bf16_oneshot_kernel<1,*,*> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
                      "launches_per_step": n_tern,
