@@ -213,7 +213,9 @@ __global__ __launch_bounds__(64 * NWAVE, 2) void prefill_kernel(const uint8_t* _
 // block b is computed while block b+1 is written.  Plane words are loaded a
 // k-tile (4 blocks) ahead and activations two blocks ahead, all from fixed
 // positions of a loop unrolled over two k-tiles, so the loads in flight are
-// counted exactly.  Requires K % 512 == 0.
+// counted exactly.  Requires K % 512 == 0.  The occupancy hint of 2
+// workgroups per CU is kept even for shapes that fit only one: the code it
+// produces ran 10-14% faster (8B gate and down at M = 2048, same VGPR count).
 template <int TM, int TN, int WGM, int WGN>
 struct Pf2 {
     static constexpr int kWaves = WGM * WGN;
@@ -232,7 +234,7 @@ struct Pf2 {
 };
 
 template <int TM, int TN, int WGM, int WGN, bool kDbg>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void prefill2_kernel(
+__global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
     const uint8_t* __restrict__ packed, int64_t N, int64_t K, const int8_t* __restrict__ q,
     const float* __restrict__ s_x, int64_t M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
 {
@@ -446,12 +448,13 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     if (K % 512 == 0 && M >= 128) {
-        // workgroup-shared decode: 256 x 128 tiles when they give at least half
-        // the CUs a workgroup (measured: gate M=512, 192 workgroups, 63 us vs
-        // 70 us with 128 x 64 tiles), else 128 x 64 tiles
-        const int64_t big = ((N + 127) / 128) * ((M + 255) / 256);
-        if (M >= 256 && big >= 128) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
-        return launch_pf2<4, 2, 2, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+        // workgroup-shared decode.  256 x 128 workgroup tiles (8 waves of
+        // 64 x 64) from M = 1024; below, 128 x 64 tiles (4 waves of 32 x 64,
+        // three workgroups per CU).  Measured on the 8B shapes: gate M = 2048
+        // 170 us vs 174 us, down M = 2048 141 us vs 167 us; gate M = 512
+        // 51 us vs 59 us, down M = 512 65 us vs 132 us.
+        if (M >= 1024) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+        return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
     }
     // wave tile 64 (m) x 16 (n), two workgroups per CU: measured best among the
     // tile shapes that fit 256 VGPRs without spills (8B gate, M = 2048: 259 us vs

@@ -275,9 +275,9 @@ def test_prefill_full_shape_sampled(tw, proj, m):
 
 
 def test_prefill_large_tiles_exact(tw):
-    """A shape that takes the 256 x 128 workgroup tiles (a grid of 256 of
-    them), ragged in M: int32 block accumulators bit for bit."""
-    n, k, m = 8192, 512, 1000
+    """A shape that takes the 256 x 128 workgroup tiles (M >= 1024), ragged
+    in M: int32 block accumulators bit for bit."""
+    n, k, m = 8192, 512, 1100
     t, s, x = gen(n, k, m, seed=77)
     q0, s0 = oracle.quantize_i8(x)
     import torch
