@@ -209,22 +209,32 @@ __global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __r
     }
 }
 
-// One-shot path (K a multiple of 512, x in LDS, every workgroup resident at
+// One-pass path (K a multiple of 512, x in LDS, every workgroup resident at
 // once): workgroup b owns R row tiles (b, b + G, ...) and its waves take the
 // R*nkt (row tile, k-tile) units round-robin, U <= 4 per wave.  A wave
 // requests its activations and its first unit, stages x, and then requests
 // its remaining units before computing any, so no second memory latency is
-// exposed.  Units are computed in order as they arrive; each leaves its fp32 partial in LDS, and after one barrier every
-// output is the sum of its row tile's partials in k-tile order (the result
-// does not depend on the wave split).  XC = 16-byte activation chunks per
-// thread (the launcher checks M*K/8 <= XC * threads).
-template <int MT, int U, int XC>
-__global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N,
-                                                                int64_t K, const uint16_t* __restrict__ x, int M,
-                                                                float* __restrict__ y)
+// exposed.  Units are computed in order as they arrive; each leaves its fp32
+// partial in LDS, and after one barrier every output is the sum of its row
+// tile's partials in k-tile order (the result does not depend on the wave
+// split).
+//
+// kI8 = false: bf16 activations, bf16 MFMA on weights decoded to 2t.
+// kI8 = true:  int8 activations q with row scales s_x, int8 MFMA on weights
+//              decoded to 64t; every block's exact int32 sum is scaled in
+//              fp32 (and written to acc_dbg when it is given); y = s_x * sum.
+// XC = activation chunks per thread (16 bytes of bf16, or 32 bytes of int8
+// staged in the decoded byte order); the launcher checks that they cover x.
+template <bool kI8, int MT, int U, int XC>
+__global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                            const void* __restrict__ x, const float* __restrict__ s_x,
+                                                            int M, float* __restrict__ y,
+                                                            int32_t* __restrict__ acc_dbg)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NI = MT < 4 ? MT : 4;
+    constexpr int kChunkBytes = kI8 ? 32 : 16;
+    constexpr int kLoadsPerChunk = kChunkBytes / 16;
     const int nthreads = blockDim.x, nw = nthreads >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -233,29 +243,29 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     // row tiles b, b + G, b + 2G, ... (G = grid): at any moment the
     // workgroups read neighbouring tiles, spread over all memory channels
     const int rt0 = (int)blockIdx.x, G = (int)gridDim.x;
-    const int rn = (nrt - 1 - rt0) / G + 1;                 // row tiles of this workgroup (<= R)
+    const int rn = (nrt - 1 - rt0) / G + 1;                 // row tiles of this workgroup
     const int units = rn * nkt;
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
-    const int xstride = (int)K + 8;
-    uint16_t* xs = (uint16_t*)smem;
-    float* red = (float*)(smem + (size_t)M * xstride * 2);  // [unit + 1 spare][NI][64]
-    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+    const int xrow_bytes = kI8 ? (int)K + 16 : ((int)K + 8) * 2;   // staged bytes per activation row
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [unit + 1 spare][NI][64]
 
     // activations first; a chunk index past the end re-loads the last chunk
     // and stores it to a dummy slot (the start of the partials, written only
     // after the barrier), so every load is issued and used unconditionally
-    const int per_row = (int)(K >> 3), chunks = M * per_row;
-    u32x4 xv[XC];
+    const int per_row = (int)(K * (kI8 ? 1 : 2) / kChunkBytes), chunks = M * per_row;
+    u32x4 xv[XC][kLoadsPerChunk];
     int xdst[XC];
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         const int u = threadIdx.x + c * nthreads;
         const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, c8 = uc - m * per_row;
-        xv[c] = xg[(int64_t)m * per_row + c8];
-        xdst[c] = u < chunks ? (m * xstride + 8 * c8) * 2 : M * xstride * 2;
+        const int m = uc / per_row, cc = uc - m * per_row;
+#pragma unroll
+        for (int h = 0; h < kLoadsPerChunk; ++h)
+            xv[c][h] = xg[((int64_t)m * per_row + cc) * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : M * xrow_bytes;
     }
     // keep the activation loads ahead of the unit loads: waiting for them
     // must not wait for the weights
@@ -279,7 +289,22 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     load_unit(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < XC; ++c) *(u32x4*)(smem + xdst[c]) = xv[c];
+    for (int c = 0; c < XC; ++c) {
+        if constexpr (kI8) {
+            // 32 bytes of q in the byte order of the decoded weights
+            const uint32_t Q[8] = {xv[c][0][0], xv[c][0][1], xv[c][0][2], xv[c][0][3],
+                                   xv[c][1][0], xv[c][1][1], xv[c][1][2], xv[c][1][3]};
+            u32x4 o0, o1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o0[d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+            for (int d = 4; d < 8; ++d) o1[d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+            *(u32x4*)(smem + xdst[c]) = o0;
+            *(u32x4*)(smem + xdst[c] + 16) = o1;
+        } else {
+            *(u32x4*)(smem + xdst[c]) = xv[c][0];
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 1; i < U; ++i) {
@@ -288,7 +313,7 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     }
 
     const int mrow = r < M ? r : M - 1;
-    const uint16_t* xrow = xs + mrow * xstride + 32 * g;
+    const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
     // every unit is computed (a unit past the end repeats the last one and
     // leaves its partial in the spare slot after the real ones), so no load
     // is consumed behind a branch
@@ -298,7 +323,30 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
         const int jc = j < units ? j : units - 1;
         const int lrt = jc / nkt, kt = jc - lrt * nkt;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        bf16_tile<MT>(t[i], xrow + kt * kTileK, 4, acc);
+        if constexpr (kI8) {
+            const int64_t n = (int64_t)(rt0 + lrt * G) * kTileRows + r;
+#pragma unroll
+            for (int bq = 0; bq < 4; ++bq) {
+                u32x4 B[2];
+                decode_i8(t[i].nz[bq], t[i].sg[bq], B);
+                const uint8_t* qa = xrow + (kt * 4 + bq) * kBlockK;
+                i32x4 d = {0, 0, 0, 0};
+                d = mfma_i8(*(const u32x4*)(qa), B[0], d);
+                d = mfma_i8(*(const u32x4*)(qa + 16), B[1], d);
+                const float sc = tile_scale(t[i], bq) * (1.0f / 64.0f);   // decoded weights are 64*t
+#pragma unroll
+                for (int q = 0; q < NI; ++q) acc[q] = __builtin_fmaf(sc, (float)d[q], acc[q]);
+                if (acc_dbg != nullptr && j < units) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int m = 4 * g + q;
+                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kt * 4 + bq] = d[q] >> 6;
+                    }
+                }
+            }
+        } else {
+            bf16_tile<MT>(t[i], (const uint16_t*)xrow + kt * kTileK, 4, acc);
+        }
         const int slot = j < units ? j : units;
 #pragma unroll
         for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];   // all lanes: no branch
@@ -306,6 +354,7 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
     }
     __syncthreads();
 
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
     const int nout = rn * NI * 64;
     for (int e = threadIdx.x; e < nout; e += nthreads) {
         const int l = e & 63, q = (e >> 6) % NI, lrt = (e >> 6) / NI;
@@ -315,7 +364,7 @@ __global__ __launch_bounds__(1024) void gemv_bf16_oneshot_kernel(const uint8_t* 
             const float* pr = red + ((int64_t)lrt * nkt * NI + q) * 64 + l;
             float sum = 0.f;
             for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * NI * 64];
-            y[(int64_t)m * N + row] = sum;
+            y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
         }
     }
 }
@@ -504,40 +553,37 @@ struct OneShot {
     size_t lds;
 };
 
-template <int MT, int U, int XC>
+template <bool kI8, int MT, int U, int XC>
 static bool oneshot_fits(const OneShot& c)
 {
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_bf16_oneshot_kernel<MT, U, XC>, 64 * c.nw, c.lds) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_oneshot_kernel<kI8, MT, U, XC>, 64 * c.nw, c.lds) !=
             hipSuccess ||
         per_cu <= 0)
         return false;
     return c.grid <= (int64_t)per_cu * device_cus();
 }
 
-template <int MT, int U, int XC>
-static hipError_t launch_oneshot(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
-                                 const uint16_t* x, int M, float* y)
-{
-    gemv_bf16_oneshot_kernel<MT, U, XC><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, M,
-                                                                                                  y);
-    return hipGetLastError();
-}
-
 // Dispatch on (U, XC); returns hipErrorNotSupported when the configuration
-// does not fit (then the persistent path runs).
-template <int MT>
+// is not instantiated or would not be resident in one round (then another
+// path runs).
+template <bool kI8, int MT>
 static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
-                                   const uint16_t* x, int M, float* y)
+                                   const void* x, const float* s_x, int M, float* y, int32_t* acc)
 {
-#define TERN_ONESHOT_CASE(UU, XX)                                                        \
-    if (c.U == UU && c.XC == XX) {                                                       \
-        if (!oneshot_fits<MT, UU, XX>(c)) return hipErrorNotSupported;                   \
-        return launch_oneshot<MT, UU, XX>(c, stream, packed, N, K, x, M, y);              \
+#define TERN_ONESHOT_CASE(UU, XX)                                                                              \
+    if (c.U == UU && c.XC == XX) {                                                                             \
+        if (!oneshot_fits<kI8, MT, UU, XX>(c)) return hipErrorNotSupported;                                   \
+        gemv_oneshot_kernel<kI8, MT, UU, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(      \
+            packed, N, K, x, s_x, M, y, acc);                                                                  \
+        return hipGetLastError();                                                                              \
     }
     TERN_ONESHOT_CASE(1, 1) TERN_ONESHOT_CASE(2, 1) TERN_ONESHOT_CASE(3, 1) TERN_ONESHOT_CASE(4, 1)
     TERN_ONESHOT_CASE(1, 2) TERN_ONESHOT_CASE(2, 2) TERN_ONESHOT_CASE(3, 2) TERN_ONESHOT_CASE(4, 2)
     TERN_ONESHOT_CASE(1, 4) TERN_ONESHOT_CASE(2, 4) TERN_ONESHOT_CASE(3, 4) TERN_ONESHOT_CASE(4, 4)
+    if constexpr (MT == 16) {
+        TERN_ONESHOT_CASE(1, 8) TERN_ONESHOT_CASE(2, 8) TERN_ONESHOT_CASE(3, 8) TERN_ONESHOT_CASE(4, 8)
+    }
 #undef TERN_ONESHOT_CASE
     return hipErrorNotSupported;
 }
@@ -548,14 +594,27 @@ static int64_t oneshot_u(int64_t units)
     return units <= 8 ? 1 : ((units + 15) / 16 > 2 ? (units + 15) / 16 : 2);
 }
 
-static bool pick_oneshot(int64_t N, int64_t K, int64_t M, OneShot& c)
+// One-pass configuration.  R row tiles per workgroup is chosen to minimise
+// the largest number of units any CU receives (the critical path), and among
+// equals to bring a workgroup closest to 16 units; waves take 2 units each
+// (1 when a workgroup has at most 8), so the second unit's loads overlap the
+// first unit's compute.  Measured on the 8B shapes at M = 1 (hipGraph of 36
+// launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
+// (R = 3, 12 waves) and 9.17 us (R = 6, 16 waves); 6144x4096 4.58 us with
+// R = 2 vs 4.87 us with R = 1; 4096x12288 5.64 us with 12 waves x 2 units vs
+// 6.16 us with 8 x 3.
+static bool pick_oneshot(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
 {
-    if (K % kTileK != 0 || M > 4) return false;
+    if (K % kTileK != 0 || M > 16) return false;
     const int64_t nkt = K / kTileK, nrt = (N + 15) / 16;
     const int64_t cus = device_cus();
     // waves per SIMD that fit next to each other for U = 1..4 units per wave
-    // (56-65, 62-70, 75-81 and 87-91 VGPRs)
+    // (the M <= 4 bf16 instances use 56-65, 62-70, 75-81 and 87-91 VGPRs;
+    // the occupancy query below has the last word)
     static const int64_t kWavesPerSimd[5] = {0, 8, 7, 6, 5};
+    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const size_t x_lds = (size_t)M * (i8 ? K + 16 : (K + 8) * 2);
+    auto lds_of = [&](int64_t units) { return x_lds + (size_t)(units + 1) * ni * 64 * 4; };
     int64_t best_max = -1, best_dist = 0;
     c.R = 0;
     for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
@@ -563,7 +622,8 @@ static bool pick_oneshot(int64_t N, int64_t K, int64_t M, OneShot& c)
         if (U > 4) break;
         const int64_t nw = (units + U - 1) / U;
         const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
-        if (per_cu * nw > 4 * kWavesPerSimd[U]) continue;   // not resident in one round
+        if (per_cu * nw > 4 * kWavesPerSimd[U]) continue;                      // not resident in one round
+        if ((size_t)per_cu * lds_of(units) > (size_t)kFastLds) continue;       // LDS of the workgroups on a CU
         const int64_t max_units = per_cu * units;
         const int64_t dist = units > 16 ? units - 16 : 16 - units;
         if (best_max < 0 || max_units < best_max || (max_units == best_max && dist < best_dist)) {
@@ -578,26 +638,45 @@ static bool pick_oneshot(int64_t N, int64_t K, int64_t M, OneShot& c)
     c.U = (int)oneshot_u(units);
     c.nw = (int)((units + c.U - 1) / c.U);
     c.grid = (nrt + c.R - 1) / c.R;
-    const int64_t xc = (M * (K / 8) + 64 * c.nw - 1) / (64 * c.nw);
-    if (xc > 4) return false;
-    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : 4);
-    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    c.lds = (size_t)M * (K + 8) * 2 + (size_t)(units + 1) * ni * 64 * 4;
+    const int64_t chunk = i8 ? 32 : 16;
+    const int64_t row_bytes = i8 ? K : 2 * K;
+    const int64_t xc = (M * (row_bytes / chunk) + 64 * c.nw - 1) / (64 * c.nw);
+    // 8 chunks run on the MT = 16 kernel, whose partials hold 4 rows per lane
+    // group: not for M <= 2, whose partial area is sized for 1 or 2
+    if (xc > 8 || (xc > 4 && M <= 2)) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+    c.lds = lds_of(units);
     return c.lds <= (size_t)kFastLds;
+}
+
+// the one-pass path for M <= 16 when it applies; hipErrorNotSupported otherwise
+static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
+                                 int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    OneShot c;
+    if (!pick_oneshot(N, K, M, i8, c)) return hipErrorNotSupported;
+    const int m = (int)M;
+    // 8 activation chunks per thread are instantiated for the MT = 16 kernel
+    // only, which computes the same rows as MT = 4 (4 per lane group)
+    const bool wide = M > 4 || c.XC == 8;
+    if (!i8) {
+        if (wide) return oneshot_dispatch<false, 16>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        if (M == 1) return oneshot_dispatch<false, 1>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        if (M == 2) return oneshot_dispatch<false, 2>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        return oneshot_dispatch<false, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);
+    }
+    if (wide) return oneshot_dispatch<true, 16>(c, stream, packed, N, K, x, s_x, m, y, acc);
+    if (M == 1) return oneshot_dispatch<true, 1>(c, stream, packed, N, K, x, s_x, m, y, acc);
+    if (M == 2) return oneshot_dispatch<true, 2>(c, stream, packed, N, K, x, s_x, m, y, acc);
+    return oneshot_dispatch<true, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);
 }
 
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
     {
-        OneShot c;
-        if (pick_oneshot(N, K, M, c)) {
-            hipError_t e = hipErrorNotSupported;
-            if (M == 1) e = oneshot_dispatch<1>(c, stream, packed, N, K, x, (int)M, y);
-            else if (M == 2) e = oneshot_dispatch<2>(c, stream, packed, N, K, x, (int)M, y);
-            else e = oneshot_dispatch<4>(c, stream, packed, N, K, x, (int)M, y);
-            if (e != hipErrorNotSupported) return e;
-        }
+        const hipError_t e = launch_oneshot(false, packed, N, K, x, nullptr, M, y, nullptr, stream);
+        if (e != hipErrorNotSupported) return e;
     }
     const int64_t nkt = (K / kBlockK + 3) / 4;
     int nw, tpw;
@@ -626,6 +705,10 @@ hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const u
 hipError_t launch_gemv_i8(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
+    {
+        const hipError_t e = launch_oneshot(true, packed, N, K, q, s_x, M, y, acc, stream);
+        if (e != hipErrorNotSupported) return e;
+    }
     const int64_t nkt = (K / kBlockK + 3) / 4;
     const int nw = pick_waves(nkt);
     const int kc = pick_chunk(K, M, 1);

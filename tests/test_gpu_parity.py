@@ -118,6 +118,48 @@ def test_gemv_bf16_one_pass_configs(tw, n, k, m):
     assert np.array_equal(y, host(tw.tern_gemv(p, n, k, dev(x))))
 
 
+# The one-pass kernel with int8 activations and with M = 5..8 bf16 rows:
+# int32 block accumulators bit for bit where the shape allows the full
+# oracle, sampled rows otherwise.
+@pytest.mark.parametrize("n,k,m", [(8813, 1024, 1),     # 3 row tiles per workgroup, last workgroup short
+                                   (24576, 4096, 2),    # 2 units per wave
+                                   (500, 20480, 4),     # 3 units per wave, 4 activation chunks per thread
+                                   (4096, 12288, 8),    # the 8B down shape at M = 8 (x fits only as int8)
+                                   (1000, 4096, 5),     # M = 5, partial row tile
+                                   (300, 1536, 7)])     # M = 7
+def test_gemv_i8_one_pass_configs(tw, n, k, m):
+    import torch
+    t, s, x = gen(n, k, m, seed=n + 3 * k + m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    full = n * k * m <= 64 * 1024 * 1024
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda") if full else None
+    y = host(tw.tern_gemv_i8(p, n, k, dev(q0), dev(s0), acc=acc))
+    assert y.shape == (m, n) and np.isfinite(y).all()
+    if full:
+        acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+        assert np.array_equal(host(acc), acc0)
+        assert oracle.rel_l2(y, y64) <= TOL
+    else:
+        rng = np.random.default_rng(n)
+        rows = np.unique(np.concatenate([rng.choice(n, 300, replace=False), np.arange(n - 48, n)]))
+        acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+        assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    assert np.array_equal(y, host(tw.tern_gemv_i8(p, n, k, dev(q0), dev(s0))))
+
+
+@pytest.mark.parametrize("n,k,m", [(8813, 1024, 5), (24576, 4096, 8), (1000, 2048, 6), (300, 4096, 7)])
+def test_gemv_bf16_one_pass_m5_to_8(tw, n, k, m):
+    t, s, x = gen(n, k, m, seed=n + 5 * k + m)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemv(p, n, k, dev(x)))
+    rng = np.random.default_rng(n)
+    rows = np.unique(np.concatenate([rng.choice(n, min(n, 300), replace=False), np.arange(max(0, n - 48), n)]))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t[rows], s[rows]), len(rows), k, x)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL, oracle.rel_l2(y[:, rows], y64)
+    assert np.array_equal(y, host(tw.tern_gemv(p, n, k, dev(x))))
+
+
 def test_gemv_config0(tw):
     """Config 0: one 3072x1024 ternary linear, M=1, seed 0."""
     t, s, x = synth.config0_inputs()
