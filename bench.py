@@ -47,6 +47,8 @@ def parse():
                     help="chain: one persistent tern_gemv_chain launch per step; graph: one launch per linear")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
+                    help="--mode prefill: run only this shape and M (e.g. gate:2048)")
     ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "copy"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
@@ -331,9 +333,13 @@ def mode_prefill(args, tw, synth, torch):
     """int8-MFMA prefill at M in {64, 512, 2048} on the 8B gate/up/down shapes: TOP/s counting
     2*M*N*K dense operations (the matrix cores execute the zero weights too)."""
     out = []
-    for proj in ("gate", "up", "down"):
+    cases = [(p, m) for p in ("gate", "up", "down") for m in (64, 512, 2048)]
+    if args.prefill_case:
+        proj, m = args.prefill_case.split(":")
+        cases = [(proj, int(m))]
+    for proj in dict.fromkeys(p for p, _ in cases):
         n, k, packed, _ = shape_inputs(tw, synth, torch, proj, 1)
-        for m in (64, 512, 2048):
+        for m in [m for p, m in cases if p == proj]:
             x = torch.from_numpy(synth.gen_x_bf16(np.random.default_rng(m), m, k).view(np.int16)).cuda()
             q, sx = tw.tern_quantize_i8(x)
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
