@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 2
+#define TERN_ABI_VERSION 3
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -148,6 +148,33 @@ int i8_head_gemv(const int8_t* W, const float* row_scale, int64_t V, int64_t K, 
  *   acc_dbg NULL or int32 [M][V]. */
 int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
                     const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
+
+/* Greedy decode on the output head: the int8 head GEMV fused with an argmax
+ * over the vocabulary (token identity is decided greedily on float32 logits,
+ * [P2] section "토큰 동일성의 경계: 그리디, float32, 그리고 두 개의 근접
+ * 동점", which also documents near ties; the unembedding is the largest
+ * tensor of the step, section "뉴트리노 엔진: 토큰 하나의 시간은 어디로
+ * 가는가").  For each activation row m:
+ *   idx[m] = the v with the largest logits[m][v], the lowest such v among
+ *            equal values (-0 counts as +0);  val[m] = that logit.
+ * logits are those of i8_head_gemv (bf16 x) or i8_head_gemv_i8 (int8 q, s_x:
+ * logits[m][v] = (row_scale[v] * s_x[m]) * acc[m][v], rounded to fp32 in
+ * that order); logits must be finite.
+ *   W int8 [V][K] (K % 128 == 0, 1 <= V < 2^32 - 16);  x bf16 bits / q int8
+ *   [M][K] with M*(2K+16) (bf16) or M*(K+16) (int8) <= 163840 bytes;
+ *   1 <= M <= TERN_MAX_M_GEMV;  idx int32 [M];  val fp32 [M];
+ *   logits NULL or fp32 [M][V] (written when given);
+ *   workspace: i8_head_argmax_workspace_bytes(M) bytes of device memory,
+ *   8-byte aligned, owned by the caller; the call clears and uses it, so
+ *   calls that share a workspace must not overlap in time.
+ * Errors: TERN_E_SHAPE for a shape outside these limits, TERN_E_NULL /
+ * TERN_E_ALIGN for pointers; nothing is launched then. */
+int64_t i8_head_argmax_workspace_bytes(int64_t M);
+int i8_head_argmax(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                   int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                      const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
+                      void* stream);
 
 /* Prefill-size ternary GEMM with int8 activations (batched prefill, [P2]
  * section "실행해보기: pip부터 llama.cpp 포크까지"; batched verify is

@@ -181,6 +181,33 @@ def head_i8(w8, rs, q, s_x, rows=None):
     return acc, y64, y32
 
 
+def head_i8_logits_f32(acc, rs, s_x):
+    """fp32 logits of the int8-activation head from its exact int32 sums, in
+    the operation order the library states: (rs[v] * s_x[m]) * acc[m][v], each
+    product rounded to fp32 ([P2] "3진 계열이라는 이름의 실체": the head stays
+    int8; greedy decoding compares float32 logits, [P2] "토큰 동일성의 경계:
+    그리디, float32, 그리고 두 개의 근접 동점")."""
+    acc = np.asarray(acc, dtype=np.int64)
+    assert np.abs(acc).max(initial=0) < (1 << 31), "int32 sums"
+    # int32 -> fp32 rounds to nearest-even (exact below 2^24)
+    rs = np.asarray(rs, dtype=np.float32)
+    s_x = np.asarray(s_x, dtype=np.float32)
+    scale = (rs[None, :] * s_x[:, None]).astype(np.float32)          # one fp32 product
+    return (scale * acc.astype(np.float32)).astype(np.float32)        # a second one
+
+
+def greedy_argmax(logits):
+    """Greedy decode over fp32 logits [M, V] ([P2] "토큰 동일성의 경계: 그리디,
+    float32, 그리고 두 개의 근접 동점": the next token is the argmax of float32
+    logits, and near ties occur): per row, the index of the largest value, the
+    lowest index among equal values, -0 counted as +0.  Returns (idx int32 [M],
+    val fp32 [M])."""
+    z = np.asarray(logits, dtype=np.float32) + np.float32(0.0)   # -0 -> +0
+    assert np.isfinite(z).all()
+    idx = np.argmax(z, axis=1)                                   # first (lowest) index of the maximum
+    return idx.astype(np.int32), z[np.arange(z.shape[0]), idx]
+
+
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
 

@@ -22,9 +22,11 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtern.so"
 MAX_M_GEMV = 16
 SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
-           "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain")
+           "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
+           "i8_head_argmax", "i8_head_argmax_i8")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
-               "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain")
+               "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
+               "i8_head_argmax_i8")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -61,6 +63,10 @@ def lib():
         L.tern_chain_workspace_bytes.argtypes = [ctypes.POINTER(TernChainStep), _i64]
         L.tern_chain_plan.argtypes = [ctypes.POINTER(TernChainStep), _i64, _p, _i64, _p]
         L.tern_gemv_chain.argtypes = [_p, _i64, _p]
+        L.i8_head_argmax_workspace_bytes.restype = _i64
+        L.i8_head_argmax_workspace_bytes.argtypes = [_i64]
+        L.i8_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+        L.i8_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -184,6 +190,49 @@ def i8_head_gemv_i8(w, row_scale, q, s_x, y=None, acc=None, stream=None):
     _check("i8_head_gemv_i8", lib().i8_head_gemv_i8(_ptr(w), _ptr(row_scale), v, k, _ptr(q), _ptr(s_x), m, _ptr(y),
                                                     _ptr(acc), _stream(stream)))
     return y
+
+
+def i8_head_argmax_workspace_bytes(m: int) -> int:
+    return int(lib().i8_head_argmax_workspace_bytes(m))
+
+
+def i8_head_argmax_workspace(m: int, device="cuda"):
+    """A workspace for i8_head_argmax[_i8] with up to m activation rows."""
+    import torch
+    return torch.empty(i8_head_argmax_workspace_bytes(m), dtype=torch.uint8, device=device)
+
+
+def i8_head_argmax(w, row_scale, x, workspace=None, logits=None, stream=None):
+    """Greedy argmax over the head logits of bf16 x: (idx int32 [M], val fp32 [M]); logits [M, V] filled when given."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    v, k = w.shape
+    m = x.shape[0]
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(m, x.device)
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    val = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("i8_head_argmax", lib().i8_head_argmax(_ptr(w), _ptr(row_scale), v, k, _ptr(x), m, _ptr(idx), _ptr(val),
+                                                  _ptr(logits), _ptr(workspace), _stream(stream)))
+    return idx, val
+
+
+def i8_head_argmax_i8(w, row_scale, q, s_x, workspace=None, logits=None, stream=None):
+    """Greedy argmax over the head logits of int8 q (row scales s_x): (idx, val)."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(q, "q", (torch.int8,), 2)
+    v, k = w.shape
+    m = q.shape[0]
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(m, q.device)
+    idx = torch.empty(m, dtype=torch.int32, device=q.device)
+    val = torch.empty(m, dtype=torch.float32, device=q.device)
+    _check("i8_head_argmax_i8", lib().i8_head_argmax_i8(_ptr(w), _ptr(row_scale), v, k, _ptr(q), _ptr(s_x), m,
+                                                        _ptr(idx), _ptr(val), _ptr(logits), _ptr(workspace),
+                                                        _stream(stream)))
+    return idx, val
 
 
 def tern_gemm_prefill(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=None):

@@ -158,6 +158,64 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
     }
 }
 
+// Greedy argmax fused into the head: per activation row m, the row v with the
+// largest logit, the lowest v among equal logits (-0 counted as +0).  Each
+// logit becomes a 64-bit key {order-preserving bits of the value, ~v}, so one
+// unsigned maximum decides both.  Every wave reduces its 16 rows in
+// registers and publishes one key per m with a device-scope atomic maximum;
+// the wave that completes the count reads the keys back and writes the
+// results.  keys/count start at zero (the launcher clears them).
+struct HeadArgmax {
+    unsigned long long* keys;   // [M], zero on entry
+    unsigned* count;            // zero on entry
+    int32_t* idx;               // [M]
+    float* val;                 // [M]
+    unsigned waves;             // waves that own a row tile (= row tiles)
+};
+
+__device__ __forceinline__ uint32_t order_bits(float f)
+{
+    const uint32_t u = __builtin_bit_cast(uint32_t, f + 0.0f);   // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float unorder_bits(uint32_t o)
+{
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+
+// The argmax epilogue of one wave: lane (r, g) holds logits lv[i] of row
+// v = tile*16 + r for activation rows m = 4g + i (valid when ok[i]).
+__device__ __forceinline__ void head_argmax_epilogue(const HeadArgmax& am, const float (&lv)[4], const bool (&ok)[4],
+                                                     int64_t v, int M, int lane)
+{
+    const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint64_t key = ok[i] ? ((uint64_t)order_bits(lv[i]) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)v) : 0;
+#pragma unroll
+        for (int off = 8; off >= 1; off >>= 1) {   // the 16 lanes of group g
+            const uint32_t lo = __shfl_xor((uint32_t)key, off), hi = __shfl_xor((uint32_t)(key >> 32), off);
+            const uint64_t other = ((uint64_t)hi << 32) | lo;
+            key = other > key ? other : key;
+        }
+        const int m = 4 * g + i;
+        if (r == 0 && m < M && key != 0) atomicMax(am.keys + m, (unsigned long long)key);
+    }
+    __threadfence();
+    unsigned last = 0;
+    if (lane == 0) last = atomicAdd(am.count, 1u) == am.waves - 1 ? 1u : 0u;
+    last = __shfl(last, 0);
+    if (last) {
+        __threadfence();
+        if (lane < M) {
+            const uint64_t key = __hip_atomic_load(am.keys + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            am.idx[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
+            am.val[lane] = unorder_bits((uint32_t)(key >> 32));
+        }
+    }
+}
+
 // Head kernel when all of x fits in LDS: one 16-row tile per wave over the
 // whole K, a ring of TPW 128-k units per wave.  Every ring slot is refilled
 // with the same two loads whether or not a unit is left (past the end they
@@ -167,7 +225,7 @@ template <bool kInt8, int TPW>
 __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict__ W, const float* __restrict__ rs,
                                                         int64_t V, int64_t K, const void* __restrict__ act,
                                                         const float* __restrict__ s_x, int M, float* __restrict__ y,
-                                                        int32_t* __restrict__ acc_dbg)
+                                                        int32_t* __restrict__ acc_dbg, HeadArgmax am)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -227,21 +285,25 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
         }
     }
     const int64_t vo = q * kTileRows + r;
-    if (vo < V) {
-        const float sv = rs[vo];
+    float lv[4];
+    bool ok[4];
+    {
+        const float sv = rs[vo < V ? vo : V - 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * g + i;
-            if (m < M) {
+            ok[i] = vo < V && m < M;
+            if constexpr (kInt8) lv[i] = sv * s_x[m < M ? m : M - 1] * (float)acci[i];
+            else lv[i] = sv * accf[i];
+            if (ok[i]) {
+                if (y) y[(int64_t)m * V + vo] = lv[i];
                 if constexpr (kInt8) {
-                    y[(int64_t)m * V + vo] = sv * s_x[m] * (float)acci[i];
                     if (acc_dbg) acc_dbg[(int64_t)m * V + vo] = acci[i];
-                } else {
-                    y[(int64_t)m * V + vo] = sv * accf[i];
                 }
             }
         }
     }
+    if (am.keys) head_argmax_epilogue(am, lv, ok, vo, M, lane);
 }
 
 static int head_chunk(int64_t K, int64_t M, int ebytes)
@@ -253,12 +315,13 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
 
 template <bool kInt8, int TPW>
 static hipError_t launch_head_fast(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
-                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream,
+                                   HeadArgmax am = HeadArgmax{nullptr, nullptr, nullptr, nullptr, 0})
 {
     const size_t lds = (size_t)M * (K * (kInt8 ? 1 : 2) + 16);
     const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
     head_fast_kernel<kInt8, TPW><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(W, rs, V, K, act, s_x,
-                                                                                               (int)M, y, acc);
+                                                                                               (int)M, y, acc, am);
     return hipGetLastError();
 }
 
@@ -289,6 +352,39 @@ hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K
                           const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     return launch_head<true>(W, rs, V, K, q, s_x, M, y, acc, stream);
+}
+
+// fused head + argmax: x (all M rows) must fit in LDS, as the single-pass
+// kernel stages it whole
+bool head_argmax_fits(int64_t K, int64_t M, bool int8_act)
+{
+    return (size_t)M * (K * (int8_act ? 1 : 2) + 16) <= (size_t)160 * 1024;
+}
+
+template <bool kInt8>
+static hipError_t launch_head_argmax(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
+                                     const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                     hipStream_t stream)
+{
+    // workspace: count at byte 0, keys at byte 64; cleared by a kernel (no
+    // memset, so the call can be captured in a graph)
+    hipError_t e = launch_fill_zero(ws, 64 + 8 * M, stream);
+    if (e != hipSuccess) return e;
+    const HeadArgmax am{(unsigned long long*)((uint8_t*)ws + 64), (unsigned*)ws, idx, val, (unsigned)((V + 15) / 16)};
+    return launch_head_fast<kInt8, kHeadTpw>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
+}
+
+hipError_t launch_head_argmax_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                   int64_t M, float* y, int32_t* idx, float* val, void* ws, hipStream_t stream)
+{
+    return launch_head_argmax<false>(W, rs, V, K, x, nullptr, M, y, idx, val, ws, stream);
+}
+
+hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                 const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                 hipStream_t stream)
+{
+    return launch_head_argmax<true>(W, rs, V, K, q, s_x, M, y, idx, val, ws, stream);
 }
 
 }  // namespace tern

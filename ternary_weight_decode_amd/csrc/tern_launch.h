@@ -25,6 +25,12 @@ hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t
                             float* y, hipStream_t stream);
 hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                           const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
+bool head_argmax_fits(int64_t K, int64_t M, bool int8_act);
+hipError_t launch_head_argmax_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                   int64_t M, float* y, int32_t* idx, float* val, void* ws, hipStream_t stream);
+hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                 const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                 hipStream_t stream);
 // ---- GEMV chain (persistent, one workgroup per CU) ----
 // Workspace layout: header at 0, plan entries at kChainPlanOffset, then the
 // hand-off words of every step that feeds a later one (offsets in the plan).

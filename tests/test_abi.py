@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 2
+    assert L.tern_abi_version() == 3
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -98,6 +98,27 @@ def test_null_and_alignment_errors():
     assert L.tern_stats(p, 16, 128, None, None) == E_NULL
     assert L.tern_quantize_i8(p, 2, 128, p, None, None) == E_NULL
     assert L.tern_quantize_i8(m, 2, 128, p, p, None) == E_ALIGN
+
+
+def test_head_argmax_workspace_and_argument_errors():
+    L = tw.lib()
+    assert tw.i8_head_argmax_workspace_bytes(1) == 72
+    assert tw.i8_head_argmax_workspace_bytes(16) == 64 + 128
+    assert tw.i8_head_argmax_workspace_bytes(0) == -1 and tw.i8_head_argmax_workspace_bytes(17) == -1
+    p, m = ALIGNED, MISALIGNED
+    f, fi = L.i8_head_argmax, L.i8_head_argmax_i8
+    assert f(p, p, 100, 96, p, 1, p, p, None, p, None) == E_SHAPE          # K % 128
+    assert f(p, p, 0, 128, p, 1, p, p, None, p, None) == E_SHAPE           # V = 0: no argmax
+    assert f(p, p, 100, 128, p, 0, p, p, None, p, None) == E_SHAPE         # M = 0
+    assert f(p, p, 100, 128, p, 17, p, p, None, p, None) == E_SHAPE        # M > 16
+    assert f(p, p, 100, 8192, p, 16, p, p, None, p, None) == E_SHAPE       # bf16 x of 16 x 8192 does not fit LDS
+    assert fi(p, p, 100, 8192, p, p, 16, p, p, None, p, None) != E_SHAPE   # int8 q of the same shape does
+    assert f(p, p, 100, 128, p, 1, p, p, None, None, None) == E_NULL       # workspace
+    assert f(p, p, 100, 128, p, 1, None, p, None, p, None) == E_NULL       # idx
+    assert fi(p, p, 100, 128, p, None, 1, p, p, None, p, None) == E_NULL   # s_x
+    assert f(m, p, 100, 128, p, 1, p, p, None, p, None) == E_ALIGN
+    assert f(p, p, 100, 128, p, 1, p, p, ctypes.c_void_p(0x10002), p, None) == E_ALIGN   # logits
+    assert f(p, p, 100, 128, p, 1, p, p, None, ctypes.c_void_p(0x10004), None) == E_ALIGN
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

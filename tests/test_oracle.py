@@ -239,6 +239,53 @@ def test_head_vs_bruteforce():
     assert oracle.rel_l2(y64i, acc * sx[:, None].astype(np.float64) * rs[None, :].astype(np.float64)) < 1e-15
 
 
+def test_greedy_argmax_ties_and_signed_zero():
+    """Hand-built rows: the largest value wins, the lowest index among equal
+    values, -0 equal to +0."""
+    rows = np.array([[1.0, 3.0, 3.0, 2.0],
+                     [-5.0, -1.0, -2.0, -1.0],
+                     [-0.0, 0.0, -1.0, -0.0],
+                     [0.0, -0.0, -3.0, -2.0],
+                     [7.0, 7.0, 7.0, 7.0]], np.float32)
+    idx, val = oracle.greedy_argmax(rows)
+    assert idx.tolist() == [1, 1, 0, 0, 0]
+    assert val.tolist() == [3.0, -1.0, 0.0, 0.0, 7.0]
+    assert not np.signbit(val[2])
+
+
+def test_greedy_argmax_brute_force():
+    """Against a plain loop over every element (strictly greater replaces)."""
+    rng = np.random.default_rng(3)
+    z = rng.integers(-4, 5, size=(6, 50)).astype(np.float32)   # many ties
+    idx, val = oracle.greedy_argmax(z)
+    for m in range(z.shape[0]):
+        best = 0
+        for v in range(1, z.shape[1]):
+            if z[m, v] > z[m, best]:
+                best = v
+        assert idx[m] == best and val[m] == z[m, best]
+
+
+def test_head_i8_logits_f32_order_and_exactness():
+    """Unit scales give the integer sums exactly; otherwise the value is the
+    fp32 rounding of the fp32 scale product times acc, within one rounding of
+    the exact fp64 logit and never further."""
+    rng = np.random.default_rng(4)
+    v, k, m = 300, 256, 3
+    w = rng.integers(-127, 128, size=(v, k)).astype(np.int8)
+    q = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    rs = rng.uniform(0.002, 0.02, v).astype(np.float32)
+    sx = rng.uniform(0.005, 0.05, m).astype(np.float32)
+    acc, y64, _ = oracle.head_i8(w, rs, q, sx)
+    ones = oracle.head_i8_logits_f32(acc, np.ones(v, np.float32), np.ones(m, np.float32))
+    assert np.array_equal(ones, acc.astype(np.float32))
+    y = oracle.head_i8_logits_f32(acc, rs, sx).astype(np.float64)
+    # two fp32 roundings: |y - y64| <= ~2^-23 |y64|
+    assert np.all(np.abs(y - y64) <= 2.5 * 2.0 ** -24 * np.abs(y64) + 1e-30)
+    want = (np.float32(rs[5]) * np.float32(sx[1])) * np.float32(acc[1, 5])
+    assert y[1, 5] == np.float64(np.float32(want))
+
+
 def test_parameter_counts_match_pages():
     """Shapes reproduce the parameter accounting on the discuss.pytorch.kr page
     (table in "세 모델과 하나의 컨테이너" and section "파라미터와 바이트는 서로 다른 회계다")."""
