@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
                     help="--mode prefill: run only this shape and M (e.g. gate:2048)")
-    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "copy"],
+    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "copy"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
                          "copy: plain 256 MiB device copies (reference for memory-counter scaling)")
@@ -355,6 +355,35 @@ def mode_prefill(args, tw, synth, torch):
     print(json.dumps({"mode": "prefill", "peak_tops": INT8_PEAK_TOPS, "rows": out}), flush=True)
 
 
+def mode_head(args, tw, synth, torch):
+    """The int8 head (151936 x 4096 at --config 2, x 1024 at --config 1) alone and fused with
+    the greedy argmax, bf16 and int8 activations, M = 1: us per call and GB/s of weights+scales."""
+    w, rs, xh = synth.head_inputs(args.config)
+    v, k = w.shape
+    W, RS = torch.from_numpy(w).cuda(), torch.from_numpy(rs).cuda()
+    copies = [W] + [W.clone() for _ in range(2)]          # 3 x 622 MB: every call streams from HBM
+    x = torch.from_numpy(xh.view(np.int16)).cuda()
+    q, sx = tw.tern_quantize_i8(x)
+    y = torch.empty((1, v), dtype=torch.float32, device="cuda")
+    ws = tw.i8_head_argmax_workspace(v, 1)
+    runs = {
+        "head_bf16": lambda c: tw.i8_head_gemv(c, RS, x, y=y),
+        "head_int8": lambda c: tw.i8_head_gemv_i8(c, RS, q, sx, y=y),
+        "head_argmax_bf16": lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws),
+        "head_argmax_bf16_with_logits": lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws, logits=y),
+        "head_argmax_int8": lambda c: tw.i8_head_argmax_i8(c, RS, q, sx, workspace=ws),
+    }
+    out = []
+    for name, fn in runs.items():
+        g = capture(torch, lambda: [fn(c) for c in copies])
+        ms = time_replays(torch, g, 5) / len(copies)
+        nbytes = v * k + 4 * v
+        out.append({"call": name, "V": v, "K": k, "us": round(ms * 1e3, 2),
+                    "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del g
+    print(json.dumps({"mode": "head", "rows": out}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -372,6 +401,8 @@ def main():
         return mode_smallm(args, tw, synth, torch)
     if args.mode == "prefill":
         return mode_prefill(args, tw, synth, torch)
+    if args.mode == "head":
+        return mode_head(args, tw, synth, torch)
     if args.mode == "copy":
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

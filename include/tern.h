@@ -164,12 +164,14 @@ int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t 
  *   [M][K] with M*(2K+16) (bf16) or M*(K+16) (int8) <= 163840 bytes;
  *   1 <= M <= TERN_MAX_M_GEMV;  idx int32 [M];  val fp32 [M];
  *   logits NULL or fp32 [M][V] (written when given);
- *   workspace: i8_head_argmax_workspace_bytes(M) bytes of device memory,
- *   8-byte aligned, owned by the caller; the call clears and uses it, so
- *   calls that share a workspace must not overlap in time.
+ *   workspace: i8_head_argmax_workspace_bytes(V, M) bytes of device memory
+ *   (8 bytes per 16 rows of W and activation row), 8-byte aligned, owned by
+ *   the caller; the call overwrites it, so calls that share a workspace must
+ *   not overlap in time.  Two kernels run: the head, whose waves leave one
+ *   key per 16 rows, and a reduction over those keys.
  * Errors: TERN_E_SHAPE for a shape outside these limits, TERN_E_NULL /
  * TERN_E_ALIGN for pointers; nothing is launched then. */
-int64_t i8_head_argmax_workspace_bytes(int64_t M);
+int64_t i8_head_argmax_workspace_bytes(int64_t V, int64_t M);
 int i8_head_argmax(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x, int64_t M,
                    int32_t* idx, float* val, float* logits, void* workspace, void* stream);
 int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,

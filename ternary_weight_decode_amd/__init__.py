@@ -64,7 +64,7 @@ def lib():
         L.tern_chain_plan.argtypes = [ctypes.POINTER(TernChainStep), _i64, _p, _i64, _p]
         L.tern_gemv_chain.argtypes = [_p, _i64, _p]
         L.i8_head_argmax_workspace_bytes.restype = _i64
-        L.i8_head_argmax_workspace_bytes.argtypes = [_i64]
+        L.i8_head_argmax_workspace_bytes.argtypes = [_i64, _i64]
         L.i8_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.i8_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         for name in _INT_STATUS:
@@ -192,14 +192,14 @@ def i8_head_gemv_i8(w, row_scale, q, s_x, y=None, acc=None, stream=None):
     return y
 
 
-def i8_head_argmax_workspace_bytes(m: int) -> int:
-    return int(lib().i8_head_argmax_workspace_bytes(m))
+def i8_head_argmax_workspace_bytes(v: int, m: int) -> int:
+    return int(lib().i8_head_argmax_workspace_bytes(v, m))
 
 
-def i8_head_argmax_workspace(m: int, device="cuda"):
-    """A workspace for i8_head_argmax[_i8] with up to m activation rows."""
+def i8_head_argmax_workspace(v: int, m: int, device="cuda"):
+    """A workspace for i8_head_argmax[_i8] over V head rows and up to m activation rows."""
     import torch
-    return torch.empty(i8_head_argmax_workspace_bytes(m), dtype=torch.uint8, device=device)
+    return torch.empty(i8_head_argmax_workspace_bytes(v, m), dtype=torch.uint8, device=device)
 
 
 def i8_head_argmax(w, row_scale, x, workspace=None, logits=None, stream=None):
@@ -210,7 +210,7 @@ def i8_head_argmax(w, row_scale, x, workspace=None, logits=None, stream=None):
     v, k = w.shape
     m = x.shape[0]
     if workspace is None:
-        workspace = i8_head_argmax_workspace(m, x.device)
+        workspace = i8_head_argmax_workspace(v, m, x.device)
     idx = torch.empty(m, dtype=torch.int32, device=x.device)
     val = torch.empty(m, dtype=torch.float32, device=x.device)
     _check("i8_head_argmax", lib().i8_head_argmax(_ptr(w), _ptr(row_scale), v, k, _ptr(x), m, _ptr(idx), _ptr(val),
@@ -226,7 +226,7 @@ def i8_head_argmax_i8(w, row_scale, q, s_x, workspace=None, logits=None, stream=
     v, k = w.shape
     m = q.shape[0]
     if workspace is None:
-        workspace = i8_head_argmax_workspace(m, q.device)
+        workspace = i8_head_argmax_workspace(v, m, q.device)
     idx = torch.empty(m, dtype=torch.int32, device=q.device)
     val = torch.empty(m, dtype=torch.float32, device=q.device)
     _check("i8_head_argmax_i8", lib().i8_head_argmax_i8(_ptr(w), _ptr(row_scale), v, k, _ptr(q), _ptr(s_x), m,

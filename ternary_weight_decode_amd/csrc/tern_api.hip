@@ -174,10 +174,10 @@ int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t 
     return finish(tern::launch_head_i8(W, row_scale, V, K, q, s_x, M, logits, acc_dbg, (hipStream_t)stream));
 }
 
-int64_t i8_head_argmax_workspace_bytes(int64_t M)
+int64_t i8_head_argmax_workspace_bytes(int64_t V, int64_t M)
 {
-    if (M < 1 || M > TERN_MAX_M_GEMV) return -1;
-    return 64 + 8 * M;
+    if (V < 1 || V > 0xFFFFFFF0ll || M < 1 || M > TERN_MAX_M_GEMV) return -1;
+    return (V + 15) / 16 * M * 8;
 }
 
 static int head_argmax_check(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const void* act,

@@ -162,15 +162,12 @@ __global__ __launch_bounds__(256) void head_kernel(const int8_t* __restrict__ W,
 // largest logit, the lowest v among equal logits (-0 counted as +0).  Each
 // logit becomes a 64-bit key {order-preserving bits of the value, ~v}, so one
 // unsigned maximum decides both.  Every wave reduces its 16 rows in
-// registers and publishes one key per m with a device-scope atomic maximum;
-// the wave that completes the count reads the keys back and writes the
-// results.  keys/count start at zero (the launcher clears them).
+// registers and stores one key per m in its own slot of the workspace
+// (row tile q, row m); a second kernel takes the maximum over the slots.  No
+// atomics and no fences: the launch boundary makes the slots visible, and the
+// result does not depend on the order in which waves finish.
 struct HeadArgmax {
-    unsigned long long* keys;   // [M], zero on entry
-    unsigned* count;            // zero on entry
-    int32_t* idx;               // [M]
-    float* val;                 // [M]
-    unsigned waves;             // waves that own a row tile (= row tiles)
+    unsigned long long* part;   // [row tiles][M] keys, or null: no argmax
 };
 
 __device__ __forceinline__ uint32_t order_bits(float f)
@@ -184,10 +181,10 @@ __device__ __forceinline__ float unorder_bits(uint32_t o)
     return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// The argmax epilogue of one wave: lane (r, g) holds logits lv[i] of row
-// v = tile*16 + r for activation rows m = 4g + i (valid when ok[i]).
+// The argmax epilogue of one wave (row tile q): lane (r, g) holds logits
+// lv[i] of row v = q*16 + r for activation rows m = 4g + i (valid when ok[i]).
 __device__ __forceinline__ void head_argmax_epilogue(const HeadArgmax& am, const float (&lv)[4], const bool (&ok)[4],
-                                                     int64_t v, int M, int lane)
+                                                     int64_t q, int64_t v, int M, int lane)
 {
     const int g = lane >> 4, r = lane & 15;
 #pragma unroll
@@ -200,19 +197,34 @@ __device__ __forceinline__ void head_argmax_epilogue(const HeadArgmax& am, const
             key = other > key ? other : key;
         }
         const int m = 4 * g + i;
-        if (r == 0 && m < M && key != 0) atomicMax(am.keys + m, (unsigned long long)key);
+        if (r == 0 && m < M) am.part[q * M + m] = key;
     }
-    __threadfence();
-    unsigned last = 0;
-    if (lane == 0) last = atomicAdd(am.count, 1u) == am.waves - 1 ? 1u : 0u;
-    last = __shfl(last, 0);
-    if (last) {
-        __threadfence();
-        if (lane < M) {
-            const uint64_t key = __hip_atomic_load(am.keys + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            am.idx[lane] = (int32_t)(0xFFFFFFFFu - (uint32_t)key);
-            am.val[lane] = unorder_bits((uint32_t)(key >> 32));
-        }
+}
+
+// Maximum over the row tiles' keys of activation row m = blockIdx.x.
+__global__ __launch_bounds__(1024) void head_argmax_finish_kernel(const unsigned long long* __restrict__ part,
+                                                                  int64_t nrt, int M, int32_t* __restrict__ idx,
+                                                                  float* __restrict__ val)
+{
+    __shared__ unsigned long long best_of_wave[16];
+    const int m = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    unsigned long long best = 0;
+    for (int64_t q = threadIdx.x; q < nrt; q += blockDim.x) {
+        const unsigned long long k = part[q * M + m];
+        best = k > best ? k : best;
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)best, off), hi = __shfl_xor((uint32_t)(best >> 32), off);
+        const unsigned long long other = ((unsigned long long)hi << 32) | lo;
+        best = other > best ? other : best;
+    }
+    if (lane == 0) best_of_wave[wave] = best;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int w = 1; w < (int)(blockDim.x >> 6); ++w) best = best_of_wave[w] > best ? best_of_wave[w] : best;
+        idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+        val[m] = unorder_bits((uint32_t)(best >> 32));
     }
 }
 
@@ -303,7 +315,7 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
             }
         }
     }
-    if (am.keys) head_argmax_epilogue(am, lv, ok, vo, M, lane);
+    if (am.part) head_argmax_epilogue(am, lv, ok, q, vo, M, lane);
 }
 
 static int head_chunk(int64_t K, int64_t M, int ebytes)
@@ -316,7 +328,7 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
 template <bool kInt8, int TPW>
 static hipError_t launch_head_fast(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                    const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream,
-                                   HeadArgmax am = HeadArgmax{nullptr, nullptr, nullptr, nullptr, 0})
+                                   HeadArgmax am = HeadArgmax{nullptr})
 {
     const size_t lds = (size_t)M * (K * (kInt8 ? 1 : 2) + 16);
     const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
@@ -355,7 +367,7 @@ hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K
 }
 
 // fused head + argmax: x (all M rows) must fit in LDS, as the single-pass
-// kernel stages it whole
+// kernel stages it whole; the workspace holds one key per (row tile, m)
 bool head_argmax_fits(int64_t K, int64_t M, bool int8_act)
 {
     return (size_t)M * (K * (int8_act ? 1 : 2) + 16) <= (size_t)160 * 1024;
@@ -366,12 +378,12 @@ static hipError_t launch_head_argmax(const int8_t* W, const float* rs, int64_t V
                                      const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                      hipStream_t stream)
 {
-    // workspace: count at byte 0, keys at byte 64; cleared by a kernel (no
-    // memset, so the call can be captured in a graph)
-    hipError_t e = launch_fill_zero(ws, 64 + 8 * M, stream);
+    const HeadArgmax am{(unsigned long long*)ws};
+    hipError_t e = launch_head_fast<kInt8, kHeadTpw>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
     if (e != hipSuccess) return e;
-    const HeadArgmax am{(unsigned long long*)((uint8_t*)ws + 64), (unsigned*)ws, idx, val, (unsigned)((V + 15) / 16)};
-    return launch_head_fast<kInt8, kHeadTpw>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
+    head_argmax_finish_kernel<<<dim3((unsigned)M), dim3(1024), 0, stream>>>((const unsigned long long*)ws,
+                                                                           (V + 15) / 16, (int)M, idx, val);
+    return hipGetLastError();
 }
 
 hipError_t launch_head_argmax_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x,

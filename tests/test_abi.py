@@ -102,9 +102,10 @@ def test_null_and_alignment_errors():
 
 def test_head_argmax_workspace_and_argument_errors():
     L = tw.lib()
-    assert tw.i8_head_argmax_workspace_bytes(1) == 72
-    assert tw.i8_head_argmax_workspace_bytes(16) == 64 + 128
-    assert tw.i8_head_argmax_workspace_bytes(0) == -1 and tw.i8_head_argmax_workspace_bytes(17) == -1
+    assert tw.i8_head_argmax_workspace_bytes(151936, 1) == 9496 * 8
+    assert tw.i8_head_argmax_workspace_bytes(100, 16) == 7 * 16 * 8
+    assert tw.i8_head_argmax_workspace_bytes(100, 0) == -1 and tw.i8_head_argmax_workspace_bytes(100, 17) == -1
+    assert tw.i8_head_argmax_workspace_bytes(0, 1) == -1
     p, m = ALIGNED, MISALIGNED
     f, fi = L.i8_head_argmax, L.i8_head_argmax_i8
     assert f(p, p, 100, 96, p, 1, p, p, None, p, None) == E_SHAPE          # K % 128

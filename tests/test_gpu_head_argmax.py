@@ -106,7 +106,7 @@ def test_head_argmax_reuses_its_workspace(tw):
     v, k, m = 7000, 1024, 2
     w, rs, x = head_inputs(v, k, m, seed=5)
     q, sx = oracle.quantize_i8(x)
-    ws = tw.i8_head_argmax_workspace(m)
+    ws = tw.i8_head_argmax_workspace(v, m)
     first = [host(t) for t in tw.i8_head_argmax_i8(dev(w), dev(rs), dev(q), dev(sx), workspace=ws)]
     for _ in range(3):
         again = [host(t) for t in tw.i8_head_argmax_i8(dev(w), dev(rs), dev(q), dev(sx), workspace=ws)]
