@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
                     help="--mode prefill: run only this shape and M (e.g. gate:2048)")
-    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "copy"],
+    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "fv5", "copy"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
                          "copy: plain 256 MiB device copies (reference for memory-counter scaling)")
@@ -384,6 +384,52 @@ def mode_head(args, tw, synth, torch):
     print(json.dumps({"mode": "head", "rows": out}), flush=True)
 
 
+FV5_UNITS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",)))
+
+
+def mode_fv5(args, tw, synth, torch):
+    """Five-level (FV5-style, 3.25 bits per weight) GEMV on the fused 8B linears of one layer
+    at M in {1, 4, 8, 16}, with the ternary GEMV of the same shapes beside it; weights rotate
+    over >= 1 GB of copies so each launch reads HBM.  Also the bytes-weighted M = 1 layer
+    aggregate (one layer = the four fused launches)."""
+    out, layer = [], {"fv5": [0.0, 0], "ternary": [0.0, 0]}
+    for label, projs in FV5_UNITS:
+        lins = [synth.Linear(2, 0, p, *synth.SHAPES_8B[p], synth.P_ZERO, synth.P_PLUS) for p in projs]
+        parts = [synth.linear5_inputs(lin) for lin in lins]
+        lv = np.concatenate([d[0] for d in parts], axis=0)
+        lo = np.concatenate([d[1] for d in parts], axis=0)
+        hi = np.concatenate([d[2] for d in parts], axis=0)
+        n, k = lv.shape
+        p5 = tw.tern5_pack(torch.from_numpy(lv).cuda(), torch.from_numpy(lo).cuda(), torch.from_numpy(hi).cuda())
+        t = np.clip(lv, -1, 1)
+        s16 = np.repeat(lo, 2, axis=1).astype(np.float16).view(np.int16)
+        p3 = tw.tern_pack(torch.from_numpy(t).cuda(), torch.from_numpy(s16).cuda())
+        del lv, lo, hi, parts, t
+        x16 = torch.from_numpy(synth.gen_x_bf16(np.random.default_rng(5), 16, k).view(np.int16)).cuda()
+        for fmt, packed, nbytes_w, call in (("fv5", p5, tw.tern5_packed_bytes(n, k), tw.tern5_gemv),
+                                           ("ternary", p3, tw.tern_packed_bytes(n, k), tw.tern_gemv)):
+            copies = rotate_copies(torch, packed)
+            for m in (1, 4, 8, 16):
+                x = x16[:m].contiguous()
+                y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+                g = capture(torch, lambda: [call(c, n, k, x, y=y) for c in copies])
+                ms = time_replays(torch, g, 5) / len(copies)
+                nbytes = nbytes_w + 2 * m * k + 4 * m * n
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                out.append({"unit": label, "format": fmt, "n_k": [n, k], "M": m, "us": round(ms * 1e3, 2),
+                            "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+                if m == 1:
+                    layer[fmt][0] += ms * 1e3
+                    layer[fmt][1] += nbytes
+                del g
+            del copies
+        del p5, p3
+    agg = {fmt: {"us_per_layer": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),
+                 "pct_hbm_peak": round(100 * b / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 1)}
+           for fmt, (us, b) in layer.items()}
+    print(json.dumps({"mode": "fv5", "rows": out, "layer_m1": agg}), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -403,6 +449,8 @@ def main():
         return mode_prefill(args, tw, synth, torch)
     if args.mode == "head":
         return mode_head(args, tw, synth, torch)
+    if args.mode == "fv5":
+        return mode_fv5(args, tw, synth, torch)
     if args.mode == "copy":
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)

@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 3
+#define TERN_ABI_VERSION 4
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -240,6 +240,47 @@ int tern_chain_plan(const tern_chain_step* steps, int64_t nsteps, void* workspac
  * hold them.  Every wait inside is bounded (a stalled run ends after seconds
  * and counts an error, see tern_chain_workspace_bytes). */
 int tern_gemv_chain(void* workspace, int64_t nsteps, void* stream);
+
+/* ---- five-level weights (FV5-style) ----
+ *
+ * The GGUF pack of the pages stores every attention and MLP linear as FV5:
+ * blocks of 256 weights with two f32 scales (s_lo, s_hi) and three 32-byte
+ * bit-planes, 3.25 bits per weight ([P2] section "FV5와 FV5B", the block
+ * table); the page reads the planes as sign, zero and two magnitude steps.
+ * This library takes that reading as five levels l in {-2, -1, 0, +1, +2}:
+ *   W[n][k] = sign(l) * (|l| == 2 ? s_hi[n][b] : s_lo[n][b]),  b = k/256,
+ * and W = 0 where l = 0.  Its bit layout ("five-level blob") is its own:
+ *   K % 512 == 0; rows padded to Np = 16*ceil(N/16); planes p = 0 nonzero
+ *   (l != 0), 1 sign (l < 0), 2 high (|l| == 2), each 256 bits of a block
+ *   as eight little-endian 32-bit words, word w holding weights
+ *   k = 256b + 32w + i with weight i at bit 16*(i&1) + (i>>1).  With
+ *   rt = n/16, r = n%16, kt = b/2, bh = b%2, nkt = K/512, g = w%4,
+ *   j = 2*bh + w/4:
+ *     word index = ((rt*nkt + kt)*3 + p)*256 + (g*16 + r)*4 + j
+ *     (byte offset = 4*index; Np*K*3/8 bytes of planes)
+ *   then f32 scales from byte Np*K*3/8: s_lo of (n, b) at element
+ *   ((rt*nkt + kt)*16 + r)*4 + 2*bh, s_hi at the next element.
+ *   Canonical form: sign = high = 0 wherever nonzero = 0 (tern5_pack emits
+ *   it; the GEMV reads a high or sign bit only where nonzero is set). */
+
+/* Bytes of the five-level blob of W[N][K]: Np*K*3/8 + Np*(K/256)*8, or -1
+ * for N < 0, K < 0 or K % 512 != 0. */
+int64_t tern5_packed_bytes(int64_t N, int64_t K);
+
+/* Pack levels int8 [N][K] (values in [-2, 2]; others are clamped to that
+ * range) and f32 scales s_lo, s_hi [N][K/256] into a blob of
+ * tern5_packed_bytes(N, K) bytes (every byte written, padding rows as zeros).
+ * levels and packed 16-byte aligned, scales 4-byte aligned. */
+int tern5_pack(const int8_t* levels, const float* s_lo, const float* s_hi, int64_t N, int64_t K, void* packed,
+               void* stream);
+
+/* y[m][n] = sum_k W[n][k] * x[m][k] for the five-level W, fp32 accumulation
+ * on the matrix cores (bf16 x times 2*sign(l) exactly, the two scales of a
+ * block applied once to their fp32 sums).
+ *   packed  tern5_pack blob of W[N][K], K % 512 == 0
+ *   x       bf16 bits [M][K], 1 <= M <= TERN_MAX_M_GEMV, 16-byte aligned
+ *   y       fp32 [M][N], 4-byte aligned */
+int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream);
 
 #ifdef __cplusplus
 }

@@ -134,13 +134,19 @@ def dense(levels, s_lo, s_hi) -> np.ndarray:
     return np.sign(levels) * mag * (levels != 0)
 
 
-def gemv_bf16(packed, n: int, k: int, x_bf16, rows=None):
-    """y[m][n] = sum_k w[n][k] * x[m][k] in fp64 with x given as bf16 bits;
-    rows (optional) selects output rows.  Returns (y64, y32)."""
-    levels, s_lo, s_hi = unpack(packed, n, k) if rows is None else _unpack_rows(packed, n, k, rows)
+def gemv_bf16_levels(levels, s_lo, s_hi, x_bf16):
+    """y[m][n] = sum_k w[n][k] * x[m][k] in fp64 from unpacked levels and
+    scales, x given as bf16 bits.  Returns (y64, y32)."""
     x = (np.asarray(x_bf16, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     y64 = x @ dense(levels, s_lo, s_hi).T
     return y64, y64.astype(np.float32)
+
+
+def gemv_bf16(packed, n: int, k: int, x_bf16, rows=None):
+    """The same product read from a packed blob; rows (optional) selects
+    output rows.  Returns (y64, y32)."""
+    levels, s_lo, s_hi = unpack(packed, n, k) if rows is None else _unpack_rows(packed, n, k, rows)
+    return gemv_bf16_levels(levels, s_lo, s_hi, x_bf16)
 
 
 def _unpack_rows(packed, n, k, rows):

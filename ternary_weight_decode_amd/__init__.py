@@ -11,7 +11,9 @@ fails to load, every call raises.
 Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 ``tern_gemv``, ``tern_gemv_i8``, ``i8_head_gemv``, ``i8_head_gemv_i8``,
 ``tern_gemm_prefill``, ``tern_packed_bytes``, and the dependent-GEMV chain
-``tern_chain_workspace_bytes``, ``tern_chain_plan``, ``tern_gemv_chain``.
+``tern_chain_workspace_bytes``, ``tern_chain_plan``, ``tern_gemv_chain``, the
+fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
+(FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv``.
 """
 from __future__ import annotations
 
@@ -23,10 +25,10 @@ MAX_M_GEMV = 16
 SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
-           "i8_head_argmax", "i8_head_argmax_i8")
+           "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
-               "i8_head_argmax_i8")
+               "i8_head_argmax_i8", "tern5_pack", "tern5_gemv")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -67,6 +69,10 @@ def lib():
         L.i8_head_argmax_workspace_bytes.argtypes = [_i64, _i64]
         L.i8_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.i8_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
+        L.tern5_packed_bytes.restype = _i64
+        L.tern5_packed_bytes.argtypes = [_i64, _i64]
+        L.tern5_pack.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
+        L.tern5_gemv.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -297,3 +303,38 @@ def tern_chain_errors(workspace) -> int:
     """Count of aborted waits recorded in a chain workspace (0 in normal operation)."""
     import torch
     return int(workspace[8:12].view(torch.int32).item())
+
+
+# ---------------------------------------------------------------- five-level
+
+def tern5_packed_bytes(n: int, k: int) -> int:
+    return int(lib().tern5_packed_bytes(n, k))
+
+
+def tern5_pack(levels, s_lo, s_hi, out=None, stream=None):
+    """levels int8 [N,K] in [-2,2], K % 512 == 0; s_lo, s_hi fp32 [N,K/256] -> five-level uint8 blob."""
+    import torch
+    _need(levels, "levels", (torch.int8,), 2)
+    _need(s_lo, "s_lo", (torch.float32,), 2)
+    _need(s_hi, "s_hi", (torch.float32,), 2)
+    n, k = levels.shape
+    if tuple(s_lo.shape) != (n, k // 256) or tuple(s_hi.shape) != (n, k // 256):
+        raise RuntimeError("tern5_pack: s_lo and s_hi must be [N, K/256]")
+    nbytes = tern5_packed_bytes(n, k)
+    if nbytes < 0:
+        _check("tern5_pack", 2)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.uint8, device=levels.device)
+    _check("tern5_pack", lib().tern5_pack(_ptr(levels), _ptr(s_lo), _ptr(s_hi), n, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def tern5_gemv(packed, n: int, k: int, x, y=None, stream=None):
+    """y[m,n] = sum_k W[n,k] x[m,k] for the five-level W; x bf16 [M,K], M <= 16 -> y fp32 [M,N]."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=x.device)
+    _check("tern5_gemv", lib().tern5_gemv(_ptr(packed), n, k, _ptr(x), m, _ptr(y), _stream(stream)))
+    return y

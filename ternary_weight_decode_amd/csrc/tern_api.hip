@@ -338,3 +338,37 @@ int tern_gemv_chain(void* workspace, int64_t nsteps, void* stream)
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int64_t tern5_packed_bytes(int64_t N, int64_t K)
+{
+    if (N < 0 || K < 0 || K % 512 != 0) return -1;
+    return tern::npad16(N) * K * 3 / 8 + tern::npad16(N) * (K / 256) * 8;
+}
+
+int tern5_pack(const int8_t* levels, const float* s_lo, const float* s_hi, int64_t N, int64_t K, void* packed,
+               void* stream)
+{
+    if (N < 0 || K < 0 || K % 512 != 0) return TERN_E_SHAPE;
+    if (N == 0 || K == 0) return TERN_OK;
+    if (!levels || !s_lo || !s_hi || !packed) return TERN_E_NULL;
+    if (!aligned16(levels) || !aligned16(packed) || !aligned4(s_lo) || !aligned4(s_hi)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_pack5(levels, s_lo, s_hi, N, K, (uint8_t*)packed, (hipStream_t)stream));
+}
+
+int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream)
+{
+    if (N < 0 || K < 0 || K % 512 != 0 || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (N == 0 || M == 0) return TERN_OK;
+    if (!y || (K > 0 && (!packed || !x))) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || (x && !aligned16(x)) || !aligned4(y)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
+    return finish(tern::launch_gemv5_bf16((const uint8_t*)packed, N, K, x, M, y, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -17,6 +17,7 @@
 // non-temporal 16-byte loads.
 #include "tern_device.h"
 #include "tern_launch.h"
+#include "tern_oneshot.h"
 #include "tern_tile.h"
 
 namespace tern {
@@ -485,7 +486,7 @@ static int pick_chunk(int64_t K, int64_t M, int64_t bytes_per_elem)
     return (int)(kr < cap ? kr : cap);
 }
 
-static constexpr int64_t kFastLds = 160 * 1024;     // LDS budget of the fast path (all of a CU's LDS)
+static constexpr int64_t kFastLds = kCuLds;     // LDS budget of the fast path (all of a CU's LDS)
 
 // waves per workgroup and k-tiles in flight per wave for the fast path
 // (nw never exceeds the number of k-tiles, so every wave works on every row
@@ -497,14 +498,6 @@ static void pick_fast(int64_t nkt, int& nw, int& tpw)
 {
     nw = nkt >= 16 ? 16 : (nkt >= 8 ? 8 : (nkt >= 4 ? 4 : (int)(nkt < 1 ? 1 : nkt)));
     tpw = 1;
-}
-
-static int device_cus()
-{
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
-    return cus;
 }
 
 // Workgroups that stay resident at once for this kernel instance (the grid of
@@ -538,42 +531,13 @@ static hipError_t launch_fast_mt(int tpw, int nw, size_t lds, hipStream_t stream
     return launch_fast<MT, 1>(nw, lds, stream, packed, N, K, x, M, y);
 }
 
-// One-shot configuration.  R row tiles per workgroup is chosen to minimise
-// the largest number of units any CU receives (the critical path), and among
-// equals to bring a workgroup closest to 16 units; waves take 2 units each
-// (1 when a workgroup has at most 8), so the second unit's loads overlap the
-// first unit's compute.  Measured on the 8B shapes at M = 1 (hipGraph of 36
-// launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
-// (R = 3, 12 waves) and 9.17 us (R = 6, 16 waves); 6144x4096 4.58 us with
-// R = 2 vs 4.87 us with R = 1; 4096x12288 5.64 us with 12 waves x 2 units vs
-// 6.16 us with 8 x 3.
-struct OneShot {
-    int R, nw, U, XC;
-    int64_t grid;
-    size_t lds;
-};
-
-template <bool kI8, int MT, int U, int XC>
-static bool oneshot_fits(const OneShot& c)
-{
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemv_oneshot_kernel<kI8, MT, U, XC>, 64 * c.nw, c.lds) !=
-            hipSuccess ||
-        per_cu <= 0)
-        return false;
-    return c.grid <= (int64_t)per_cu * device_cus();
-}
-
-// Dispatch on (U, XC); returns hipErrorNotSupported when the configuration
-// is not instantiated or would not be resident in one round (then another
-// path runs).
 template <bool kI8, int MT>
 static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
                                    const void* x, const float* s_x, int M, float* y, int32_t* acc)
 {
 #define TERN_ONESHOT_CASE(UU, XX)                                                                              \
     if (c.U == UU && c.XC == XX) {                                                                             \
-        if (!oneshot_fits<kI8, MT, UU, XX>(c)) return hipErrorNotSupported;                                   \
+        if (!oneshot_resident(gemv_oneshot_kernel<kI8, MT, UU, XX>, c)) return hipErrorNotSupported;          \
         gemv_oneshot_kernel<kI8, MT, UU, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(      \
             packed, N, K, x, s_x, M, y, acc);                                                                  \
         return hipGetLastError();                                                                              \
@@ -588,65 +552,11 @@ static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const u
     return hipErrorNotSupported;
 }
 
-// units per wave for a workgroup of `units` units
-static int64_t oneshot_u(int64_t units)
+// The ternary instances with M <= 4 use 56-65, 62-70, 75-81 and 87-91 VGPRs
+// for U = 1..4 (the occupancy query has the last word).
+static OneShotShape oneshot_shape(int64_t K, bool i8)
 {
-    return units <= 8 ? 1 : ((units + 15) / 16 > 2 ? (units + 15) / 16 : 2);
-}
-
-// One-pass configuration.  R row tiles per workgroup is chosen to minimise
-// the largest number of units any CU receives (the critical path), and among
-// equals to bring a workgroup closest to 16 units; waves take 2 units each
-// (1 when a workgroup has at most 8), so the second unit's loads overlap the
-// first unit's compute.  Measured on the 8B shapes at M = 1 (hipGraph of 36
-// launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
-// (R = 3, 12 waves) and 9.17 us (R = 6, 16 waves); 6144x4096 4.58 us with
-// R = 2 vs 4.87 us with R = 1; 4096x12288 5.64 us with 12 waves x 2 units vs
-// 6.16 us with 8 x 3.
-static bool pick_oneshot(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
-{
-    if (K % kTileK != 0 || M > 16) return false;
-    const int64_t nkt = K / kTileK, nrt = (N + 15) / 16;
-    const int64_t cus = device_cus();
-    // waves per SIMD that fit next to each other for U = 1..4 units per wave
-    // (the M <= 4 bf16 instances use 56-65, 62-70, 75-81 and 87-91 VGPRs;
-    // the occupancy query below has the last word)
-    static const int64_t kWavesPerSimd[5] = {0, 8, 7, 6, 5};
-    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    const size_t x_lds = (size_t)M * (i8 ? K + 16 : (K + 8) * 2);
-    auto lds_of = [&](int64_t units) { return x_lds + (size_t)(units + 1) * ni * 64 * 4; };
-    int64_t best_max = -1, best_dist = 0;
-    c.R = 0;
-    for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
-        const int64_t units = R * nkt, U = oneshot_u(units);
-        if (U > 4) break;
-        const int64_t nw = (units + U - 1) / U;
-        const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
-        if (per_cu * nw > 4 * kWavesPerSimd[U]) continue;                      // not resident in one round
-        if ((size_t)per_cu * lds_of(units) > (size_t)kFastLds) continue;       // LDS of the workgroups on a CU
-        const int64_t max_units = per_cu * units;
-        const int64_t dist = units > 16 ? units - 16 : 16 - units;
-        if (best_max < 0 || max_units < best_max || (max_units == best_max && dist < best_dist)) {
-            best_max = max_units;
-            best_dist = dist;
-            c.R = R;
-        }
-        if (grid == 1) break;
-    }
-    if (c.R == 0) return false;
-    const int64_t units = c.R * nkt;
-    c.U = (int)oneshot_u(units);
-    c.nw = (int)((units + c.U - 1) / c.U);
-    c.grid = (nrt + c.R - 1) / c.R;
-    const int64_t chunk = i8 ? 32 : 16;
-    const int64_t row_bytes = i8 ? K : 2 * K;
-    const int64_t xc = (M * (row_bytes / chunk) + 64 * c.nw - 1) / (64 * c.nw);
-    // 8 chunks run on the MT = 16 kernel, whose partials hold 4 rows per lane
-    // group: not for M <= 2, whose partial area is sized for 1 or 2
-    if (xc > 8 || (xc > 4 && M <= 2)) return false;
-    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
-    c.lds = lds_of(units);
-    return c.lds <= (size_t)kFastLds;
+    return OneShotShape{i8 ? K + 16 : (K + 8) * 2, i8 ? K : 2 * K, i8 ? 32 : 16, {0, 8, 7, 6, 5}};
 }
 
 // the one-pass path for M <= 16 when it applies; hipErrorNotSupported otherwise
@@ -654,7 +564,7 @@ static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int6
                                  int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     OneShot c;
-    if (!pick_oneshot(N, K, M, i8, c)) return hipErrorNotSupported;
+    if (!pick_oneshot(N, K, M, oneshot_shape(K, i8), c)) return hipErrorNotSupported;
     const int m = (int)M;
     // 8 activation chunks per thread are instantiated for the MT = 16 kernel
     // only, which computes the same rows as MT = 4 (4 per lane group)

@@ -68,6 +68,12 @@ hipError_t launch_chain_plan(const ChainStep* steps, int nsteps, uint8_t* ws, in
 hipError_t launch_chain(uint8_t* ws, int nsteps, hipStream_t stream);
 hipError_t chain_grid(int* grid);
 
+// ---- five-level (FV5-style) weights ----
+hipError_t launch_pack5(const int8_t* lv, const float* s_lo, const float* s_hi, int64_t N, int64_t K,
+                        uint8_t* packed, hipStream_t stream);
+hipError_t launch_gemv5_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                             hipStream_t stream);
+
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream);
 

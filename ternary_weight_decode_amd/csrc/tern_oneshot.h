@@ -1,0 +1,106 @@
+// tern_oneshot.h — launch configuration of the one-pass GEMV kernels (the
+// ternary and the five-level formats share it).
+//
+// A unit is one 16-row tile x one 512-k tile.  A workgroup owns R row tiles
+// (every R-th of the grid) and its waves take U units each, all loads issued
+// up front; activations are staged once in LDS and each unit leaves its fp32
+// partial in LDS, summed afterwards in k-tile order.  The whole grid must be
+// resident in one round.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tern {
+
+constexpr int64_t kCuLds = 160 * 1024;     // LDS of one gfx950 CU
+
+inline int device_cus()
+{
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return 256;
+    return cus;
+}
+
+struct OneShot {
+    int R, nw, U, XC;
+    int64_t grid;
+    size_t lds;
+};
+
+// units per wave for a workgroup of `units` units
+inline int64_t oneshot_u(int64_t units)
+{
+    return units <= 8 ? 1 : ((units + 15) / 16 > 2 ? (units + 15) / 16 : 2);
+}
+
+// Activation staging and partials of one workgroup.
+struct OneShotShape {
+    int64_t x_row_bytes;      // staged LDS bytes per activation row
+    int64_t x_src_bytes;      // bytes of one activation row in global memory
+    int64_t chunk_bytes;      // activation bytes one thread loads per chunk
+    int64_t waves_per_simd[5];// waves of U = 1..4 units that fit on a SIMD (registers)
+};
+
+// R row tiles per workgroup is chosen to minimise the largest number of
+// units any CU receives (the critical path), and among equals to bring a
+// workgroup closest to 16 units; waves take 2 units each (1 when a workgroup
+// has at most 8), so the second unit's loads overlap the first unit's
+// compute.  Measured on the 8B ternary shapes at M = 1 (hipGraph of 36
+// launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
+// (R = 3, 12 waves) and 9.17 us (R = 6, 16 waves); 6144x4096 4.58 us with
+// R = 2 vs 4.87 us with R = 1; 4096x12288 5.64 us with 12 waves x 2 units vs
+// 6.16 us with 8 x 3.  Returns false when no configuration fits (another
+// path runs then).
+inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s, OneShot& c)
+{
+    if (K % 512 != 0 || M > 16) return false;
+    const int64_t nkt = K / 512, nrt = (N + 15) / 16;
+    const int64_t cus = device_cus();
+    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
+    const size_t x_lds = (size_t)(M * s.x_row_bytes);
+    auto lds_of = [&](int64_t units) { return x_lds + (size_t)(units + 1) * ni * 64 * 4; };
+    int64_t best_max = -1, best_dist = 0;
+    c.R = 0;
+    for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
+        const int64_t units = R * nkt, U = oneshot_u(units);
+        if (U > 4) break;
+        const int64_t nw = (units + U - 1) / U;
+        const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
+        if (per_cu * nw > 4 * s.waves_per_simd[U]) continue;                  // not resident in one round
+        if ((size_t)per_cu * lds_of(units) > (size_t)kCuLds) continue;       // LDS of the workgroups on a CU
+        const int64_t max_units = per_cu * units;
+        const int64_t dist = units > 16 ? units - 16 : 16 - units;
+        if (best_max < 0 || max_units < best_max || (max_units == best_max && dist < best_dist)) {
+            best_max = max_units;
+            best_dist = dist;
+            c.R = R;
+        }
+        if (grid == 1) break;
+    }
+    if (c.R == 0) return false;
+    const int64_t units = c.R * nkt;
+    c.U = (int)oneshot_u(units);
+    c.nw = (int)((units + c.U - 1) / c.U);
+    c.grid = (nrt + c.R - 1) / c.R;
+    const int64_t xc = (M * (s.x_src_bytes / s.chunk_bytes) + 64 * c.nw - 1) / (64 * c.nw);
+    // 8 chunks run on the MT = 16 kernels, whose partials hold 4 rows per
+    // lane group: not for M <= 2, whose partial area is sized for 1 or 2
+    if (xc > 8 || (xc > 4 && M <= 2)) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+    c.lds = lds_of(units);
+    return c.lds <= (size_t)kCuLds;
+}
+
+// true when `grid` workgroups of this kernel instance are resident at once
+template <typename F>
+inline bool oneshot_resident(F kern, const OneShot& c)
+{
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * c.nw, c.lds) != hipSuccess || per_cu <= 0)
+        return false;
+    return c.grid <= (int64_t)per_cu * device_cus();
+}
+
+}  // namespace tern

@@ -117,6 +117,38 @@ def gen_head(rng_w: np.random.Generator, rng_s: np.random.Generator, v: int, k: 
     return w, rs
 
 
+P_HIGH5 = 0.25             # five-level weights: share of nonzero weights at magnitude 2
+
+
+def gen_levels5(rng: np.random.Generator, n: int, k: int, p_zero: float = P_ZERO,
+                p_high: float = P_HIGH5) -> np.ndarray:
+    """Five-level weights in {-2..2} from one U[0,1) draw u per weight: zero for
+    u < p_zero; the rest, rescaled to v in [0,1), is -2 / +2 / -1 / +1 on the
+    intervals split at p_high/2, p_high and (1 + p_high)/2."""
+    u = np.empty((n, k), dtype=np.float64)
+    rng.random(out=u)
+    v = (u - p_zero) / (1.0 - p_zero)
+    out = np.where(v < (1.0 + p_high) / 2, -1, 1)
+    out = np.where(v < p_high, 2, out)
+    out = np.where(v < p_high / 2, -2, out)
+    return np.where(u < p_zero, 0, out).astype(np.int8)
+
+
+def gen_scales5(rng: np.random.Generator, n: int, nblocks: int):
+    """fp32 (s_lo, s_hi) per 256-weight block: s_lo U[0.01, 0.05], s_hi = s_lo * U[1.5, 2.5]."""
+    lo = rng.uniform(0.01, 0.05, size=(n, nblocks))
+    hi = lo * rng.uniform(1.5, 2.5, size=(n, nblocks))
+    return lo.astype(np.float32), hi.astype(np.float32)
+
+
+def linear5_inputs(lin: Linear, m: int = 1):
+    """Five-level weights of a linear (same seeds and zero share as the ternary states)."""
+    lv = gen_levels5(rng_for(lin.config, lin.layer, lin.pid, 0), lin.n, lin.k, lin.p_zero)
+    lo, hi = gen_scales5(rng_for(lin.config, lin.layer, lin.pid, 1), lin.n, lin.k // 256)
+    x = gen_x_bf16(rng_for(lin.config, lin.layer, lin.pid, 2), m, lin.k)
+    return lv, lo, hi, x
+
+
 def config0_inputs():
     """Single 3072x1024 ternary linear (0.6B gate shape), M=1, one generator seeded 0,
     drawn in the order ternary states -> scales -> activations."""

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 3
+    assert L.tern_abi_version() == 4
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -120,6 +120,32 @@ def test_head_argmax_workspace_and_argument_errors():
     assert f(m, p, 100, 128, p, 1, p, p, None, p, None) == E_ALIGN
     assert f(p, p, 100, 128, p, 1, p, p, ctypes.c_void_p(0x10002), p, None) == E_ALIGN   # logits
     assert f(p, p, 100, 128, p, 1, p, p, None, ctypes.c_void_p(0x10004), None) == E_ALIGN
+
+
+def test_five_level_sizes_and_argument_errors():
+    L = tw.lib()
+    # planes Np*K*3/8 then Np*(K/256) pairs of f32 scales (3.25 bits per weight)
+    assert tw.tern5_packed_bytes(16, 512) == 3072 + 16 * 2 * 8
+    assert tw.tern5_packed_bytes(12288, 4096) == 12288 * 4096 * 13 // 32
+    assert tw.tern5_packed_bytes(17, 1024) == 13312
+    assert tw.tern5_packed_bytes(0, 512) == 0
+    assert tw.tern5_packed_bytes(16, 768) == -1 and tw.tern5_packed_bytes(-1, 512) == -1
+    p, m = ALIGNED, MISALIGNED
+    g, pk = L.tern5_gemv, L.tern5_pack
+    assert g(p, 16, 768, p, 1, p, None) == E_SHAPE            # K % 512
+    assert g(p, 16, 512, p, 17, p, None) == E_SHAPE           # M > 16
+    assert g(p, -1, 512, p, 1, p, None) == E_SHAPE
+    assert pk(p, p, p, 16, 256, p, None) == E_SHAPE
+    assert g(None, 0, 512, None, 1, None, None) == E_OK
+    assert g(None, 16, 512, None, 0, None, None) == E_OK
+    assert pk(None, None, None, 0, 512, None, None) == E_OK
+    assert g(None, 16, 512, p, 1, p, None) == E_NULL
+    assert g(p, 16, 512, p, 1, None, None) == E_NULL
+    assert g(m, 16, 512, p, 1, p, None) == E_ALIGN
+    assert g(p, 16, 512, m, 1, p, None) == E_ALIGN
+    assert pk(p, None, p, 16, 512, p, None) == E_NULL
+    assert pk(m, p, p, 16, 512, p, None) == E_ALIGN
+    assert pk(p, p, ctypes.c_void_p(0x10002), 16, 512, p, None) == E_ALIGN
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):
