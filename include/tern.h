@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 4
+#define TERN_ABI_VERSION 5
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -281,6 +281,48 @@ int tern5_pack(const int8_t* levels, const float* s_lo, const float* s_hi, int64
  *   x       bf16 bits [M][K], 1 <= M <= TERN_MAX_M_GEMV, 16-byte aligned
  *   y       fp32 [M][N], 4-byte aligned */
 int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream);
+
+/* ---- block-scaled int8 tensors (FV5B-style) ----
+ *
+ * The GGUF pack of the pages stores the token embedding and the output head
+ * as FV5B: blocks of 256 int8 weights with one f32 scale, 8.125 bits per
+ * weight ([P2] section "FV5와 FV5B", the block table); embedding and head
+ * stay int8 ([P2] section "3진 계열이라는 이름의 실체").  Storage here:
+ * W int8 [V][K] row-major (16-byte aligned) and S f32 [V][K/256]; the
+ * weight is W[v][k] * S[v][k/256].  The head calls stage all of x in LDS:
+ * they need K % 256 == 0, 1 <= M <= TERN_MAX_M_GEMV and M*(K*e + 16) <=
+ * 160 KiB (e = 2 for bf16 x, 1 for int8 q), else TERN_E_SHAPE; V <= 2^32-16. */
+
+/* logits[m][v] = sum_b S[v][b] * sum_{k in block b} W[v][k] * x[m][k], each
+ * block's sum in fp32 on the matrix cores, folded into the row total in
+ * block order.  x bf16 bits [M][K]; logits fp32 [M][V]. */
+int fv5b_head_gemv(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                   float* logits, void* stream);
+
+/* int8 activations: acc[m][v][b] = sum_{k in block b} W[v][k] * q[m][k]
+ * (exact int32), logits[m][v] = s_x[m] * sum_b S[v][b] * acc[m][v][b] (fp32).
+ * acc_dbg NULL or int32 [M][V][K/256]. */
+int fv5b_head_gemv_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
+                      int64_t M, float* logits, int32_t* acc_dbg, void* stream);
+
+/* The block-scaled head fused with greedy argmax, as i8_head_argmax: idx /
+ * val of the largest logit per activation row (lowest v among equal
+ * logits, -0 as +0); logits optional; the workspace is the one
+ * i8_head_argmax_workspace_bytes(V, M) sizes (8-byte aligned). */
+int fv5b_head_argmax(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                     int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
+                        int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+
+/* Embedding rows for M token ids (the step before the first linear):
+ *   out[m][k] = W[ids[m]][k] * S[ids[m]][k/256], one fp32 rounding;
+ *   out_bf16[m][k] = that value rounded to bf16, nearest-even (the
+ *   activation format of tern_gemv).
+ * ids int32 [M]; an id outside [0, V) gives a zero row (W is not read).
+ * out fp32 [M][K] and out_bf16 [M][K]: either may be NULL, not both; both
+ * 16-byte aligned.  K % 256 == 0; M >= 0 (M == 0 or K == 0: nothing). */
+int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M, float* out,
+               uint16_t* out_bf16, void* stream);
 
 #ifdef __cplusplus
 }

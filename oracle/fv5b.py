@@ -37,15 +37,25 @@ def _blocks(k: int) -> int:
     return k // 256
 
 
-def head_bf16(w8, s, x_bf16, rows=None):
-    """fp64 logits [M][rows] of the block-scaled int8 head for bf16 x; returns (y64, y32)."""
-    w8 = np.asarray(w8, dtype=np.int8)
-    v, k = w8.shape
-    nb = _blocks(k)
+def _row_chunks(v, rows, chunk=8192):
     r = np.arange(v) if rows is None else np.asarray(rows)
-    wd = w8[r].astype(np.float64) * np.repeat(np.asarray(s, dtype=np.float32)[r].astype(np.float64), 256, axis=1)
-    y64 = _x64(x_bf16) @ wd.T
-    assert wd.shape[1] == nb * 256
+    return [r[i:i + chunk] for i in range(0, len(r), chunk)] or [r]
+
+
+def head_bf16(w8, s, x_bf16, rows=None):
+    """fp64 logits [M][rows] of the block-scaled int8 head for bf16 x; returns
+    (y64, y32).  Rows are independent; they are taken in chunks to bound
+    memory."""
+    w8 = np.asarray(w8, dtype=np.int8)
+    s = np.asarray(s, dtype=np.float32)
+    v, k = w8.shape
+    _blocks(k)
+    x = _x64(x_bf16)
+    parts = []
+    for r in _row_chunks(v, rows):
+        wd = w8[r].astype(np.float64) * np.repeat(s[r].astype(np.float64), 256, axis=1)
+        parts.append(x @ wd.T)
+    y64 = np.concatenate(parts, axis=1)
     return y64, y64.astype(np.float32)
 
 
@@ -54,10 +64,12 @@ def head_acc_i8(w8, q, rows=None):
     w8 = np.asarray(w8, dtype=np.int8)
     v, k = w8.shape
     nb = _blocks(k)
-    r = np.arange(v) if rows is None else np.asarray(rows)
-    wb = w8[r].astype(np.int64).reshape(len(r), nb, 256)
     qb = np.asarray(q, dtype=np.int8).astype(np.int64).reshape(-1, nb, 256)
-    return np.einsum("mbk,vbk->mvb", qb, wb)
+    parts = []
+    for r in _row_chunks(v, rows):
+        wb = w8[r].astype(np.int64).reshape(len(r), nb, 256)
+        parts.append(np.einsum("mbk,vbk->mvb", qb, wb))
+    return np.concatenate(parts, axis=1)
 
 
 def head_i8(w8, s, q, s_x, rows=None):
@@ -98,7 +110,7 @@ def round_bf16(f32):
     as_f = lambda b: (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     x = f.astype(np.float64)
     d_lo, d_hi = np.abs(x - as_f(lo)), np.abs(as_f(hi) - x)
-    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (lo & 1 == 1))
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & ((lo & 1) == 1))
     return np.where(pick_hi, hi, lo).astype(np.uint16)
 
 

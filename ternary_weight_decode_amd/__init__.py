@@ -13,7 +13,9 @@ Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 ``tern_gemm_prefill``, ``tern_packed_bytes``, and the dependent-GEMV chain
 ``tern_chain_workspace_bytes``, ``tern_chain_plan``, ``tern_gemv_chain``, the
 fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
-(FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv``.
+(FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv``, and the
+block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
+``fv5b_head_argmax[_i8]``, ``fv5b_embed``.
 """
 from __future__ import annotations
 
@@ -25,10 +27,12 @@ MAX_M_GEMV = 16
 SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
-           "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv")
+           "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv",
+           "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
-               "i8_head_argmax_i8", "tern5_pack", "tern5_gemv")
+               "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "fv5b_head_gemv", "fv5b_head_gemv_i8",
+               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -73,6 +77,11 @@ def lib():
         L.tern5_packed_bytes.argtypes = [_i64, _i64]
         L.tern5_pack.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
         L.tern5_gemv.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
+        L.fv5b_head_gemv.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.fv5b_head_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        L.fv5b_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+        L.fv5b_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
+        L.fv5b_embed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -338,3 +347,79 @@ def tern5_gemv(packed, n: int, k: int, x, y=None, stream=None):
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _check("tern5_gemv", lib().tern5_gemv(_ptr(packed), n, k, _ptr(x), m, _ptr(y), _stream(stream)))
     return y
+
+
+# ------------------------------------------------- block-scaled int8 (FV5B)
+
+def _fv5b_args(w, s, act, act_dtypes):
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(s, "S", (torch.float32,), 2)
+    _need(act, "activations", act_dtypes, 2)
+    v, k = w.shape
+    if tuple(s.shape) != (v, k // 256):
+        raise RuntimeError("S must be [V, K/256]")
+    return v, k, act.shape[0]
+
+
+def fv5b_head_gemv(w, s, x, y=None, stream=None):
+    """logits[m,v] = sum_b S[v,b] sum_{k in b} W[v,k] x[m,k]; W int8 [V,K], S fp32 [V,K/256], x bf16 [M,K]."""
+    import torch
+    v, k, m = _fv5b_args(w, s, x, (torch.bfloat16, torch.int16, torch.uint16))
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=x.device)
+    _check("fv5b_head_gemv", lib().fv5b_head_gemv(_ptr(w), _ptr(s), v, k, _ptr(x), m, _ptr(y), _stream(stream)))
+    return y
+
+
+def fv5b_head_gemv_i8(w, s, q, s_x, y=None, acc=None, stream=None):
+    """int8 activations: logits = s_x[m] sum_b S[v,b] acc[m,v,b]; acc (optional) int32 [M,V,K/256]."""
+    import torch
+    v, k, m = _fv5b_args(w, s, q, (torch.int8,))
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=q.device)
+    _check("fv5b_head_gemv_i8", lib().fv5b_head_gemv_i8(_ptr(w), _ptr(s), v, k, _ptr(q), _ptr(s_x), m, _ptr(y),
+                                                        _ptr(acc), _stream(stream)))
+    return y
+
+
+def fv5b_head_argmax(w, s, x, workspace=None, logits=None, stream=None):
+    """Greedy argmax over the block-scaled head's logits of bf16 x: (idx int32 [M], val fp32 [M])."""
+    import torch
+    v, k, m = _fv5b_args(w, s, x, (torch.bfloat16, torch.int16, torch.uint16))
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, x.device)
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    val = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("fv5b_head_argmax", lib().fv5b_head_argmax(_ptr(w), _ptr(s), v, k, _ptr(x), m, _ptr(idx), _ptr(val),
+                                                      _ptr(logits), _ptr(workspace), _stream(stream)))
+    return idx, val
+
+
+def fv5b_head_argmax_i8(w, s, q, s_x, workspace=None, logits=None, stream=None):
+    """Greedy argmax over the block-scaled head's logits of int8 q: (idx, val)."""
+    import torch
+    v, k, m = _fv5b_args(w, s, q, (torch.int8,))
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, q.device)
+    idx = torch.empty(m, dtype=torch.int32, device=q.device)
+    val = torch.empty(m, dtype=torch.float32, device=q.device)
+    _check("fv5b_head_argmax_i8", lib().fv5b_head_argmax_i8(_ptr(w), _ptr(s), v, k, _ptr(q), _ptr(s_x), m,
+                                                            _ptr(idx), _ptr(val), _ptr(logits), _ptr(workspace),
+                                                            _stream(stream)))
+    return idx, val
+
+
+def fv5b_embed(w, s, ids, f32=True, bf16=True, stream=None):
+    """Embedding rows of int32 token ids [M]: (fp32 [M,K] or None, bf16 [M,K] or None); ids outside [0,V) give zeros."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(s, "S", (torch.float32,), 2)
+    _need(ids, "ids", (torch.int32,), 1)
+    v, k = w.shape
+    m = ids.shape[0]
+    out = torch.empty((m, k), dtype=torch.float32, device=ids.device) if f32 else None
+    ob = torch.empty((m, k), dtype=torch.bfloat16, device=ids.device) if bf16 else None
+    _check("fv5b_embed", lib().fv5b_embed(_ptr(w), _ptr(s), v, k, _ptr(ids), m, _ptr(out), _ptr(ob),
+                                          _stream(stream)))
+    return out, ob

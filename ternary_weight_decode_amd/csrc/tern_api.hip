@@ -372,3 +372,83 @@ int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int6
 }
 
 }  // extern "C"
+
+// ---- block-scaled (FV5B-style) head and embedding rows
+
+namespace {
+
+int fv5b_head_check(const int8_t* W, const float* S, int64_t V, int64_t K, const void* act, const float* s_x,
+                    bool int8_act, int64_t M, const void* out, bool out_4)
+{
+    if (V < 1 || V > 0xFFFFFFF0ll || K < 256 || K % 256 != 0 || M < 1 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (!tern::head_argmax_fits(K, M, int8_act)) return TERN_E_SHAPE;
+    if (!W || !S || !act || !out || (int8_act && !s_x)) return TERN_E_NULL;
+    if (!aligned16(W) || !aligned16(act) || !aligned4(S) || (s_x && !aligned4(s_x)) || (out_4 && !aligned4(out)))
+        return TERN_E_ALIGN;
+    return TERN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fv5b_head_gemv(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                   float* logits, void* stream)
+{
+    int rc = fv5b_head_check(W, S, V, K, x, nullptr, false, M, logits, true);
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_bf16(W, S, V, K, x, M, logits, (hipStream_t)stream));
+}
+
+int fv5b_head_gemv_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
+                      int64_t M, float* logits, int32_t* acc_dbg, void* stream)
+{
+    int rc = fv5b_head_check(W, S, V, K, q, s_x, true, M, logits, true);
+    if (rc) return rc;
+    if (acc_dbg && !aligned4(acc_dbg)) return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_i8(W, S, V, K, q, s_x, M, logits, acc_dbg, (hipStream_t)stream));
+}
+
+int fv5b_head_argmax(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                     int32_t* idx, float* val, float* logits, void* workspace, void* stream)
+{
+    int rc = fv5b_head_check(W, S, V, K, x, nullptr, false, M, workspace, false);
+    if (rc) return rc;
+    if (!idx || !val) return TERN_E_NULL;
+    if (!aligned4(idx) || !aligned4(val) || (logits && !aligned4(logits)) || ((uintptr_t)workspace & 7))
+        return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_argmax_bf16(W, S, V, K, x, M, logits, idx, val, workspace,
+                                                     (hipStream_t)stream));
+}
+
+int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
+                        int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream)
+{
+    int rc = fv5b_head_check(W, S, V, K, q, s_x, true, M, workspace, false);
+    if (rc) return rc;
+    if (!idx || !val) return TERN_E_NULL;
+    if (!aligned4(idx) || !aligned4(val) || (logits && !aligned4(logits)) || ((uintptr_t)workspace & 7))
+        return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_argmax_i8(W, S, V, K, q, s_x, M, logits, idx, val, workspace,
+                                                   (hipStream_t)stream));
+}
+
+int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M, float* out,
+               uint16_t* out_bf16, void* stream)
+{
+    if (V < 0 || K < 0 || K % 256 != 0 || M < 0) return TERN_E_SHAPE;
+    if (M == 0 || K == 0) return TERN_OK;
+    if (!ids || (!out && !out_bf16) || (V > 0 && (!W || !S))) return TERN_E_NULL;
+    if ((W && !aligned16(W)) || (S && !aligned4(S)) || !aligned4(ids) || (out && !aligned16(out)) ||
+        (out_bf16 && !aligned16(out_bf16)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_fv5b_embed(W, S, V, K, ids, M, out, out_bf16, (hipStream_t)stream));
+}
+
+}  // extern "C"

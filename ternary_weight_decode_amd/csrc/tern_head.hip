@@ -233,12 +233,21 @@ __global__ __launch_bounds__(1024) void head_argmax_finish_kernel(const unsigned
 // with the same two loads whether or not a unit is left (past the end they
 // read 16 bytes at the start of W, unused), so the compiler can count the
 // loads in flight exactly instead of waiting for all of them.
-template <bool kInt8, int TPW>
+//
+// kBlk: block-scaled weights (FV5B-style: one f32 scale per 256-weight block
+// of a row, rs = S [V][K/256]).  Each block's MFMA sum (exact int32 with int8
+// activations, fp32 with bf16) is folded into the row total with its scale
+// (one FMA per element and block, in block order); the int8 block sums go
+// to acc_dbg [M][V][K/256] on request; logits = total (bf16) or
+// s_x[m] * total (int8).  Every slot also loads its block's scale (4 bytes
+// per lane, shared by the 4 lanes of a row and the block's two units).
+template <bool kInt8, int TPW, bool kBlk = false>
 __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict__ W, const float* __restrict__ rs,
                                                         int64_t V, int64_t K, const void* __restrict__ act,
                                                         const float* __restrict__ s_x, int M, float* __restrict__ y,
                                                         int32_t* __restrict__ acc_dbg, HeadArgmax am)
 {
+    static_assert(!kBlk || TPW % 2 == 0, "a block's two units share a ring parity");
     extern __shared__ __align__(16) uint8_t smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -253,12 +262,15 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
     v = v < V ? v : V - 1;                                 // rows past V re-read the last row (outputs dropped)
     const int8_t* row = W + (has ? v : 0) * K + 16 * g;
 
+    const int nblk = (int)(K >> 8);                        // 256-weight blocks per row (kBlk)
     u32x4 lo[TPW], hi[TPW];
+    float bs[TPW];
     auto load = [&](int s, int j) {
         const bool valid = has && j < nunit;
         const int8_t* p = valid ? row + (int64_t)j * kBlockK : W;
         lo[s] = head_ld16(p);
         hi[s] = head_ld16(valid ? p + 64 : W);
+        if constexpr (kBlk) bs[s] = rs[valid ? v * nblk + (j >> 1) : 0];
     };
 #pragma unroll
     for (int s = 0; s < TPW; ++s) load(s, s);
@@ -276,6 +288,8 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
 
     f32x4 accf = {0.f, 0.f, 0.f, 0.f};
     i32x4 acci = {0, 0, 0, 0};
+    f32x4 tot = {0.f, 0.f, 0.f, 0.f};                      // kBlk: scaled block sums so far
+    const int64_t vo = q * kTileRows + r;
     const uint8_t* arow = smem + mrow * astride + 16 * g * ebytes;
     for (int u0 = 0; u0 < nunit; u0 += TPW) {
 #pragma unroll
@@ -292,24 +306,45 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
 #pragma unroll
                     for (int t = 0; t < 4; ++t) accf = mfma_bf16(*(const u32x4*)(a + kHalfOff[t]), B[t], accf);
                 }
+                if constexpr (kBlk) {
+                    if (s & 1) {                           // the second unit of block j / 2
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            if constexpr (kInt8) {
+                                tot[i] = __builtin_fmaf(bs[s], (float)acci[i], tot[i]);
+                                const int m = 4 * g + i;
+                                if (acc_dbg && vo < V && m < M)
+                                    acc_dbg[((int64_t)m * V + vo) * nblk + (j >> 1)] = acci[i];
+                            } else {
+                                tot[i] = __builtin_fmaf(bs[s], accf[i], tot[i]);
+                            }
+                        }
+                        accf = f32x4{0.f, 0.f, 0.f, 0.f};
+                        acci = i32x4{0, 0, 0, 0};
+                    }
+                }
             }
             load(s, j + TPW);
         }
     }
-    const int64_t vo = q * kTileRows + r;
     float lv[4];
     bool ok[4];
     {
-        const float sv = rs[vo < V ? vo : V - 1];
+        const float sv = kBlk ? 1.0f : rs[vo < V ? vo : V - 1];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int m = 4 * g + i;
             ok[i] = vo < V && m < M;
-            if constexpr (kInt8) lv[i] = sv * s_x[m < M ? m : M - 1] * (float)acci[i];
-            else lv[i] = sv * accf[i];
+            if constexpr (kBlk) {
+                if constexpr (kInt8) lv[i] = s_x[m < M ? m : M - 1] * tot[i];
+                else lv[i] = tot[i];
+            } else {
+                if constexpr (kInt8) lv[i] = sv * s_x[m < M ? m : M - 1] * (float)acci[i];
+                else lv[i] = sv * accf[i];
+            }
             if (ok[i]) {
                 if (y) y[(int64_t)m * V + vo] = lv[i];
-                if constexpr (kInt8) {
+                if constexpr (kInt8 && !kBlk) {
                     if (acc_dbg) acc_dbg[(int64_t)m * V + vo] = acci[i];
                 }
             }
@@ -325,15 +360,15 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
     return (int)(K < cap ? K : cap);
 }
 
-template <bool kInt8, int TPW>
+template <bool kInt8, int TPW, bool kBlk = false>
 static hipError_t launch_head_fast(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                    const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream,
                                    HeadArgmax am = HeadArgmax{nullptr})
 {
     const size_t lds = (size_t)M * (K * (kInt8 ? 1 : 2) + 16);
     const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
-    head_fast_kernel<kInt8, TPW><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(W, rs, V, K, act, s_x,
-                                                                                               (int)M, y, acc, am);
+    head_fast_kernel<kInt8, TPW, kBlk><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(
+        W, rs, V, K, act, s_x, (int)M, y, acc, am);
     return hipGetLastError();
 }
 
@@ -373,13 +408,13 @@ bool head_argmax_fits(int64_t K, int64_t M, bool int8_act)
     return (size_t)M * (K * (int8_act ? 1 : 2) + 16) <= (size_t)160 * 1024;
 }
 
-template <bool kInt8>
+template <bool kInt8, bool kBlk = false>
 static hipError_t launch_head_argmax(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                      const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                      hipStream_t stream)
 {
     const HeadArgmax am{(unsigned long long*)ws};
-    hipError_t e = launch_head_fast<kInt8, kHeadTpw>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
+    hipError_t e = launch_head_fast<kInt8, kHeadTpw, kBlk>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
     if (e != hipSuccess) return e;
     head_argmax_finish_kernel<<<dim3((unsigned)M), dim3(1024), 0, stream>>>((const unsigned long long*)ws,
                                                                            (V + 15) / 16, (int)M, idx, val);
@@ -397,6 +432,88 @@ hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, in
                                  hipStream_t stream)
 {
     return launch_head_argmax<true>(W, rs, V, K, q, s_x, M, y, idx, val, ws, stream);
+}
+
+// ---- block-scaled (FV5B-style) head: x must fit in LDS (head_argmax_fits)
+
+hipError_t launch_fv5b_head_bf16(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                 int64_t M, float* y, hipStream_t stream)
+{
+    return launch_head_fast<false, kHeadTpw, true>(W, S, V, K, x, nullptr, M, y, nullptr, stream);
+}
+
+hipError_t launch_fv5b_head_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q,
+                               const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    return launch_head_fast<true, kHeadTpw, true>(W, S, V, K, q, s_x, M, y, acc, stream);
+}
+
+hipError_t launch_fv5b_head_argmax_bf16(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                        int64_t M, float* y, int32_t* idx, float* val, void* ws, hipStream_t stream)
+{
+    return launch_head_argmax<false, true>(W, S, V, K, x, nullptr, M, y, idx, val, ws, stream);
+}
+
+hipError_t launch_fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q,
+                                      const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                      hipStream_t stream)
+{
+    return launch_head_argmax<true, true>(W, S, V, K, q, s_x, M, y, idx, val, ws, stream);
+}
+
+// Embedding rows: one thread per 16 weights of an output row; out[m][k] =
+// W[id][k] * S[id][k/256] (one fp32 rounding), out_bf16 its nearest-even
+// bf16; an id outside [0, V) writes a zero row without reading W.
+__global__ void fv5b_embed_kernel(const int8_t* __restrict__ W, const float* __restrict__ S, int64_t V, int64_t K,
+                                  const int32_t* __restrict__ ids, int64_t M, float* __restrict__ out,
+                                  uint16_t* __restrict__ out_bf16)
+{
+    const int64_t per_row = K / 16, total = M * per_row;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t m = t / per_row, c = t - m * per_row;
+        const int64_t id = ids[m];
+        float f[16];
+        if (id >= 0 && id < V) {
+            const u32x4 w = *(const u32x4*)(W + id * K + 16 * c);
+            const float sc = S[id * (K / 256) + (16 * c) / 256];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) f[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * sc;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) f[i] = 0.f;
+        }
+        if (out) {
+            f32x4* o = (f32x4*)(out + m * K + 16 * c);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
+        }
+        if (out_bf16) {
+            uint32_t h[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // nearest-even bf16 of a finite fp32 value: add 0x7FFF plus the
+                // lowest kept bit, keep the high half
+                uint32_t b0 = __builtin_bit_cast(uint32_t, f[2 * i]);
+                uint32_t b1 = __builtin_bit_cast(uint32_t, f[2 * i + 1]);
+                b0 = (b0 + 0x7FFFu + ((b0 >> 16) & 1u)) >> 16;
+                b1 = (b1 + 0x7FFFu + ((b1 >> 16) & 1u)) >> 16;
+                h[i] = b0 | (b1 << 16);
+            }
+            u32x4* o = (u32x4*)(out_bf16 + m * K + 16 * c);
+            o[0] = u32x4{h[0], h[1], h[2], h[3]};
+            o[1] = u32x4{h[4], h[5], h[6], h[7]};
+        }
+    }
+}
+
+hipError_t launch_fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M,
+                             float* out, uint16_t* out_bf16, hipStream_t stream)
+{
+    const int64_t items = M * (K / 16);
+    int64_t grid = (items + 255) / 256;
+    grid = grid < 1 ? 1 : (grid > 65536 ? 65536 : grid);
+    fv5b_embed_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(W, S, V, K, ids, M, out, out_bf16);
+    return hipGetLastError();
 }
 
 }  // namespace tern

@@ -149,6 +149,14 @@ def linear5_inputs(lin: Linear, m: int = 1):
     return lv, lo, hi, x
 
 
+def gen_head_blocks(rng_w: np.random.Generator, rng_s: np.random.Generator, v: int, k: int):
+    """Block-scaled (FV5B-style) int8 rows: round(N(0,30)) clipped to [-127, 127] and one fp32
+    scale U[0.002, 0.02] per 256 weights of a row."""
+    w = np.clip(np.rint(rng_w.normal(0.0, 30.0, size=(v, k))), -127, 127).astype(np.int8)
+    s = rng_s.uniform(0.002, 0.02, size=(v, k // 256)).astype(np.float32)
+    return w, s
+
+
 def config0_inputs():
     """Single 3072x1024 ternary linear (0.6B gate shape), M=1, one generator seeded 0,
     drawn in the order ternary states -> scales -> activations."""

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 4
+    assert L.tern_abi_version() == 5
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -146,6 +146,33 @@ def test_five_level_sizes_and_argument_errors():
     assert pk(p, None, p, 16, 512, p, None) == E_NULL
     assert pk(m, p, p, 16, 512, p, None) == E_ALIGN
     assert pk(p, p, ctypes.c_void_p(0x10002), 16, 512, p, None) == E_ALIGN
+
+
+def test_fv5b_argument_errors():
+    L = tw.lib()
+    p, m = ALIGNED, MISALIGNED
+    h, hi, a, e = L.fv5b_head_gemv, L.fv5b_head_gemv_i8, L.fv5b_head_argmax, L.fv5b_embed
+    assert h(p, p, 100, 384, p, 1, p, None) == E_SHAPE                 # K % 256
+    assert h(p, p, 100, 0, p, 1, p, None) == E_SHAPE                   # K = 0
+    assert h(p, p, 0, 256, p, 1, p, None) == E_SHAPE                   # V = 0
+    assert h(p, p, 100, 256, p, 17, p, None) == E_SHAPE                # M > 16
+    assert h(p, p, 100, 8192, p, 16, p, None) == E_SHAPE               # x does not fit in LDS
+    assert hi(p, p, 100, 8192, p, p, 16, p, None, None) != E_SHAPE     # int8 q of that shape does
+    assert h(p, None, 100, 256, p, 1, p, None) == E_NULL
+    assert h(p, p, 100, 256, p, 1, None, None) == E_NULL
+    assert hi(p, p, 100, 256, p, None, 1, p, None, None) == E_NULL     # s_x
+    assert h(m, p, 100, 256, p, 1, p, None) == E_ALIGN
+    assert h(p, ctypes.c_void_p(0x10002), 100, 256, p, 1, p, None) == E_ALIGN
+    assert hi(p, p, 100, 256, p, p, 1, p, ctypes.c_void_p(0x10002), None) == E_ALIGN
+    assert a(p, p, 100, 256, p, 1, None, p, None, p, None) == E_NULL  # idx
+    assert a(p, p, 100, 256, p, 1, p, p, None, None, None) == E_NULL  # workspace
+    assert a(p, p, 100, 256, p, 1, p, p, None, m, None) == E_ALIGN     # workspace 8-byte
+    assert e(p, p, 10, 384, p, 4, p, p, None) == E_SHAPE               # K % 256
+    assert e(p, p, 10, 256, p, -1, p, p, None) == E_SHAPE
+    assert e(None, None, 10, 256, None, 0, None, None, None) == E_OK   # M = 0
+    assert e(p, p, 10, 256, None, 4, p, p, None) == E_NULL             # ids
+    assert e(p, p, 10, 256, p, 4, None, None, None) == E_NULL          # no output
+    assert e(p, p, 10, 256, p, 4, m, None, None) == E_ALIGN            # out 16-byte
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):
