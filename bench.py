@@ -226,7 +226,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
                      "timing": "HIP events around back-to-back launches of the step's ternary chain"})
     else:
         base.update({"traffic": measured_traffic(root, args.compose),
-                     "kernel": "gemv_bf16_oneshot_kernel<1,*,*> (tern_gemv, M=1)",
+                     "kernel": "gemv_oneshot_kernel<false,1,*,*> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
                      "launches_per_step": n_tern,
@@ -357,7 +357,9 @@ def mode_prefill(args, tw, synth, torch):
 
 def mode_head(args, tw, synth, torch):
     """The int8 head (151936 x 4096 at --config 2, x 1024 at --config 1) alone and fused with
-    the greedy argmax, bf16 and int8 activations, M = 1: us per call and GB/s of weights+scales."""
+    the greedy argmax, bf16 and int8 activations, M = 1, with a per-row scale and with a scale per
+    256-weight block (FV5B-style); then the embedding-row gather of 1 and 512 tokens: us per call
+    and GB/s of the bytes each call must move."""
     w, rs, xh = synth.head_inputs(args.config)
     v, k = w.shape
     W, RS = torch.from_numpy(w).cuda(), torch.from_numpy(rs).cuda()
@@ -366,19 +368,36 @@ def mode_head(args, tw, synth, torch):
     q, sx = tw.tern_quantize_i8(x)
     y = torch.empty((1, v), dtype=torch.float32, device="cuda")
     ws = tw.i8_head_argmax_workspace(v, 1)
+    # block-scaled (FV5B-style) scales of the same rows: one fp32 per 256 weights
+    S = torch.from_numpy(np.random.default_rng(11).uniform(0.002, 0.02, (v, k // 256)).astype(np.float32)).cuda()
+    row_bytes, blk_bytes = v * k + 4 * v, v * k + 4 * v * (k // 256)
     runs = {
-        "head_bf16": lambda c: tw.i8_head_gemv(c, RS, x, y=y),
-        "head_int8": lambda c: tw.i8_head_gemv_i8(c, RS, q, sx, y=y),
-        "head_argmax_bf16": lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws),
-        "head_argmax_bf16_with_logits": lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws, logits=y),
-        "head_argmax_int8": lambda c: tw.i8_head_argmax_i8(c, RS, q, sx, workspace=ws),
+        "head_bf16": (lambda c: tw.i8_head_gemv(c, RS, x, y=y), row_bytes),
+        "head_int8": (lambda c: tw.i8_head_gemv_i8(c, RS, q, sx, y=y), row_bytes),
+        "head_argmax_bf16": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws), row_bytes),
+        "head_argmax_bf16_with_logits": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws, logits=y), row_bytes),
+        "head_argmax_int8": (lambda c: tw.i8_head_argmax_i8(c, RS, q, sx, workspace=ws), row_bytes),
+        "fv5b_head_bf16": (lambda c: tw.fv5b_head_gemv(c, S, x, y=y), blk_bytes),
+        "fv5b_head_int8": (lambda c: tw.fv5b_head_gemv_i8(c, S, q, sx, y=y), blk_bytes),
+        "fv5b_head_argmax_bf16": (lambda c: tw.fv5b_head_argmax(c, S, x, workspace=ws), blk_bytes),
+        "fv5b_head_argmax_int8": (lambda c: tw.fv5b_head_argmax_i8(c, S, q, sx, workspace=ws), blk_bytes),
     }
     out = []
-    for name, fn in runs.items():
+    for name, (fn, nbytes) in runs.items():
         g = capture(torch, lambda: [fn(c) for c in copies])
         ms = time_replays(torch, g, 5) / len(copies)
-        nbytes = v * k + 4 * v
         out.append({"call": name, "V": v, "K": k, "us": round(ms * 1e3, 2),
+                    "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+        del g
+    # embedding rows (the step before the first linear): 1 token, and a 512-token prefill batch
+    for m in (1, 512):
+        ids = torch.from_numpy(np.random.default_rng(m).integers(0, v, m).astype(np.int32)).cuda()
+        outs = (torch.empty((m, k), dtype=torch.float32, device="cuda"),
+                torch.empty((m, k), dtype=torch.bfloat16, device="cuda"))
+        g = capture(torch, lambda: [tw.fv5b_embed(c, S, ids, out=outs[0], out_bf16=outs[1]) for c in copies])
+        ms = time_replays(torch, g, 5) / len(copies)
+        nbytes = m * (k + 4 * (k // 256) + 4 + 6 * k)
+        out.append({"call": f"fv5b_embed_m{m}", "V": v, "K": k, "us": round(ms * 1e3, 2),
                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
         del g
     print(json.dumps({"mode": "head", "rows": out}), flush=True)

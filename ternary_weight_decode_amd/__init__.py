@@ -410,16 +410,19 @@ def fv5b_head_argmax_i8(w, s, q, s_x, workspace=None, logits=None, stream=None):
     return idx, val
 
 
-def fv5b_embed(w, s, ids, f32=True, bf16=True, stream=None):
-    """Embedding rows of int32 token ids [M]: (fp32 [M,K] or None, bf16 [M,K] or None); ids outside [0,V) give zeros."""
+def fv5b_embed(w, s, ids, f32=True, bf16=True, out=None, out_bf16=None, stream=None):
+    """Embedding rows of int32 token ids [M]: (fp32 [M,K] or None, bf16 [M,K] or None); ids outside [0,V)
+    give zeros.  Preallocated outputs may be passed as out / out_bf16."""
     import torch
     _need(w, "W", (torch.int8,), 2)
     _need(s, "S", (torch.float32,), 2)
     _need(ids, "ids", (torch.int32,), 1)
     v, k = w.shape
     m = ids.shape[0]
-    out = torch.empty((m, k), dtype=torch.float32, device=ids.device) if f32 else None
-    ob = torch.empty((m, k), dtype=torch.bfloat16, device=ids.device) if bf16 else None
-    _check("fv5b_embed", lib().fv5b_embed(_ptr(w), _ptr(s), v, k, _ptr(ids), m, _ptr(out), _ptr(ob),
+    if out is None and f32:
+        out = torch.empty((m, k), dtype=torch.float32, device=ids.device)
+    if out_bf16 is None and bf16:
+        out_bf16 = torch.empty((m, k), dtype=torch.bfloat16, device=ids.device)
+    _check("fv5b_embed", lib().fv5b_embed(_ptr(w), _ptr(s), v, k, _ptr(ids), m, _ptr(out), _ptr(out_bf16),
                                           _stream(stream)))
-    return out, ob
+    return out, out_bf16
