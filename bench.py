@@ -176,7 +176,7 @@ def time_replays(torch, g, reps: int) -> float:
 TRAFFIC_PROFILE = "profiles/tern_gemv_m1_8b_token_fused_hbm_traffic.txt"
 
 
-GEMV_SOURCES = ("tern_gemv.hip", "tern_tile.h", "tern_device.h")   # the M = 1 GEMV kernel's sources
+GEMV_SOURCES = ("tern_gemv.hip", "tern_oneshot.h", "tern_tile.h", "tern_device.h")   # the M = 1 GEMV's sources
 
 
 def measured_traffic(root: str, compose: str):
@@ -194,7 +194,7 @@ def measured_traffic(root: str, compose: str):
     except OSError:
         return None
     m = re.search(r"ternary GEMV per launch .*?: HBM ([0-9.]+) MB", text)
-    h = re.search(r"sha256 \(tern_gemv.hip, tern_tile.h, tern_device.h\) at measurement: ([0-9a-f]{64})", text)
+    h = re.search(r"sha256 \(" + ", ".join(GEMV_SOURCES) + r"\) at measurement: ([0-9a-f]{64})", text)
     if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
         return None
     return int(float(m.group(1)) * 1e6)
