@@ -149,6 +149,39 @@ def gemv_bf16(packed, n: int, k: int, x_bf16, rows=None):
     return gemv_bf16_levels(levels, s_lo, s_hi, x_bf16)
 
 
+def acc_i8_levels(levels, q):
+    """Exact block sums for int8 activations q [M][K]: acc[m][n][b][0] =
+    sum over block b of sign(l)*q where |l| = 1, acc[m][n][b][1] the same
+    where |l| = 2 (int64)."""
+    levels = np.asarray(levels, dtype=np.int64)
+    n, k = levels.shape
+    nb = k // 256
+    qb = np.asarray(q, dtype=np.int8).astype(np.int64).reshape(-1, nb, 256)
+    sign = np.sign(levels).reshape(n, nb, 256)
+    mag = np.abs(levels).reshape(n, nb, 256)
+    lo = np.einsum("mbk,nbk->mnb", qb, sign * (mag == 1))
+    hi = np.einsum("mbk,nbk->mnb", qb, sign * (mag == 2))
+    return np.stack([lo, hi], axis=3)
+
+
+def gemv_i8_levels(levels, s_lo, s_hi, q, s_x):
+    """int8 activations q with row scales s_x: y[m][n] = s_x[m] * sum_b
+    (s_lo[n][b] * acc_lo + s_hi[n][b] * acc_hi) in fp64.  Returns
+    (acc int64 [M][N][K/256][2], y64, y32)."""
+    acc = acc_i8_levels(levels, q)
+    lo = np.asarray(s_lo, np.float32).astype(np.float64)
+    hi = np.asarray(s_hi, np.float32).astype(np.float64)
+    tot = np.einsum("mnb,nb->mn", acc[..., 0], lo) + np.einsum("mnb,nb->mn", acc[..., 1], hi)
+    y64 = np.asarray(s_x, np.float32).astype(np.float64)[:, None] * tot
+    return acc, y64, y64.astype(np.float32)
+
+
+def gemv_i8(packed, n: int, k: int, q, s_x, rows=None):
+    """The int8-activation product read from a packed blob (rows optional)."""
+    levels, s_lo, s_hi = unpack(packed, n, k) if rows is None else _unpack_rows(packed, n, k, rows)
+    return gemv_i8_levels(levels, s_lo, s_hi, q, s_x)
+
+
 def _unpack_rows(packed, n, k, rows):
     """unpack restricted to the given rows (same bit-level reading)."""
     levels, s_lo, s_hi = [], [], []

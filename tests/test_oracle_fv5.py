@@ -22,7 +22,7 @@ def _read_golden():
         tok = line.split()
         if tok[0] == "example":
             cur = {"name": tok[1], "N": int(tok[3]), "K": int(tok[5]), "total": int(tok[7]),
-                   "l": [], "s": [], "bytes": {}, "y": {}}
+                   "l": [], "s": [], "bytes": {}, "y": {}, "acc": {}, "yq": {}}
         elif tok[0] == "l":
             cur["l"].append((int(tok[1]), int(tok[2]), int(tok[3])))
         elif tok[0] == "s":
@@ -31,6 +31,10 @@ def _read_golden():
             cur["bytes"][int(tok[1])] = int(tok[2], 16)
         elif tok[0] == "y":
             cur["y"][int(tok[1])] = float(tok[2])
+        elif tok[0] == "acc":
+            cur["acc"][(int(tok[1]), int(tok[2]))] = (int(tok[3]), int(tok[4]))
+        elif tok[0] == "yq":
+            cur["yq"][int(tok[1])] = float(tok[2])
         elif tok[0] == "end":
             ex[cur["name"]] = cur
     return ex
@@ -47,6 +51,58 @@ def golden_inputs(e):
         lo[r, b], hi[r, b] = a, c
     x = synth.f32_to_bf16_bits((np.arange(k) % 7 - 3).astype(np.float32)[None, :])
     return lv, lo, hi, x
+
+
+def golden_q(k):
+    return ((np.arange(k) % 5) - 2).astype(np.int8)[None, :], np.array([0.5], np.float32)
+
+
+@pytest.mark.parametrize("name", ["ex1", "ex2"])
+def test_golden_gemv_i8(name):
+    e = _read_golden()[name]
+    lv, lo, hi, _ = golden_inputs(e)
+    q, sx = golden_q(e["K"])
+    acc, y64, _ = fv5.gemv_i8(fv5.pack(lv, lo, hi), e["N"], e["K"], q, sx)
+    want = np.zeros_like(acc)
+    for (r, b), (a_lo, a_hi) in e["acc"].items():
+        want[0, r, b] = (a_lo, a_hi)
+    assert np.array_equal(acc, want)
+    wy = np.zeros(e["N"])
+    for r, v in e["yq"].items():
+        wy[r] = v
+    assert np.array_equal(y64[0], wy)
+
+
+def test_gemv_i8_vs_brute_force_and_ternary():
+    rng = np.random.default_rng(5)
+    n, k, m = 4, 512, 2
+    lv, lo, hi = gen5(rng, n, k)
+    q = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    sx = rng.uniform(0.01, 0.1, m).astype(np.float32)
+    acc, y64, _ = fv5.gemv_i8(fv5.pack(lv, lo, hi), n, k, q, sx)
+    for mm in range(m):
+        for nn in range(n):
+            tot = 0.0
+            for b in range(k // 256):
+                a = [0, 0]
+                for kk in range(256 * b, 256 * b + 256):
+                    lvl = int(lv[nn, kk])
+                    if lvl:
+                        a[abs(lvl) - 1] += (1 if lvl > 0 else -1) * int(q[mm, kk])
+                assert acc[mm, nn, b].tolist() == a
+                tot += float(lo[nn, b]) * a[0] + float(hi[nn, b]) * a[1]
+            assert abs(y64[mm, nn] - float(sx[mm]) * tot) <= 1e-12 * (1 + abs(tot))
+    # levels in {-1, 0, +1}: the ternary int8 oracle (plain C) with scale s_lo
+    t = synth.gen_ternary(rng, 40, 1024)
+    s16 = synth.gen_scales(rng, 40, 4)
+    lo2 = s16.view(np.float16).astype(np.float32)
+    q2 = rng.integers(-127, 128, size=(3, 1024)).astype(np.int8)
+    sx2 = rng.uniform(0.01, 0.1, 3).astype(np.float32)
+    acc5, y5, _ = fv5.gemv_i8_levels(t, lo2, lo2 * 3, q2, sx2)
+    acc3, y3, _ = oracle.tern_i8(oracle.pack(t, np.repeat(s16, 2, axis=1)), 40, 1024, q2, sx2)
+    assert np.array_equal(acc5[..., 0], acc3.astype(np.int64).reshape(3, 40, 4, 2).sum(axis=3))
+    assert not acc5[..., 1].any()
+    assert oracle.rel_l2(y5, y3) < 1e-13
 
 
 def gen5(rng, n, k, p=(0.1, 0.1, 0.6, 0.1, 0.1)):
