@@ -408,10 +408,12 @@ FV5_UNITS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up"))
 
 def mode_fv5(args, tw, synth, torch):
     """Five-level (FV5-style, 3.25 bits per weight) GEMV on the fused 8B linears of one layer
-    at M in {1, 4, 8, 16}, with the ternary GEMV of the same shapes beside it; weights rotate
+    at M in {1, 4, 8, 16}, bf16 and int8 activations, with the ternary GEMV of the same shapes
+    beside it; weights rotate
     over >= 1 GB of copies so each launch reads HBM.  Also the bytes-weighted M = 1 layer
     aggregate (one layer = the four fused launches)."""
-    out, layer = [], {"fv5": [0.0, 0], "ternary": [0.0, 0]}
+    out = []
+    layer = {f"{f}_{a}": [0.0, 0] for f in ("fv5", "ternary") for a in ("bf16", "int8")}
     for label, projs in FV5_UNITS:
         lins = [synth.Linear(2, 0, p, *synth.SHAPES_8B[p], synth.P_ZERO, synth.P_PLUS) for p in projs]
         parts = [synth.linear5_inputs(lin) for lin in lins]
@@ -425,22 +427,30 @@ def mode_fv5(args, tw, synth, torch):
         p3 = tw.tern_pack(torch.from_numpy(t).cuda(), torch.from_numpy(s16).cuda())
         del lv, lo, hi, parts, t
         x16 = torch.from_numpy(synth.gen_x_bf16(np.random.default_rng(5), 16, k).view(np.int16)).cuda()
-        for fmt, packed, nbytes_w, call in (("fv5", p5, tw.tern5_packed_bytes(n, k), tw.tern5_gemv),
-                                           ("ternary", p3, tw.tern_packed_bytes(n, k), tw.tern_gemv)):
+        q16, sx16 = tw.tern_quantize_i8(x16)
+        for fmt, packed, nbytes_w, call, call_i8 in (
+                ("fv5", p5, tw.tern5_packed_bytes(n, k), tw.tern5_gemv, tw.tern5_gemv_i8),
+                ("ternary", p3, tw.tern_packed_bytes(n, k), tw.tern_gemv, tw.tern_gemv_i8)):
             copies = rotate_copies(torch, packed)
             for m in (1, 4, 8, 16):
                 x = x16[:m].contiguous()
+                q, sx = q16[:m].contiguous(), sx16[:m].contiguous()
                 y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-                g = capture(torch, lambda: [call(c, n, k, x, y=y) for c in copies])
-                ms = time_replays(torch, g, 5) / len(copies)
-                nbytes = nbytes_w + 2 * m * k + 4 * m * n
-                gbs = nbytes / (ms * 1e-3) / 1e9
-                out.append({"unit": label, "format": fmt, "n_k": [n, k], "M": m, "us": round(ms * 1e3, 2),
-                            "GB/s": round(gbs, 1), "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
-                if m == 1:
-                    layer[fmt][0] += ms * 1e3
-                    layer[fmt][1] += nbytes
-                del g
+                for act in ("bf16", "int8"):
+                    if act == "bf16":
+                        g = capture(torch, lambda: [call(c, n, k, x, y=y) for c in copies])
+                    else:
+                        g = capture(torch, lambda: [call_i8(c, n, k, q, sx, y=y) for c in copies])
+                    ms = time_replays(torch, g, 5) / len(copies)
+                    nbytes = nbytes_w + m * (2 * k if act == "bf16" else k + 4) + 4 * m * n
+                    gbs = nbytes / (ms * 1e-3) / 1e9
+                    out.append({"unit": label, "format": fmt, "act": act, "n_k": [n, k], "M": m,
+                                "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+                    if m == 1:
+                        layer[f"{fmt}_{act}"][0] += ms * 1e3
+                        layer[f"{fmt}_{act}"][1] += nbytes
+                    del g
             del copies
         del p5, p3
     agg = {fmt: {"us_per_layer": round(us, 2), "GB/s": round(b / (us * 1e-6) / 1e9, 1),

@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 5
+#define TERN_ABI_VERSION 6
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -281,6 +281,16 @@ int tern5_pack(const int8_t* levels, const float* s_lo, const float* s_hi, int64
  *   x       bf16 bits [M][K], 1 <= M <= TERN_MAX_M_GEMV, 16-byte aligned
  *   y       fp32 [M][N], 4-byte aligned */
 int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream);
+
+/* int8 activations (tern_quantize_i8 output) for the five-level W:
+ *   acc[m][n][b][0] = sum_{k in block b, |l| = 1} sign(l) * q[m][k],
+ *   acc[m][n][b][1] = the same over |l| = 2 (exact int32, 256-weight blocks),
+ *   y[m][n] = s_x[m] * sum_b (s_lo[n][b] * acc[..][0] + s_hi[n][b] * acc[..][1])
+ * with the block sums scaled in fp32.
+ *   q int8 [M][K] (16-byte aligned), s_x fp32 [M], 1 <= M <= TERN_MAX_M_GEMV;
+ *   y fp32 [M][N];  acc_dbg NULL or int32 [M][N][K/256][2] (debug). */
+int tern5_gemv_i8(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M, float* y,
+                  int32_t* acc_dbg, void* stream);
 
 /* ---- block-scaled int8 tensors (FV5B-style) ----
  *

@@ -13,7 +13,7 @@ Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 ``tern_gemm_prefill``, ``tern_packed_bytes``, and the dependent-GEMV chain
 ``tern_chain_workspace_bytes``, ``tern_chain_plan``, ``tern_gemv_chain``, the
 fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
-(FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv``, and the
+(FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv[_i8]``, and the
 block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
 ``fv5b_head_argmax[_i8]``, ``fv5b_embed``.
 """
@@ -27,11 +27,11 @@ MAX_M_GEMV = 16
 SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_bytes", "tern_pack", "tern_stats",
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
-           "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv",
+           "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
-               "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "fv5b_head_gemv", "fv5b_head_gemv_i8",
+               "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
                "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
 
 _lib = None
@@ -77,6 +77,7 @@ def lib():
         L.tern5_packed_bytes.argtypes = [_i64, _i64]
         L.tern5_pack.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
         L.tern5_gemv.argtypes = [_p, _i64, _i64, _p, _i64, _p, _p]
+        L.tern5_gemv_i8.argtypes = [_p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.fv5b_head_gemv.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
         L.fv5b_head_gemv_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.fv5b_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
@@ -346,6 +347,19 @@ def tern5_gemv(packed, n: int, k: int, x, y=None, stream=None):
     if y is None:
         y = torch.empty((m, n), dtype=torch.float32, device=x.device)
     _check("tern5_gemv", lib().tern5_gemv(_ptr(packed), n, k, _ptr(x), m, _ptr(y), _stream(stream)))
+    return y
+
+
+def tern5_gemv_i8(packed, n: int, k: int, q, s_x, y=None, acc=None, stream=None):
+    """int8 activations for the five-level W: y = s_x[m] sum_b (s_lo acc_lo + s_hi acc_hi);
+    acc (optional) int32 [M,N,K/256,2]."""
+    import torch
+    _need(q, "q", (torch.int8,), 2)
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, n), dtype=torch.float32, device=q.device)
+    _check("tern5_gemv_i8", lib().tern5_gemv_i8(_ptr(packed), n, k, _ptr(q), _ptr(s_x), m, _ptr(y), _ptr(acc),
+                                                _stream(stream)))
     return y
 
 

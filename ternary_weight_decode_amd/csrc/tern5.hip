@@ -1,5 +1,5 @@
 // tern5.hip — five-level (FV5-style) weights: load-time packing and the
-// bf16 GEMV / small-M GEMM on the gfx950 matrix cores.
+// GEMV / small-M GEMM (bf16 or int8 activations) on the gfx950 matrix cores.
 //
 // Format (block structure from the FV5 row of the block-format table on the
 // discuss.pytorch.kr Neutrino-1 page, section "FV5와 FV5B"): 256-weight
@@ -73,6 +73,65 @@ __device__ __forceinline__ void tile5_bf16(const Tile5& t, const uint16_t* xt, f
     }
 }
 
+// int8 activations: qa(j, h) gives the 16-byte A operand h of slot j (q of
+// this lane's row at k = 512*kt + 128*j + 32*g, in the decoded byte order).  Each magnitude's words decode
+// to bytes 64*sign with their own sign bits (the int8 decode needs the sign
+// bit clear where the magnitude bit is clear), the matrix core sums each
+// 256-block exactly in int32, and the block sums are scaled in fp32.  dbg,
+// when given, receives the exact sums [m][n][block][lo, hi] of this unit.
+template <int MT, typename QA>
+__device__ __forceinline__ void tile5_i8(const Tile5& t, QA qa, f32x4& acc, int32_t* dbg, int64_t N, int M,
+                                         int64_t n, int nb256, int b0, int g)
+{
+    i32x4 dl[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}}, dh[2] = {{0, 0, 0, 0}, {0, 0, 0, 0}};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int bh = j >> 1;
+        const uint32_t L = t.nz[j] & ~t.hi[j], H = t.nz[j] & t.hi[j];
+        u32x4 BL[2], BH[2];
+        decode_i8(L, t.sg[j] & L, BL);
+        decode_i8(H, t.sg[j] & H, BH);
+        const u32x4 a0 = qa(j, 0), a1 = qa(j, 1);
+        dl[bh] = mfma_i8(a0, BL[0], dl[bh]);
+        dh[bh] = mfma_i8(a0, BH[0], dh[bh]);
+        dl[bh] = mfma_i8(a1, BL[1], dl[bh]);
+        dh[bh] = mfma_i8(a1, BH[1], dh[bh]);
+    }
+#pragma unroll
+    for (int q = 0; q < (MT < 4 ? MT : 4); ++q) {
+        // decoded weights are 64*sign: |sums| < 2^22, exact in fp32
+        acc[q] = __builtin_fmaf(t.sc[0] * (1.0f / 64.0f), (float)dl[0][q], acc[q]);
+        acc[q] = __builtin_fmaf(t.sc[1] * (1.0f / 64.0f), (float)dh[0][q], acc[q]);
+        acc[q] = __builtin_fmaf(t.sc[2] * (1.0f / 64.0f), (float)dl[1][q], acc[q]);
+        acc[q] = __builtin_fmaf(t.sc[3] * (1.0f / 64.0f), (float)dh[1][q], acc[q]);
+    }
+    if (dbg != nullptr) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int m = 4 * g + q;
+            if (m < M && n < N) {
+#pragma unroll
+                for (int bh = 0; bh < 2; ++bh) {
+                    int32_t* d = dbg + (((int64_t)m * N + n) * nb256 + b0 + bh) * 2;
+                    d[0] = dl[bh][q] >> 6;
+                    d[1] = dh[bh][q] >> 6;
+                }
+            }
+        }
+    }
+}
+
+// 32 bytes of q (natural order, lo = bytes 0..15, hi = 16..31) -> the two
+// 16-byte A operands in the decoded byte order
+__device__ __forceinline__ void q_decoded_order(const u32x4& lo, const u32x4& hi, u32x4& o0, u32x4& o1)
+{
+    const uint32_t Q[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o0[d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+    for (int d = 4; d < 8; ++d) o1[d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+}
+
 // ------------------------------------------------------------------ pack
 
 // One thread per (row n < Np, block b, word w): reads the 32 levels of the
@@ -123,14 +182,19 @@ __global__ void pack5_kernel(const int8_t* __restrict__ lv, const float* __restr
 // One pass over the weights (the configuration of tern_oneshot.h): x is
 // staged in LDS once per workgroup, every wave's units are requested up front
 // (the first before x is staged, the rest right after), partials are summed
-// in LDS in k-tile order.  XC = 16-byte activation chunks per thread.
-template <int MT, int U, int XC>
+// in LDS in k-tile order.  kI8: int8 activations q with row scales s_x (staged
+// in the decoded byte order), y = s_x * sum.  XC = activation chunks per
+// thread (16 bytes of bf16, or 32 bytes of int8).
+template <bool kI8, int MT, int U, int XC>
 __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
-                                                             const uint16_t* __restrict__ x, int M,
-                                                             float* __restrict__ y)
+                                                             const void* __restrict__ x,
+                                                             const float* __restrict__ s_x, int M,
+                                                             float* __restrict__ y, int32_t* __restrict__ acc_dbg)
 {
     extern __shared__ __align__(16) uint8_t smem[];
     constexpr int NI = MT < 4 ? MT : 4;
+    constexpr int kChunkBytes = kI8 ? 32 : 16;
+    constexpr int kLoadsPerChunk = kChunkBytes / 16;
     const int nthreads = blockDim.x, nw = nthreads >> 6;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
@@ -142,22 +206,24 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint32_t* scales = (const TERN_GLOBAL uint32_t*)(packed + t5_plane_bytes(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
-    const int xrow_bytes = ((int)K + 8) * 2;
-    float* red = (float*)(smem + (size_t)M * xrow_bytes);  // [unit + 1 spare][NI][64]
+    const int xrow_bytes = kI8 ? (int)K + 16 : ((int)K + 8) * 2;   // staged bytes per activation row
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [unit + 1 spare][NI][64]
 
     // activations first; a chunk index past the end re-loads the last chunk
     // and stores it to a dummy slot (the start of the partials, written only
     // after the barrier), so every load is issued and used unconditionally
-    const int per_row = (int)(K * 2 / 16), chunks = M * per_row;
-    u32x4 xv[XC];
+    const int per_row = (int)(K * (kI8 ? 1 : 2) / kChunkBytes), chunks = M * per_row;
+    u32x4 xv[XC][kLoadsPerChunk];
     int xdst[XC];
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         const int u = threadIdx.x + c * nthreads;
         const int uc = u < chunks ? u : chunks - 1;
         const int m = uc / per_row, cc = uc - m * per_row;
-        xv[c] = xg[(int64_t)m * per_row + cc];
-        xdst[c] = u < chunks ? m * xrow_bytes + 16 * cc : M * xrow_bytes;
+#pragma unroll
+        for (int h = 0; h < kLoadsPerChunk; ++h)
+            xv[c][h] = xg[((int64_t)m * per_row + cc) * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : M * xrow_bytes;
     }
     __builtin_amdgcn_sched_barrier(0);
     Tile5 t[U];
@@ -172,7 +238,16 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     load_unit(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int c = 0; c < XC; ++c) *(u32x4*)(smem + xdst[c]) = xv[c];
+    for (int c = 0; c < XC; ++c) {
+        if constexpr (kI8) {
+            u32x4 o0, o1;
+            q_decoded_order(xv[c][0], xv[c][kLoadsPerChunk - 1], o0, o1);
+            *(u32x4*)(smem + xdst[c]) = o0;
+            *(u32x4*)(smem + xdst[c] + 16) = o1;
+        } else {
+            *(u32x4*)(smem + xdst[c]) = xv[c][0];
+        }
+    }
     __syncthreads();
 #pragma unroll
     for (int i = 1; i < U; ++i) {
@@ -181,14 +256,21 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     }
 
     const int mrow = r < M ? r : M - 1;
-    const uint16_t* xrow = (const uint16_t*)(smem + mrow * xrow_bytes) + 32 * g;
+    const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int j = wave + i * nw;
         const int jc = j < units ? j : units - 1;
-        const int kt = jc - (jc / nkt) * nkt;
+        const int lrt = jc / nkt, kt = jc - lrt * nkt;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        tile5_bf16<MT>(t[i], xrow + kt * kTileK, acc);
+        if constexpr (kI8) {
+            const int64_t n = (int64_t)(rt0 + lrt * G) * kTileRows + r;
+            const uint8_t* qt = xrow + kt * kTileK;
+            tile5_i8<MT>(t[i], [&](int jj, int h) { return *(const u32x4*)(qt + kBlockK * jj + 16 * h); }, acc,
+                         j < units ? acc_dbg : nullptr, N, M, n, (int)(K >> 8), 2 * kt, g);
+        } else {
+            tile5_bf16<MT>(t[i], (const uint16_t*)xrow + kt * kTileK, acc);
+        }
         const int slot = j < units ? j : units;
 #pragma unroll
         for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];
@@ -206,17 +288,19 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
             const float* pr = red + ((int64_t)lrt * nkt * NI + q) * 64 + l;
             float sum = 0.f;
             for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * NI * 64];
-            y[(int64_t)m * N + row] = sum;
+            y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
         }
     }
 }
 
 // Any shape: one workgroup per row tile, its waves split the k-tiles
-// round-robin, activations read from global memory (cached), partials summed
-// in LDS in wave order.
-template <int MT>
+// round-robin, activations read from global memory (cached; int8 q is put
+// in the decoded byte order in registers), partials summed in LDS in wave
+// order.
+template <bool kI8, int MT>
 __global__ __launch_bounds__(512) void gemv5_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
-                                                    const uint16_t* __restrict__ x, int M, float* __restrict__ y)
+                                                    const void* __restrict__ x, const float* __restrict__ s_x,
+                                                    int M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
 {
     constexpr int NI = MT < 4 ? MT : 4;
     __shared__ float red[8 * NI * 64];
@@ -228,11 +312,23 @@ __global__ __launch_bounds__(512) void gemv5_kernel(const uint8_t* __restrict__ 
     const uint32_t* words = (const uint32_t*)packed;
     const uint32_t* scales = (const uint32_t*)(packed + t5_plane_bytes(N, K));
     const int mrow = r < M ? r : M - 1;
-    const uint16_t* xr = x + (int64_t)mrow * K + 32 * g;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int kt = wave; kt < nkt; kt += nw) {
         const Tile5 t = load_tile5(words, scales, rt, kt, nkt, r, g);
-        tile5_bf16<MT>(t, xr + (int64_t)kt * kTileK, acc);
+        if constexpr (kI8) {
+            // this lane's four 32-byte slots of q, put in the decoded byte order in registers
+            const int8_t* qr = (const int8_t*)x + (int64_t)mrow * K + (int64_t)kt * kTileK + 32 * g;
+            u32x4 A[4][2];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                q_decoded_order(*(const u32x4*)(qr + kBlockK * j), *(const u32x4*)(qr + kBlockK * j + 16), A[j][0],
+                                A[j][1]);
+            tile5_i8<MT>(t, [&](int jj, int h) { return A[jj][h]; }, acc, acc_dbg, N, M, rt * kTileRows + r,
+                         (int)(K >> 8), 2 * kt, g);
+        } else {
+            const uint16_t* xr = (const uint16_t*)x + (int64_t)mrow * K + 32 * g;
+            tile5_bf16<MT>(t, xr + (int64_t)kt * kTileK, acc);
+        }
     }
 #pragma unroll
     for (int q = 0; q < NI; ++q) red[(wave * NI + q) * 64 + lane] = acc[q];
@@ -245,7 +341,7 @@ __global__ __launch_bounds__(512) void gemv5_kernel(const uint8_t* __restrict__ 
         if (l < lanes_used && m < M && row < N) {
             float sum = 0.f;
             for (int w = 0; w < nw; ++w) sum += red[(w * NI + q) * 64 + l];
-            y[(int64_t)m * N + row] = sum;
+            y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
         }
     }
 }
@@ -268,15 +364,15 @@ hipError_t launch_pack5(const int8_t* lv, const float* s_lo, const float* s_hi, 
     return hipGetLastError();
 }
 
-template <int MT>
+template <bool kI8, int MT>
 static hipError_t gemv5_oneshot_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N,
-                                         int64_t K, const uint16_t* x, int M, float* y)
+                                         int64_t K, const void* x, const float* s_x, int M, float* y, int32_t* acc)
 {
 #define TERN5_CASE(UU, XX)                                                                                     \
     if (c.U == UU && c.XC == XX) {                                                                             \
-        if (!oneshot_resident(gemv5_oneshot_kernel<MT, UU, XX>, c)) return hipErrorNotSupported;              \
-        gemv5_oneshot_kernel<MT, UU, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(          \
-            packed, N, K, x, M, y);                                                                            \
+        if (!oneshot_resident(gemv5_oneshot_kernel<kI8, MT, UU, XX>, c)) return hipErrorNotSupported;         \
+        gemv5_oneshot_kernel<kI8, MT, UU, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(     \
+            packed, N, K, x, s_x, M, y, acc);                                                                  \
         return hipGetLastError();                                                                              \
     }
     TERN5_CASE(1, 1) TERN5_CASE(2, 1) TERN5_CASE(3, 1) TERN5_CASE(4, 1)
@@ -289,35 +385,47 @@ static hipError_t gemv5_oneshot_dispatch(const OneShot& c, hipStream_t stream, c
     return hipErrorNotSupported;
 }
 
-// Waves of U = 1..4 units per SIMD (registers of the M <= 4 instances; the
-// occupancy query has the last word).
-static const OneShotShape kFiveShape = {0, 0, 16, {0, 8, 6, 4, 4}};
-
-hipError_t launch_gemv5_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
-                             hipStream_t stream)
+template <bool kI8>
+static hipError_t launch_gemv5(const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
+                               int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
-    OneShotShape s = kFiveShape;
-    s.x_row_bytes = (K + 8) * 2;
-    s.x_src_bytes = 2 * K;
+    // waves of U = 1..4 units per SIMD (registers: bf16 60, 77, 95-99 and
+    // 111-115 VGPRs, int8 68, 74, 90 and 106; the occupancy query has the
+    // last word)
+    const OneShotShape s = kI8 ? OneShotShape{K + 16, K, 32, {0, 7, 6, 5, 4}}
+                               : OneShotShape{(K + 8) * 2, 2 * K, 16, {0, 8, 6, 4, 4}};
     OneShot c;
     if (pick_oneshot(N, K, M, s, c)) {
         const int m = (int)M;
+        // 8 activation chunks per thread are instantiated for MT = 16 only
         const bool wide = M > 4 || c.XC == 8;
         hipError_t e;
-        if (wide) e = gemv5_oneshot_dispatch<16>(c, stream, packed, N, K, x, m, y);
-        else if (M == 1) e = gemv5_oneshot_dispatch<1>(c, stream, packed, N, K, x, m, y);
-        else if (M == 2) e = gemv5_oneshot_dispatch<2>(c, stream, packed, N, K, x, m, y);
-        else e = gemv5_oneshot_dispatch<4>(c, stream, packed, N, K, x, m, y);
+        if (wide) e = gemv5_oneshot_dispatch<kI8, 16>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        else if (M == 1) e = gemv5_oneshot_dispatch<kI8, 1>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        else if (M == 2) e = gemv5_oneshot_dispatch<kI8, 2>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        else e = gemv5_oneshot_dispatch<kI8, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);
         if (e != hipErrorNotSupported) return e;
     }
     const int64_t nkt = K / kTileK;
     const int nw = nkt >= 8 ? 8 : (int)nkt;
     const dim3 grid((unsigned)((N + 15) / 16)), block(64 * nw);
-    if (M == 1) gemv5_kernel<1><<<grid, block, 0, stream>>>(packed, N, K, x, (int)M, y);
-    else if (M == 2) gemv5_kernel<2><<<grid, block, 0, stream>>>(packed, N, K, x, (int)M, y);
-    else if (M <= 4) gemv5_kernel<4><<<grid, block, 0, stream>>>(packed, N, K, x, (int)M, y);
-    else gemv5_kernel<16><<<grid, block, 0, stream>>>(packed, N, K, x, (int)M, y);
+    if (M == 1) gemv5_kernel<kI8, 1><<<grid, block, 0, stream>>>(packed, N, K, x, s_x, (int)M, y, acc);
+    else if (M == 2) gemv5_kernel<kI8, 2><<<grid, block, 0, stream>>>(packed, N, K, x, s_x, (int)M, y, acc);
+    else if (M <= 4) gemv5_kernel<kI8, 4><<<grid, block, 0, stream>>>(packed, N, K, x, s_x, (int)M, y, acc);
+    else gemv5_kernel<kI8, 16><<<grid, block, 0, stream>>>(packed, N, K, x, s_x, (int)M, y, acc);
     return hipGetLastError();
+}
+
+hipError_t launch_gemv5_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                             hipStream_t stream)
+{
+    return launch_gemv5<false>(packed, N, K, x, nullptr, M, y, nullptr, stream);
+}
+
+hipError_t launch_gemv5_i8(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
+                           float* y, int32_t* acc, hipStream_t stream)
+{
+    return launch_gemv5<true>(packed, N, K, q, s_x, M, y, acc, stream);
 }
 
 }  // namespace tern

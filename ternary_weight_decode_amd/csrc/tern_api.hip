@@ -359,6 +359,21 @@ int tern5_pack(const int8_t* levels, const float* s_lo, const float* s_hi, int64
     return finish(tern::launch_pack5(levels, s_lo, s_hi, N, K, (uint8_t*)packed, (hipStream_t)stream));
 }
 
+int tern5_gemv_i8(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M, float* y,
+                  int32_t* acc_dbg, void* stream)
+{
+    if (N < 0 || K < 0 || K % 512 != 0 || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
+    if (N == 0 || M == 0) return TERN_OK;
+    if (!y || !s_x || (K > 0 && (!packed || !q))) return TERN_E_NULL;
+    if ((packed && !aligned16(packed)) || (q && !aligned16(q)) || !aligned4(y) || !aligned4(s_x) ||
+        (acc_dbg && !aligned4(acc_dbg)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    if (K == 0) return finish(tern::launch_fill_zero(y, M * N * 4, (hipStream_t)stream));
+    return finish(tern::launch_gemv5_i8((const uint8_t*)packed, N, K, q, s_x, M, y, acc_dbg, (hipStream_t)stream));
+}
+
 int tern5_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream)
 {
     if (N < 0 || K < 0 || K % 512 != 0 || M < 0 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;

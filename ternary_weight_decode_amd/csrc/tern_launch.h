@@ -86,6 +86,8 @@ hipError_t launch_pack5(const int8_t* lv, const float* s_lo, const float* s_hi, 
                         uint8_t* packed, hipStream_t stream);
 hipError_t launch_gemv5_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                              hipStream_t stream);
+hipError_t launch_gemv5_i8(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
+                           float* y, int32_t* acc, hipStream_t stream);
 
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream);

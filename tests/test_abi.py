@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 5
+    assert L.tern_abi_version() == 6
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -146,6 +146,13 @@ def test_five_level_sizes_and_argument_errors():
     assert pk(p, None, p, 16, 512, p, None) == E_NULL
     assert pk(m, p, p, 16, 512, p, None) == E_ALIGN
     assert pk(p, p, ctypes.c_void_p(0x10002), 16, 512, p, None) == E_ALIGN
+    gi = L.tern5_gemv_i8
+    assert gi(p, 16, 768, p, p, 1, p, None, None) == E_SHAPE
+    assert gi(p, 16, 512, p, p, 17, p, None, None) == E_SHAPE
+    assert gi(None, 0, 512, None, None, 1, None, None, None) == E_OK
+    assert gi(p, 16, 512, p, None, 1, p, None, None) == E_NULL        # s_x
+    assert gi(p, 16, 512, m, p, 1, p, None, None) == E_ALIGN
+    assert gi(p, 16, 512, p, p, 1, p, ctypes.c_void_p(0x10002), None) == E_ALIGN
 
 
 def test_fv5b_argument_errors():

@@ -1,7 +1,8 @@
 """GPU parity of the five-level (FV5-style) calls against the CPU oracle
-(oracle/fv5.py) on the same seeded inputs: packed bytes bit for bit, GEMV
-outputs within a relative L2 error of 1e-5 of the fp64 oracle (fp32
-accumulation of exact bf16 products gives ~1e-7)."""
+(oracle/fv5.py) on the same seeded inputs: packed bytes and the int8 path's
+per-block sums of each magnitude bit for bit, GEMV outputs within a relative
+L2 error of 1e-5 of the fp64 oracle (fp32 accumulation of exact products
+gives ~1e-7)."""
 import numpy as np
 import pytest
 
@@ -154,3 +155,59 @@ def test_pack5_full_size_sampled_tiles(tw):
         assert np.array_equal(p[rt * plane_tile:(rt + 1) * plane_tile], sub[:plane_tile])
         s0 = planes_total + rt * scale_tile
         assert np.array_equal(p[s0:s0 + scale_tile], sub[plane_tile:])
+
+
+# ---------------------------------------------------------------- int8 activations
+
+def gen_q(m, k, seed):
+    rng = np.random.default_rng(seed)
+    return rng.integers(-127, 128, size=(m, k)).astype(np.int8), rng.uniform(0.005, 0.05, m).astype(np.float32)
+
+
+def test_gemv5_i8_golden_examples(tw):
+    import torch
+    from test_oracle_fv5 import _read_golden, golden_inputs, golden_q
+    for name, e in _read_golden().items():
+        lv, lo, hi, _ = golden_inputs(e)
+        q, sx = golden_q(e["K"])
+        acc = torch.empty((1, e["N"], e["K"] // 256, 2), dtype=torch.int32, device="cuda")
+        y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), e["N"], e["K"], dev(q), dev(sx), acc=acc))
+        want = np.zeros((1, e["N"], e["K"] // 256, 2), np.int64)
+        for (r, b), (a_lo, a_hi) in e["acc"].items():
+            want[0, r, b] = (a_lo, a_hi)
+        assert np.array_equal(host(acc).astype(np.int64), want), name
+        wy = np.zeros(e["N"], np.float32)
+        for r, v in e["yq"].items():
+            wy[r] = v
+        assert np.array_equal(y[0], wy), name
+
+
+I8_CASES = [(16, 512, 1), (37, 1536, 1), (37, 1536, 2), (100, 2048, 3), (300, 4096, 4), (1000, 2560, 5),
+            (600, 1024, 8), (129, 3072, 16), (4100, 512, 1), (40, 24576, 8), (64, 32768, 16)]
+
+
+@pytest.mark.parametrize("n,k,m", I8_CASES)
+def test_gemv5_i8_block_sums_exact(tw, n, k, m):
+    import torch
+    lv, lo, hi, _ = gen(n, k, 1, seed=5 * n + k + m)
+    q, sx = gen_q(m, k, seed=n + m)
+    acc = torch.empty((m, n, k // 256, 2), dtype=torch.int32, device="cuda")
+    y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx), acc=acc))
+    acc64, y64, _ = fv5.gemv_i8_levels(lv, lo, hi, q, sx)
+    assert np.array_equal(host(acc).astype(np.int64), acc64)
+    assert rel_l2(y, y64) < TOL
+    # without the debug output the same kernel gives the same y
+    y2 = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx)))
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("n,k", FULL)
+@pytest.mark.parametrize("m", [1, 8])
+def test_gemv5_i8_full_size_sampled_rows(tw, n, k, m):
+    lv, lo, hi, _ = gen(n, k, 1, seed=n + 2 * k + m)
+    q, sx = gen_q(m, k, seed=n + m)
+    y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx)))
+    rng = np.random.default_rng(n + 1)
+    rows = np.unique(np.concatenate([rng.choice(n, 48, replace=False), [0, 15, 16, n - 1]]))
+    _, want, _ = fv5.gemv_i8_levels(lv[rows], lo[rows], hi[rows], q, sx)
+    assert rel_l2(y[:, rows], want) < TOL
