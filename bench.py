@@ -49,7 +49,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
                     help="--mode prefill: run only this shape and M (e.g. gate:2048)")
-    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "fv5", "copy"],
+    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "fv5", "sweep", "copy"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
                          "copy: plain 256 MiB device copies (reference for memory-counter scaling)")
@@ -403,6 +403,32 @@ def mode_head(args, tw, synth, torch):
     print(json.dumps({"mode": "head", "rows": out}), flush=True)
 
 
+def mode_sweep(args, tw, synth, torch):
+    """The M = 1 ternary GEMV (bf16 activations) at K = 4096 over N from 1024 to 196608 rows: how the
+    per-launch latency gives way to streaming as the matrix grows.  Weights rotate over >= 1 GB of
+    copies so each launch reads HBM; us per launch from hipGraph replays."""
+    out = []
+    k = 4096
+    rng = np.random.default_rng(17)
+    x = torch.from_numpy(synth.gen_x_bf16(rng, 1, k).view(np.int16)).cuda()
+    for n in (1024, 4096, 12288, 24576, 49152, 98304, 196608):
+        t = torch.from_numpy(synth.gen_ternary(rng, n, k)).cuda()
+        sc = torch.from_numpy(synth.gen_scales(rng, n, k // 128).view(np.int16)).cuda()
+        packed = tw.tern_pack(t, sc)
+        del t, sc
+        copies = rotate_copies(torch, packed)
+        y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        g = capture(torch, lambda: [tw.tern_gemv(c, n, k, x, y=y) for c in copies])
+        ms = time_replays(torch, g, 5) / len(copies)
+        nbytes = tw.tern_packed_bytes(n, k) + 2 * k + 4 * n
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out.append({"n_k": [n, k], "MB": round(nbytes / 1e6, 2), "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+                    "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+        log(f"sweep N={n}: {ms * 1e3:.2f} us, {gbs:.0f} GB/s")
+        del g, copies, packed
+    print(json.dumps({"mode": "sweep", "rows": out}), flush=True)
+
+
 FV5_UNITS = (("qkv", ("q", "k", "v")), ("o", ("o",)), ("gateup", ("gate", "up")), ("down", ("down",)))
 
 
@@ -480,6 +506,8 @@ def main():
         return mode_head(args, tw, synth, torch)
     if args.mode == "fv5":
         return mode_fv5(args, tw, synth, torch)
+    if args.mode == "sweep":
+        return mode_sweep(args, tw, synth, torch)
     if args.mode == "copy":
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
