@@ -211,3 +211,19 @@ def test_gemv5_i8_full_size_sampled_rows(tw, n, k, m):
     rows = np.unique(np.concatenate([rng.choice(n, 48, replace=False), [0, 15, 16, n - 1]]))
     _, want, _ = fv5.gemv_i8_levels(lv[rows], lo[rows], hi[rows], q, sx)
     assert rel_l2(y[:, rows], want) < TOL
+
+
+def test_gemv5_multi_round_grid(tw):
+    """65541 x 4096 five-level weights: the one-pass grid runs in several
+    rounds; sampled rows (incl. the ragged last tile), bf16 and int8."""
+    n, k, m = 65541, 4096, 2
+    lv, lo, hi, x = gen(n, k, m, seed=41)
+    q, sx = gen_q(m, k, seed=42)
+    p = gpu_pack(tw, lv, lo, hi)
+    y = host(tw.tern5_gemv(p, n, k, dev(x)))
+    yi = host(tw.tern5_gemv_i8(p, n, k, dev(q), dev(sx)))
+    rows = np.unique(np.concatenate([np.random.default_rng(3).choice(n, 200, replace=False), np.arange(n - 21, n)]))
+    want, _ = fv5.gemv_bf16_levels(lv[rows], lo[rows], hi[rows], x)
+    assert rel_l2(y[:, rows], want) < TOL
+    _, want_i, _ = fv5.gemv_i8_levels(lv[rows], lo[rows], hi[rows], q, sx)
+    assert rel_l2(yi[:, rows], want_i) < TOL

@@ -347,3 +347,27 @@ def test_full_8b_shapes_sampled(tw, proj):
     # occupancy of the packed blob matches the drawn states
     c = host(tw.tern_stats(p, n, k))
     assert c[0] == np.count_nonzero(t) and c[1] == np.count_nonzero(t < 0) and c[2] == 0
+
+
+@pytest.mark.parametrize("m", [1, 3])
+def test_gemv_multi_round_grid(tw, m):
+    """A matrix too large for any one-round split (65541 x 4096): the one-pass
+    kernel's grid runs in several rounds.  Sampled rows (incl. the ragged last
+    tile) against the oracle, bf16 and int8 activations; the int8 block
+    accumulators of the sampled rows bit for bit."""
+    import torch
+    n, k = 65541, 4096
+    t, s, x = gen(n, k, m, seed=m)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemv(p, n, k, dev(x)))
+    rows = np.unique(np.concatenate([np.random.default_rng(m).choice(n, 200, replace=False),
+                                     np.arange(n - 21, n)]))
+    packed_rows = oracle.pack(t[rows], s[rows])
+    y64, _ = oracle.gemv_bf16(packed_rows, len(rows), k, x)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    q, sx = oracle.quantize_i8(x)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    yi = host(tw.tern_gemv_i8(p, n, k, dev(q), dev(sx), acc=acc))
+    acc_o, yi64, _ = oracle.tern_i8(packed_rows, len(rows), k, q, sx)
+    assert np.array_equal(host(acc)[:, rows], acc_o)
+    assert oracle.rel_l2(yi[:, rows], yi64) <= TOL
