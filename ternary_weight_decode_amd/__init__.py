@@ -28,7 +28,7 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
-           "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
+           "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed", "tern_gemv_config")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
@@ -83,6 +83,8 @@ def lib():
         L.fv5b_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.fv5b_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         L.fv5b_embed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p]
+        L.tern_gemv_config.restype = ctypes.c_int
+        L.tern_gemv_config.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i64)]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -440,3 +442,19 @@ def fv5b_embed(w, s, ids, f32=True, bf16=True, out=None, out_bf16=None, stream=N
     _check("fv5b_embed", lib().fv5b_embed(_ptr(w), _ptr(s), v, k, _ptr(ids), m, _ptr(out), _ptr(out_bf16),
                                           _stream(stream)))
     return out, out_bf16
+
+
+GEMV_KINDS = {"ternary_bf16": 0, "ternary_int8": 1, "fv5_bf16": 2, "fv5_int8": 3}
+
+
+def tern_gemv_config(n: int, k: int, m: int, kind: str = "ternary_bf16"):
+    """The one-pass launch configuration for this GEMV shape (host-side, no device needed), as a dict,
+    or None when another kernel takes the shape."""
+    out = (_i64 * 8)()
+    rc = lib().tern_gemv_config(n, k, m, GEMV_KINDS[kind], out)
+    if rc < 0:
+        _check("tern_gemv_config", -rc)
+    if rc == 0:
+        return None
+    keys = ("R", "waves", "U", "XC", "grid", "lds", "rounds", "MT")
+    return dict(zip(keys, (int(v) for v in out)))

@@ -385,17 +385,22 @@ static hipError_t gemv5_oneshot_dispatch(const OneShot& c, hipStream_t stream, c
     return hipErrorNotSupported;
 }
 
+// waves of U = 1..4 units per SIMD (registers: bf16 60, 77, 95-99 and
+// 111-115 VGPRs, int8 68, 74, 90 and 106; the occupancy query has the last
+// word)
+bool gemv5_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
+{
+    const OneShotShape s = i8 ? OneShotShape{K + 16, K, 32, {0, 7, 6, 5, 4}}
+                              : OneShotShape{(K + 8) * 2, 2 * K, 16, {0, 8, 6, 4, 4}};
+    return pick_oneshot(N, K, M, s, c);
+}
+
 template <bool kI8>
 static hipError_t launch_gemv5(const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
                                int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
-    // waves of U = 1..4 units per SIMD (registers: bf16 60, 77, 95-99 and
-    // 111-115 VGPRs, int8 68, 74, 90 and 106; the occupancy query has the
-    // last word)
-    const OneShotShape s = kI8 ? OneShotShape{K + 16, K, 32, {0, 7, 6, 5, 4}}
-                               : OneShotShape{(K + 8) * 2, 2 * K, 16, {0, 8, 6, 4, 4}};
     OneShot c;
-    if (pick_oneshot(N, K, M, s, c)) {
+    if (gemv5_oneshot_config(N, K, M, kI8, c)) {
         const int m = (int)M;
         // 8 activation chunks per thread are instantiated for MT = 16 only
         const bool wide = M > 4 || c.XC == 8;

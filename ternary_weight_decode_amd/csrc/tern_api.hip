@@ -467,3 +467,26 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
 }
 
 }  // extern "C"
+
+extern "C" {
+
+int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out)
+{
+    if (!out) return -TERN_E_NULL;
+    if (kind < 0 || kind > 3 || N < 1 || K < 1 || M < 1 || M > TERN_MAX_M_GEMV) return -TERN_E_SHAPE;
+    const bool i8 = (kind & 1) != 0;
+    tern::OneShot c{};
+    const bool one = kind < 2 ? tern::gemv_oneshot_config(N, K, M, i8, c) : tern::gemv5_oneshot_config(N, K, M, i8, c);
+    if (!one) return 0;
+    out[0] = c.R;
+    out[1] = c.nw;
+    out[2] = c.U;
+    out[3] = c.XC;
+    out[4] = c.grid;
+    out[5] = (int64_t)c.lds;
+    out[6] = c.rounds ? 1 : 0;
+    out[7] = (M > 4 || c.XC == 8) ? 16 : (M == 1 ? 1 : (M == 2 ? 2 : 4));
+    return 1;
+}
+
+}  // extern "C"

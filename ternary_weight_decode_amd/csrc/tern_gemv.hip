@@ -560,6 +560,11 @@ static OneShotShape oneshot_shape(int64_t K, bool i8)
 }
 
 // the one-pass path for M <= 16 when it applies; hipErrorNotSupported otherwise
+bool gemv_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
+{
+    return pick_oneshot(N, K, M, oneshot_shape(K, i8), c);
+}
+
 static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
                                  int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 6
+    assert L.tern_abi_version() == 7
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
