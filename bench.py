@@ -489,7 +489,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path runs on a single "
-              f"MI355X; see the design notes for how it would shard)", file=sys.stderr)
+              f"MI355X; across GPUs it would shard every linear by output rows, each GPU holding and computing "
+              f"its rows, with an all-gather of y where the next linear needs the whole vector)", file=sys.stderr)
         sys.exit(2)
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)

@@ -5,8 +5,8 @@ brute-force references.  Only the tests, ``__graft_entry__.smoke()`` and the
 benchmark's ``cpu_baseline`` leg may import this package; the product path
 never does.  It shares no code with the HIP library.
 
-Every function states what it follows; the full list of readings of the
-pages is kept in the repository's design notes.  Functions with no pin other
+Every function states what it follows and the reading of the pages it takes
+where they are silent.  Functions with no pin other
 than their own definition say "parity unpinned" (none at present: each is
 pinned by a worked example, a closed form, an invariant or brute force in
 ``tests/test_oracle.py``).

@@ -8,8 +8,8 @@
  * library: the packed layout is re-implemented here from its written
  * definition, bit by bit.
  *
- * What each function follows (pages of the Neutrino-1 discussion, see the
- * repository's design notes for the full list of readings):
+ * What each function follows (pages of the Neutrino-1 discussion, and the
+ * reading taken where they are silent):
  *  - ternary linear: "Fermion Research, 3진 계열 포맷으로 직접 학습한 Neutrino-1
  *    모델군 3종 공개" (discuss.pytorch.kr), section "학습 중에 포맷이 있어야 하는
  *    이유", equation y_j = sum_i w_ij x_i; with w in {-1,0,+1} the product is
