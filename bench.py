@@ -389,6 +389,23 @@ def mode_head(args, tw, synth, torch):
         out.append({"call": name, "V": v, "K": k, "us": round(ms * 1e3, 2),
                     "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
         del g
+    # the argmax fused with the next token's embedding row (a 151936 x hidden table), against the two calls
+    E = torch.from_numpy(np.random.default_rng(12).integers(-127, 128, (v, k), dtype=np.int8)).cuda()
+    ES = torch.from_numpy(np.random.default_rng(13).uniform(0.002, 0.02, (v, k // 256)).astype(np.float32)).cuda()
+    eb = torch.empty((1, k), dtype=torch.bfloat16, device="cuda")
+    idx1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    pair = {
+        "fv5b_head_argmax_then_embed": lambda c: (idx1.copy_(tw.fv5b_head_argmax(c, S, x, workspace=ws)[0]),
+                                                  tw.fv5b_embed(E, ES, idx1, f32=False, out_bf16=eb)),
+        "fv5b_head_argmax_embed": lambda c: tw.fv5b_head_argmax_embed(c, S, x, E, ES, workspace=ws, f32=False,
+                                                                      out_bf16=eb),
+    }
+    for name, fn in pair.items():
+        g = capture(torch, lambda: [fn(c) for c in copies])
+        ms = time_replays(torch, g, 5) / len(copies)
+        out.append({"call": name, "V": v, "K": k, "us": round(ms * 1e3, 2),
+                    "GB/s": round(blk_bytes / (ms * 1e-3) / 1e9, 1)})
+        del g
     # embedding rows (the step before the first linear): 1 token, and a 512-token prefill batch
     for m in (1, 512):
         ids = torch.from_numpy(np.random.default_rng(m).integers(0, v, m).astype(np.int32)).cuda()

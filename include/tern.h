@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 7
+#define TERN_ABI_VERSION 8
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -323,6 +323,18 @@ int fv5b_head_argmax(const int8_t* W, const float* S, int64_t V, int64_t K, cons
                      int32_t* idx, float* val, float* logits, void* workspace, void* stream);
 int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
                         int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+
+/* The end of one decode token and the start of the next in one call:
+ * fv5b_head_argmax (bf16 x), then the embedding row of each chosen index
+ * idx[m] from the block-scaled table E int8 [Ve][Ke] with scales ES f32
+ * [Ve][Ke/256], written as fv5b_embed writes it (emb fp32 [M][Ke], emb_bf16
+ * [M][Ke]; either may be NULL, not both; an index outside [0, Ve) gives a
+ * zero row).  The gather runs inside the argmax's final kernel, so the index
+ * never travels through memory first.  Ke % 256 == 0; E, emb and emb_bf16
+ * 16-byte aligned. */
+int fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                           int32_t* idx, float* val, float* logits, void* workspace, const int8_t* E, const float* ES,
+                           int64_t Ve, int64_t Ke, float* emb, uint16_t* emb_bf16, void* stream);
 
 /* Embedding rows for M token ids (the step before the first linear):
  *   out[m][k] = W[ids[m]][k] * S[ids[m]][k/256], one fp32 rounding;

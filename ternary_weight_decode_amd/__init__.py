@@ -15,7 +15,8 @@ Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
 (FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv[_i8]``, and the
 block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
-``fv5b_head_argmax[_i8]``, ``fv5b_embed``.
+``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed``, and the
+launch-configuration view ``tern_gemv_config``.
 """
 from __future__ import annotations
 
@@ -28,11 +29,12 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv", "i8_head_gemv_i8", "tern_gemm_prefill",
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
-           "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed", "tern_gemv_config")
+           "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
+           "tern_gemv_config")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
-               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_embed")
+               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -83,6 +85,8 @@ def lib():
         L.fv5b_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.fv5b_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         L.fv5b_embed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p]
+        L.fv5b_head_argmax_embed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p, _p, _i64, _i64, _p, _p,
+                                             _p]
         L.tern_gemv_config.restype = ctypes.c_int
         L.tern_gemv_config.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i64)]
         for name in _INT_STATUS:
@@ -424,6 +428,31 @@ def fv5b_head_argmax_i8(w, s, q, s_x, workspace=None, logits=None, stream=None):
                                                             _ptr(idx), _ptr(val), _ptr(logits), _ptr(workspace),
                                                             _stream(stream)))
     return idx, val
+
+
+def fv5b_head_argmax_embed(w, s, x, e, es, workspace=None, logits=None, f32=True, bf16=True, out=None,
+                           out_bf16=None, stream=None):
+    """Greedy argmax over the block-scaled head's logits of bf16 x, then the embedding rows of the chosen
+    indices from the block-scaled table (e int8 [Ve,Ke], es fp32 [Ve,Ke/256]), in one call:
+    (idx int32 [M], val fp32 [M], emb fp32 [M,Ke] or None, emb bf16 [M,Ke] or None)."""
+    import torch
+    v, k, m = _fv5b_args(w, s, x, (torch.bfloat16, torch.int16, torch.uint16))
+    _need(e, "E", (torch.int8,), 2)
+    _need(es, "ES", (torch.float32,), 2)
+    ve, ke = e.shape
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, x.device)
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    val = torch.empty(m, dtype=torch.float32, device=x.device)
+    if out is None and f32:
+        out = torch.empty((m, ke), dtype=torch.float32, device=x.device)
+    if out_bf16 is None and bf16:
+        out_bf16 = torch.empty((m, ke), dtype=torch.bfloat16, device=x.device)
+    _check("fv5b_head_argmax_embed",
+           lib().fv5b_head_argmax_embed(_ptr(w), _ptr(s), v, k, _ptr(x), m, _ptr(idx), _ptr(val), _ptr(logits),
+                                        _ptr(workspace), _ptr(e), _ptr(es), ve, ke, _ptr(out), _ptr(out_bf16),
+                                        _stream(stream)))
+    return idx, val, out, out_bf16
 
 
 def fv5b_embed(w, s, ids, f32=True, bf16=True, out=None, out_bf16=None, stream=None):

@@ -452,6 +452,22 @@ int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, c
                                                    (hipStream_t)stream));
 }
 
+int fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                           int32_t* idx, float* val, float* logits, void* workspace, const int8_t* E, const float* ES,
+                           int64_t Ve, int64_t Ke, float* emb, uint16_t* emb_bf16, void* stream)
+{
+    int rc = fv5b_head_check(W, S, V, K, x, nullptr, false, M, workspace, false);
+    if (rc) return rc;
+    if (Ve < 1 || Ke < 256 || Ke % 256 != 0) return TERN_E_SHAPE;
+    if (!idx || !val || !E || !ES || (!emb && !emb_bf16)) return TERN_E_NULL;
+    if (!aligned4(idx) || !aligned4(val) || (logits && !aligned4(logits)) || ((uintptr_t)workspace & 7) ||
+        !aligned16(E) || !aligned4(ES) || (emb && !aligned16(emb)) || (emb_bf16 && !aligned16(emb_bf16)))
+        return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_argmax_embed(W, S, V, K, x, M, logits, idx, val, workspace, E, ES, Ve, Ke,
+                                                      emb, emb_bf16, (hipStream_t)stream));
+}
+
 int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M, float* out,
                uint16_t* out_bf16, void* stream)
 {

@@ -201,11 +201,62 @@ __device__ __forceinline__ void head_argmax_epilogue(const HeadArgmax& am, const
     }
 }
 
-// Maximum over the row tiles' keys of activation row m = blockIdx.x.
+// Rows of a block-scaled int8 table (FV5B-style: W int8 [V][K], S f32
+// [V][K/256]) for token ids: out[m][k] = W[id][k] * S[id][k/256] (one fp32
+// rounding) and out_bf16 its nearest-even bf16; an id outside [0, V) gives a
+// zero row without reading W.  Either output may be null.
+struct EmbedRows {
+    const int8_t* W;
+    const float* S;
+    int64_t V, K;
+    float* out;
+    uint16_t* out_bf16;
+};
+
+// 16 weights (chunk c) of output row m for token id
+__device__ __forceinline__ void embed_chunk(const EmbedRows& e, int64_t id, int64_t m, int64_t c)
+{
+    float f[16];
+    if (id >= 0 && id < e.V) {
+        const u32x4 w = *(const u32x4*)(e.W + id * e.K + 16 * c);
+        const float sc = e.S[id * (e.K / 256) + (16 * c) / 256];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * sc;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) f[i] = 0.f;
+    }
+    if (e.out) {
+        f32x4* o = (f32x4*)(e.out + m * e.K + 16 * c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
+    }
+    if (e.out_bf16) {
+        uint32_t h[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // nearest-even bf16 of a finite fp32 value: add 0x7FFF plus the
+            // lowest kept bit, keep the high half
+            uint32_t b0 = __builtin_bit_cast(uint32_t, f[2 * i]);
+            uint32_t b1 = __builtin_bit_cast(uint32_t, f[2 * i + 1]);
+            b0 = (b0 + 0x7FFFu + ((b0 >> 16) & 1u)) >> 16;
+            b1 = (b1 + 0x7FFFu + ((b1 >> 16) & 1u)) >> 16;
+            h[i] = b0 | (b1 << 16);
+        }
+        u32x4* o = (u32x4*)(e.out_bf16 + m * e.K + 16 * c);
+        o[0] = u32x4{h[0], h[1], h[2], h[3]};
+        o[1] = u32x4{h[4], h[5], h[6], h[7]};
+    }
+}
+
+// Maximum over the row tiles' keys of activation row m = blockIdx.x; with
+// emb.W set, the workgroup then writes the embedding row of the chosen index
+// (the next token's input) into row m of emb's outputs.
 __global__ __launch_bounds__(1024) void head_argmax_finish_kernel(const unsigned long long* __restrict__ part,
                                                                   int64_t nrt, int M, int32_t* __restrict__ idx,
-                                                                  float* __restrict__ val)
+                                                                  float* __restrict__ val, EmbedRows emb)
 {
+    __shared__ int64_t chosen;
     __shared__ unsigned long long best_of_wave[16];
     const int m = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     unsigned long long best = 0;
@@ -223,9 +274,14 @@ __global__ __launch_bounds__(1024) void head_argmax_finish_kernel(const unsigned
     __syncthreads();
     if (threadIdx.x == 0) {
         for (int w = 1; w < (int)(blockDim.x >> 6); ++w) best = best_of_wave[w] > best ? best_of_wave[w] : best;
-        idx[m] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
+        const uint32_t v = 0xFFFFFFFFu - (uint32_t)best;
+        idx[m] = (int32_t)v;
         val[m] = unorder_bits((uint32_t)(best >> 32));
+        chosen = v;
     }
+    if (emb.W == nullptr) return;   // uniform across the workgroup
+    __syncthreads();
+    for (int64_t c = threadIdx.x; c < emb.K / 16; c += blockDim.x) embed_chunk(emb, chosen, m, c);
 }
 
 // Head kernel when all of x fits in LDS: one 16-row tile per wave over the
@@ -411,13 +467,14 @@ bool head_argmax_fits(int64_t K, int64_t M, bool int8_act)
 template <bool kInt8, bool kBlk = false>
 static hipError_t launch_head_argmax(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                      const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
-                                     hipStream_t stream)
+                                     hipStream_t stream, EmbedRows emb = EmbedRows{nullptr, nullptr, 0, 0, nullptr,
+                                                                                  nullptr})
 {
     const HeadArgmax am{(unsigned long long*)ws};
     hipError_t e = launch_head_fast<kInt8, kHeadTpw, kBlk>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
     if (e != hipSuccess) return e;
     head_argmax_finish_kernel<<<dim3((unsigned)M), dim3(1024), 0, stream>>>((const unsigned long long*)ws,
-                                                                           (V + 15) / 16, (int)M, idx, val);
+                                                                           (V + 15) / 16, (int)M, idx, val, emb);
     return hipGetLastError();
 }
 
@@ -461,48 +518,13 @@ hipError_t launch_fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V
     return launch_head_argmax<true, true>(W, S, V, K, q, s_x, M, y, idx, val, ws, stream);
 }
 
-// Embedding rows: one thread per 16 weights of an output row; out[m][k] =
-// W[id][k] * S[id][k/256] (one fp32 rounding), out_bf16 its nearest-even
-// bf16; an id outside [0, V) writes a zero row without reading W.
-__global__ void fv5b_embed_kernel(const int8_t* __restrict__ W, const float* __restrict__ S, int64_t V, int64_t K,
-                                  const int32_t* __restrict__ ids, int64_t M, float* __restrict__ out,
-                                  uint16_t* __restrict__ out_bf16)
+// Embedding rows: one thread per 16 weights of an output row (embed_chunk).
+__global__ void fv5b_embed_kernel(EmbedRows e, const int32_t* __restrict__ ids, int64_t M)
 {
-    const int64_t per_row = K / 16, total = M * per_row;
+    const int64_t per_row = e.K / 16, total = M * per_row;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = t / per_row, c = t - m * per_row;
-        const int64_t id = ids[m];
-        float f[16];
-        if (id >= 0 && id < V) {
-            const u32x4 w = *(const u32x4*)(W + id * K + 16 * c);
-            const float sc = S[id * (K / 256) + (16 * c) / 256];
-#pragma unroll
-            for (int i = 0; i < 16; ++i) f[i] = (float)(int8_t)(w[i >> 2] >> (8 * (i & 3))) * sc;
-        } else {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) f[i] = 0.f;
-        }
-        if (out) {
-            f32x4* o = (f32x4*)(out + m * K + 16 * c);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[i] = f32x4{f[4 * i], f[4 * i + 1], f[4 * i + 2], f[4 * i + 3]};
-        }
-        if (out_bf16) {
-            uint32_t h[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // nearest-even bf16 of a finite fp32 value: add 0x7FFF plus the
-                // lowest kept bit, keep the high half
-                uint32_t b0 = __builtin_bit_cast(uint32_t, f[2 * i]);
-                uint32_t b1 = __builtin_bit_cast(uint32_t, f[2 * i + 1]);
-                b0 = (b0 + 0x7FFFu + ((b0 >> 16) & 1u)) >> 16;
-                b1 = (b1 + 0x7FFFu + ((b1 >> 16) & 1u)) >> 16;
-                h[i] = b0 | (b1 << 16);
-            }
-            u32x4* o = (u32x4*)(out_bf16 + m * K + 16 * c);
-            o[0] = u32x4{h[0], h[1], h[2], h[3]};
-            o[1] = u32x4{h[4], h[5], h[6], h[7]};
-        }
+        embed_chunk(e, ids[m], m, c);
     }
 }
 
@@ -512,8 +534,17 @@ hipError_t launch_fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t
     const int64_t items = M * (K / 16);
     int64_t grid = (items + 255) / 256;
     grid = grid < 1 ? 1 : (grid > 65536 ? 65536 : grid);
-    fv5b_embed_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(W, S, V, K, ids, M, out, out_bf16);
+    fv5b_embed_kernel<<<dim3((unsigned)grid), dim3(256), 0, stream>>>(EmbedRows{W, S, V, K, out, out_bf16}, ids, M);
     return hipGetLastError();
+}
+
+hipError_t launch_fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                         int64_t M, float* y, int32_t* idx, float* val, void* ws, const int8_t* E,
+                                         const float* ES, int64_t Ve, int64_t Ke, float* emb, uint16_t* emb_bf16,
+                                         hipStream_t stream)
+{
+    return launch_head_argmax<false, true>(W, S, V, K, x, nullptr, M, y, idx, val, ws, stream,
+                                           EmbedRows{E, ES, Ve, Ke, emb, emb_bf16});
 }
 
 }  // namespace tern

@@ -49,6 +49,10 @@ hipError_t launch_fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V
                                       hipStream_t stream);
 hipError_t launch_fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M,
                              float* out, uint16_t* out_bf16, hipStream_t stream);
+hipError_t launch_fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                         int64_t M, float* y, int32_t* idx, float* val, void* ws, const int8_t* E,
+                                         const float* ES, int64_t Ve, int64_t Ke, float* emb, uint16_t* emb_bf16,
+                                         hipStream_t stream);
 // ---- GEMV chain (persistent, one workgroup per CU) ----
 // Workspace layout: header at 0, plan entries at kChainPlanOffset, then the
 // hand-off words of every step that feeds a later one (offsets in the plan).

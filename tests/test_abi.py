@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 7
+    assert L.tern_abi_version() == 8
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -180,6 +180,12 @@ def test_fv5b_argument_errors():
     assert e(p, p, 10, 256, None, 4, p, p, None) == E_NULL             # ids
     assert e(p, p, 10, 256, p, 4, None, None, None) == E_NULL          # no output
     assert e(p, p, 10, 256, p, 4, m, None, None) == E_ALIGN            # out 16-byte
+    ae = L.fv5b_head_argmax_embed
+    assert ae(p, p, 100, 256, p, 1, p, p, None, p, p, p, 10, 384, p, None, None) == E_SHAPE   # Ke % 256
+    assert ae(p, p, 100, 256, p, 1, p, p, None, p, p, p, 0, 256, p, None, None) == E_SHAPE    # Ve = 0
+    assert ae(p, p, 100, 256, p, 1, p, p, None, p, None, p, 10, 256, p, None, None) == E_NULL  # E
+    assert ae(p, p, 100, 256, p, 1, p, p, None, p, p, p, 10, 256, None, None, None) == E_NULL  # no output
+    assert ae(p, p, 100, 256, p, 1, p, p, None, p, m, p, 10, 256, p, None, None) == E_ALIGN    # E 16-byte
 
 
 def test_binding_raises_without_library(monkeypatch, tmp_path):

@@ -153,3 +153,39 @@ def test_embed_bit_exact(tw, v, k, m):
     assert np.array_equal(host(b).view(np.uint16), fv5b.embed_bf16(w, s, ids))
     f_only, none = tw.fv5b_embed(dev(w), dev(s), dev(ids), bf16=False)
     assert none is None and np.array_equal(host(f_only), host(f))
+
+
+def test_head_argmax_embed(tw):
+    """Head + argmax + the chosen rows' embeddings in one call.  Each
+    activation row gets a planted winner (a head row aligned with it), so the
+    oracle's argmax is unambiguous; the gathered rows must equal the oracle's
+    embedding of those indices bit for bit, and a table smaller than the
+    winning index gives a zero row."""
+    import torch
+    v, k, m = 20000, 4096, 3
+    rng = np.random.default_rng(77)
+    w, s, x, _, _ = inputs(v, k, m, seed=78)
+    winners = [17, 9001, 19999]
+    xf = synth.bf16_bits_to_f32(x)
+    for r, wi in enumerate(winners):
+        w[wi] = np.clip(np.rint(100.0 * np.sign(xf[r])), -127, 127).astype(np.int8)
+        s[wi] = 0.02
+    y64, _ = fv5b.head_bf16(w, s, x)
+    for r, wi in enumerate(winners):
+        top = np.sort(y64[r])[::-1]
+        assert int(np.argmax(y64[r])) == wi and top[0] - top[1] > 1e-3 * abs(top[0])
+    ve, ke = 30000, 1024
+    e, es = synth.gen_head_blocks(rng, rng, ve, ke)
+    idx, val, emb, embh = tw.fv5b_head_argmax_embed(dev(w), dev(s), dev(x), dev(e), dev(es))
+    assert host(idx).tolist() == winners
+    want = fv5b.embed_f32(e, es, winners)
+    assert np.array_equal(host(emb).view(np.uint32), want.view(np.uint32))
+    assert np.array_equal(host(embh).view(np.uint16), fv5b.round_bf16(want))
+    i2, v2 = tw.fv5b_head_argmax(dev(w), dev(s), dev(x))
+    assert np.array_equal(host(i2), host(idx)) and np.array_equal(host(v2), host(val))
+    # a table of 9001 rows: the first winner has a row, the others do not
+    e_small, es_small = e[:9001].copy(), es[:9001].copy()
+    _, _, emb2, _ = tw.fv5b_head_argmax_embed(dev(w), dev(s), dev(x), dev(e_small), dev(es_small), bf16=False)
+    want2 = fv5b.embed_f32(e_small, es_small, winners)
+    assert np.array_equal(host(emb2).view(np.uint32), want2.view(np.uint32))
+    assert not want2[1:].any()
