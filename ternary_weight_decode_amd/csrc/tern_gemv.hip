@@ -370,6 +370,141 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     }
 }
 
+// Two-phase variant of the one-pass kernel for activations too large for
+// LDS (large K at M >= 5 bf16, or M >= 13 int8): one row tile per
+// workgroup, nw = nkt / 2 waves with two units each, unit i of every wave in
+// half i of K.  Both halves of x are loaded into registers up front (first
+// in the memory queue, as in the one-pass kernel); half 0 is staged and its
+// units computed, then half 1 replaces it in LDS.  Partials are summed in
+// k-tile order (deterministic).  16 MFMA activation rows (any M <= 16).
+template <bool kI8, int XC>
+__global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                           const void* __restrict__ x, const float* __restrict__ s_x,
+                                                           int M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = 4;
+    constexpr int kChunkBytes = kI8 ? 32 : 16;
+    constexpr int kLoadsPerChunk = kChunkBytes / 16;
+    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = nkt / 2
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7), nkt = nb >> 2;
+    const int64_t rt = blockIdx.x;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    const int pk = nw * kTileK;                                      // k per half
+    const int xrow_bytes = kI8 ? pk + 16 : (pk + 8) * 2;             // staged bytes per activation row
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [nkt + 1 spare][NI][64]
+    // chunk indices past the end store to a dummy slot after the partials:
+    // the second half is staged after the first units' partials are written
+    const int dummy = M * xrow_bytes + (nkt + 1) * NI * 64 * 4;
+
+    const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);  // chunks per activation row in memory
+    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
+    u32x4 xv[2][XC][kLoadsPerChunk];
+    int xdst[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int u = threadIdx.x + c * nthreads;
+        const int uc = u < chunks ? u : chunks - 1;
+        const int m = uc / per_row, cc = uc - m * per_row;
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph)
+#pragma unroll
+            for (int h = 0; h < kLoadsPerChunk; ++h)
+                xv[ph][c][h] = xg[((int64_t)m * row_chunks + ph * per_row + cc) * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : dummy;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    PlaneTile t[2];
+    auto load_unit = [&](int i) {
+        const int kt = wave + i * nw;
+        const int64_t wb = tile_word_base(rt, kt, nb);
+        const int64_t sb = tile_scale_base(rt, kt, nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        t[i].sc = ld_nt8(scales + sb + r * 4);
+    };
+    auto stage = [&](int ph) {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            if constexpr (kI8) {
+                const uint32_t Q[8] = {xv[ph][c][0][0], xv[ph][c][0][1], xv[ph][c][0][2], xv[ph][c][0][3],
+                                       xv[ph][c][1][0], xv[ph][c][1][1], xv[ph][c][1][2], xv[ph][c][1][3]};
+                u32x4 o0, o1;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) o0[d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+                for (int d = 4; d < 8; ++d) o1[d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+                *(u32x4*)(smem + xdst[c]) = o0;
+                *(u32x4*)(smem + xdst[c] + 16) = o1;
+            } else {
+                *(u32x4*)(smem + xdst[c]) = xv[ph][c][0];
+            }
+        }
+    };
+    const int mrow = r < M ? r : M - 1;
+    const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
+    // unit i of this wave: k-tile wave + i*nw, at local k-tile `wave` of half i
+    auto compute = [&](int i) {
+        const int kt = wave + i * nw;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kI8) {
+            const int64_t n = rt * kTileRows + r;
+#pragma unroll
+            for (int bq = 0; bq < 4; ++bq) {
+                u32x4 B[2];
+                decode_i8(t[i].nz[bq], t[i].sg[bq], B);
+                const uint8_t* qa = xrow + (wave * 4 + bq) * kBlockK;
+                i32x4 d = {0, 0, 0, 0};
+                d = mfma_i8(*(const u32x4*)(qa), B[0], d);
+                d = mfma_i8(*(const u32x4*)(qa + 16), B[1], d);
+                const float sc = tile_scale(t[i], bq) * (1.0f / 64.0f);   // decoded weights are 64*t
+#pragma unroll
+                for (int q = 0; q < NI; ++q) acc[q] = __builtin_fmaf(sc, (float)d[q], acc[q]);
+                if (acc_dbg != nullptr) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int m = 4 * g + q;
+                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kt * 4 + bq] = d[q] >> 6;
+                    }
+                }
+            }
+        } else {
+            bf16_tile<16>(t[i], (const uint16_t*)xrow + wave * kTileK, 4, acc);
+        }
+#pragma unroll
+        for (int q = 0; q < NI; ++q) red[(kt * NI + q) * 64 + lane] = acc[q];
+    };
+
+    load_unit(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(0);
+    __syncthreads();
+    load_unit(1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __syncthreads();                       // every wave has read half 0
+    stage(1);
+    __syncthreads();
+    compute(1);
+    __syncthreads();
+
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+    for (int e = threadIdx.x; e < NI * 64; e += nthreads) {
+        const int l = e & 63, q = e >> 6;
+        const int m = 4 * (l >> 4) + q, n = l & 15;
+        const int64_t row = rt * kTileRows + n;
+        if (l < lanes_used && m < M && row < N) {
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ int8
 
 template <int MT>
@@ -586,11 +721,55 @@ static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int6
     return oneshot_dispatch<true, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);
 }
 
+// Two-phase configuration (gemv_phased_kernel): one row tile per workgroup,
+// nkt / 2 waves, half of x in LDS at a time; false when it does not apply.
+static bool pick_phased(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
+{
+    if (K % kTileK != 0 || M < 1 || M > 16 || N < 1) return false;
+    const int64_t nkt = K / kTileK;
+    if (nkt % 2 != 0 || nkt / 2 > 16 || nkt < 2) return false;
+    c.R = 1;
+    c.U = 2;
+    c.nw = (int)(nkt / 2);
+    c.grid = (N + 15) / 16;
+    c.rounds = true;
+    const int64_t pk = c.nw * kTileK;
+    const int64_t chunk = i8 ? 32 : 16;
+    const int64_t chunks = M * pk * (i8 ? 1 : 2) / chunk;
+    const int64_t xc = (chunks + 64 * c.nw - 1) / (64 * c.nw);   // M (bf16) or M / 4 (int8)
+    if (xc > (i8 ? 4 : 8)) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+    c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)(nkt + 1) * 4 * 64 * 4 + 32;   // + dummy slot
+    return c.lds <= (size_t)kCuLds;
+}
+
+template <bool kI8>
+static hipError_t launch_phased(const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
+                                int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    OneShot c;
+    if (!pick_phased(N, K, M, kI8, c)) return hipErrorNotSupported;
+#define TERN_PHASED_CASE(XX)                                                                                       if (c.XC == XX) {                                                                                                  if (!oneshot_resident(gemv_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;                           gemv_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(                           packed, N, K, x, s_x, (int)M, y, acc);                                                                     return hipGetLastError();                                                                                  }
+    TERN_PHASED_CASE(1) TERN_PHASED_CASE(2) TERN_PHASED_CASE(4)
+    if constexpr (!kI8) {
+        TERN_PHASED_CASE(8)   // int8 needs M / 4 <= 4 chunks per thread
+    }
+#undef TERN_PHASED_CASE
+    return hipErrorNotSupported;
+}
+
+bool gemv_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
+{
+    return pick_phased(N, K, M, i8, c);
+}
+
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
     {
-        const hipError_t e = launch_oneshot(false, packed, N, K, x, nullptr, M, y, nullptr, stream);
+        hipError_t e = launch_oneshot(false, packed, N, K, x, nullptr, M, y, nullptr, stream);
+        if (e != hipErrorNotSupported) return e;
+        e = launch_phased<false>(packed, N, K, x, nullptr, M, y, nullptr, stream);
         if (e != hipErrorNotSupported) return e;
     }
     const int64_t nkt = (K / kBlockK + 3) / 4;
@@ -621,7 +800,9 @@ hipError_t launch_gemv_i8(const uint8_t* packed, int64_t N, int64_t K, const int
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     {
-        const hipError_t e = launch_oneshot(true, packed, N, K, q, s_x, M, y, acc, stream);
+        hipError_t e = launch_oneshot(true, packed, N, K, q, s_x, M, y, acc, stream);
+        if (e != hipErrorNotSupported) return e;
+        e = launch_phased<true>(packed, N, K, q, s_x, M, y, acc, stream);
         if (e != hipErrorNotSupported) return e;
     }
     const int64_t nkt = (K / kBlockK + 3) / 4;

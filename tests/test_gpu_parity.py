@@ -371,3 +371,32 @@ def test_gemv_multi_round_grid(tw, m):
     acc_o, yi64, _ = oracle.tern_i8(packed_rows, len(rows), k, q, sx)
     assert np.array_equal(host(acc)[:, rows], acc_o)
     assert oracle.rel_l2(yi[:, rows], yi64) <= TOL
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 12288, 6), (4096, 12288, 8), (1005, 12288, 7), (300, 16384, 6)])
+def test_gemv_bf16_two_phase(tw, n, k, m):
+    """bf16 activations too large for LDS (large K, M >= 6): x staged half
+    of K at a time; every output against the oracle."""
+    assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased")
+    t, s, x = gen(n, k, m, seed=n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
+@pytest.mark.parametrize("n,k,m", [(4096, 12288, 13), (1005, 12288, 16)])
+def test_gemv_i8_two_phase(tw, n, k, m):
+    """int8 activations too large for LDS (M >= 13 at K = 12288): block
+    accumulators bit for bit, y within tolerance."""
+    import torch
+    assert tw.tern_gemv_config(n, k, m, "ternary_int8") is None
+    assert tw.tern_gemv_config(n, k, m, "ternary_int8_phased")
+    t, s, x = gen(n, k, m, seed=2 * n + m)
+    q, sx = oracle.quantize_i8(x)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemv_i8(gpu_pack(tw, t, s), n, k, dev(q), dev(sx), acc=acc))
+    acc_o, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q, sx)
+    assert np.array_equal(host(acc), acc_o)
+    assert oracle.rel_l2(y, y64) <= TOL
