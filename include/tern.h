@@ -349,9 +349,10 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
 /* ---- launch-configuration introspection (no operation of the method) ----
  *
  * The one-pass GEMV configuration that tern_gemv (kind 0), tern_gemv_i8 (1),
- * tern5_gemv (2) or tern5_gemv_i8 (3) takes for this shape, or (kinds 4 and
- * 5) the two-phase configuration tern_gemv / tern_gemv_i8 take when no
- * one-pass one fits (activations staged in LDS one half of K at a time),
+ * tern5_gemv (2) or tern5_gemv_i8 (3) takes for this shape, or the two-phase
+ * configuration that tern_gemv / tern_gemv_i8 (kinds 4 and 5) or tern5_gemv /
+ * tern5_gemv_i8 (6 and 7) take when no one-pass one fits (activations staged
+ * in LDS one half of K at a time),
  * computed on the host exactly as the launchers do (the CU count is the current device's, or
  * 256 without one; the launchers also confirm residency with the occupancy
  * query).  Returns 1 and fills out[8] = {row tiles per workgroup R, waves per
@@ -359,7 +360,7 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * dynamic LDS bytes, runs in several rounds (0/1), MFMA activation rows of the
  * kernel instance}; 0 when another kernel takes the shape; -TERN_E_NULL or
  * -TERN_E_SHAPE for a NULL out or a shape outside 1 <= M <= TERN_MAX_M_GEMV,
- * N, K >= 1, kind 0..5.  Touches no device memory. */
+ * N, K >= 1, kind 0..7.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
 
 #ifdef __cplusplus

@@ -474,7 +474,7 @@ def fv5b_embed(w, s, ids, f32=True, bf16=True, out=None, out_bf16=None, stream=N
 
 
 GEMV_KINDS = {"ternary_bf16": 0, "ternary_int8": 1, "fv5_bf16": 2, "fv5_int8": 3,
-              "ternary_bf16_phased": 4, "ternary_int8_phased": 5}
+              "ternary_bf16_phased": 4, "ternary_int8_phased": 5, "fv5_bf16_phased": 6, "fv5_int8_phased": 7}
 
 
 def tern_gemv_config(n: int, k: int, m: int, kind: str = "ternary_bf16"):

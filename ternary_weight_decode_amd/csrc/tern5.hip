@@ -293,6 +293,108 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     }
 }
 
+// Two-phase variant for activations larger than LDS (large K at bf16
+// M >= 6, int8 M >= 13): one row tile per workgroup, nkt / 2 waves with two
+// units each, unit i of every wave in half i of K; both halves of x loaded
+// into registers up front, staged one half at a time (as the ternary
+// two-phase kernel).  16 MFMA activation rows.
+template <bool kI8, int XC>
+__global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                            const void* __restrict__ x, const float* __restrict__ s_x,
+                                                            int M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = 4;
+    constexpr int kChunkBytes = kI8 ? 32 : 16;
+    constexpr int kLoadsPerChunk = kChunkBytes / 16;
+    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = nkt / 2
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nkt = (int)(K >> 9);
+    const int64_t rt = blockIdx.x;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint32_t* scales = (const TERN_GLOBAL uint32_t*)(packed + t5_plane_bytes(N, K));
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    const int pk = nw * kTileK;                                      // k per half
+    const int xrow_bytes = kI8 ? pk + 16 : (pk + 8) * 2;
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [nkt][NI][64]
+    // chunk indices past the end store to a slot after the partials (the
+    // second half is staged after the first units' partials are written)
+    const int dummy = M * xrow_bytes + nkt * NI * 64 * 4;
+
+    const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);
+    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
+    u32x4 xv[2][XC][kLoadsPerChunk];
+    int xdst[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int u = threadIdx.x + c * nthreads;
+        const int uc = u < chunks ? u : chunks - 1;
+        const int m = uc / per_row, cc = uc - m * per_row;
+#pragma unroll
+        for (int ph = 0; ph < 2; ++ph)
+#pragma unroll
+            for (int h = 0; h < kLoadsPerChunk; ++h)
+                xv[ph][c][h] = xg[((int64_t)m * row_chunks + ph * per_row + cc) * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : dummy;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    Tile5 t[2];
+    auto stage = [&](int ph) {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            if constexpr (kI8) {
+                u32x4 o0, o1;
+                q_decoded_order(xv[ph][c][0], xv[ph][c][kLoadsPerChunk - 1], o0, o1);
+                *(u32x4*)(smem + xdst[c]) = o0;
+                *(u32x4*)(smem + xdst[c] + 16) = o1;
+            } else {
+                *(u32x4*)(smem + xdst[c]) = xv[ph][c][0];
+            }
+        }
+    };
+    const int mrow = r < M ? r : M - 1;
+    const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
+    auto compute = [&](int i) {
+        const int kt = wave + i * nw;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (kI8) {
+            const uint8_t* qt = xrow + wave * kTileK;
+            tile5_i8<16>(t[i], [&](int jj, int h) { return *(const u32x4*)(qt + kBlockK * jj + 16 * h); }, acc,
+                         acc_dbg, N, M, rt * kTileRows + r, (int)(K >> 8), 2 * kt, g);
+        } else {
+            tile5_bf16<16>(t[i], (const uint16_t*)xrow + wave * kTileK, acc);
+        }
+#pragma unroll
+        for (int q = 0; q < NI; ++q) red[(kt * NI + q) * 64 + lane] = acc[q];
+    };
+
+    t[0] = load_tile5(words, scales, rt, wave, nkt, r, g);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(0);
+    __syncthreads();
+    t[1] = load_tile5(words, scales, rt, wave + nw, nkt, r, g);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __syncthreads();                       // every wave has read half 0
+    stage(1);
+    __syncthreads();
+    compute(1);
+    __syncthreads();
+
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+    for (int e = threadIdx.x; e < NI * 64; e += nthreads) {
+        const int l = e & 63, q = e >> 6;
+        const int m = 4 * (l >> 4) + q, n = l & 15;
+        const int64_t row = rt * kTileRows + n;
+        if (l < lanes_used && m < M && row < N) {
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
+        }
+    }
+}
+
 // Any shape: one workgroup per row tile, its waves split the k-tiles
 // round-robin, activations read from global memory (cached; int8 q is put
 // in the decoded byte order in registers), partials summed in LDS in wave
@@ -395,6 +497,47 @@ bool gemv5_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
     return pick_oneshot(N, K, M, s, c);
 }
 
+// two-phase configuration (gemv5_phased_kernel); false when it does not apply
+bool gemv5_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
+{
+    if (K % kTileK != 0 || M < 1 || M > 16 || N < 1) return false;
+    const int64_t nkt = K / kTileK;
+    if (nkt % 2 != 0 || nkt / 2 > 16 || nkt < 2) return false;
+    c.R = 1;
+    c.U = 2;
+    c.nw = (int)(nkt / 2);
+    c.grid = (N + 15) / 16;
+    c.rounds = true;
+    const int64_t pk = c.nw * kTileK;
+    const int64_t chunks = M * pk * (i8 ? 1 : 2) / (i8 ? 32 : 16);
+    const int64_t xc = (chunks + 64 * c.nw - 1) / (64 * c.nw);   // M (bf16) or M / 4 (int8)
+    if (xc > (i8 ? 4 : 8)) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+    c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)nkt * 4 * 64 * 4 + 32;   // + dummy slot
+    return c.lds <= (size_t)kCuLds;
+}
+
+template <bool kI8>
+static hipError_t launch_gemv5_phased(const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
+                                      int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    OneShot c;
+    if (!gemv5_phased_config(N, K, M, kI8, c)) return hipErrorNotSupported;
+#define TERN5_PHASED_CASE(XX)                                                                                  \
+    if (c.XC == XX) {                                                                                          \
+        if (!oneshot_resident(gemv5_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;                  \
+        gemv5_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(              \
+            packed, N, K, x, s_x, (int)M, y, acc);                                                             \
+        return hipGetLastError();                                                                              \
+    }
+    TERN5_PHASED_CASE(1) TERN5_PHASED_CASE(2) TERN5_PHASED_CASE(4)
+    if constexpr (!kI8) {
+        TERN5_PHASED_CASE(8)
+    }
+#undef TERN5_PHASED_CASE
+    return hipErrorNotSupported;
+}
+
 template <bool kI8>
 static hipError_t launch_gemv5(const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
                                int64_t M, float* y, int32_t* acc, hipStream_t stream)
@@ -409,6 +552,10 @@ static hipError_t launch_gemv5(const uint8_t* packed, int64_t N, int64_t K, cons
         else if (M == 1) e = gemv5_oneshot_dispatch<kI8, 1>(c, stream, packed, N, K, x, s_x, m, y, acc);
         else if (M == 2) e = gemv5_oneshot_dispatch<kI8, 2>(c, stream, packed, N, K, x, s_x, m, y, acc);
         else e = gemv5_oneshot_dispatch<kI8, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        if (e != hipErrorNotSupported) return e;
+    }
+    {
+        const hipError_t e = launch_gemv5_phased<kI8>(packed, N, K, x, s_x, M, y, acc, stream);
         if (e != hipErrorNotSupported) return e;
     }
     const int64_t nkt = K / kTileK;

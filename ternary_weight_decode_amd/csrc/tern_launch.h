@@ -27,6 +27,7 @@ hipError_t launch_gemv_i8(const uint8_t* packed, int64_t N, int64_t K, const int
 bool gemv_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c);
 bool gemv5_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c);
 bool gemv_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c);
+bool gemv5_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c);
 hipError_t launch_head_bf16(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x, int64_t M,
                             float* y, hipStream_t stream);
 hipError_t launch_head_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,

@@ -109,6 +109,19 @@ def test_gemv5_general_path(tw, n, k, m):
     assert rel_l2(y, want) < TOL
 
 
+@pytest.mark.parametrize("n,k,m", [(37, 12288, 6), (300, 12288, 8), (100, 16384, 5), (17, 16384, 4)])
+def test_gemv5_two_phase(tw, n, k, m):
+    """bf16 activations larger than LDS but half of them not: the two-phase
+    kernel (K staged one half at a time); ragged row tiles included."""
+    assert tw.tern_gemv_config(n, k, m, "fv5_bf16_phased") is not None
+    lv, lo, hi, x = gen(n, k, m, seed=7 * n + m)
+    y = host(tw.tern5_gemv(gpu_pack(tw, lv, lo, hi), n, k, dev(x)))
+    want, _ = fv5.gemv_bf16_levels(lv, lo, hi, x)
+    assert rel_l2(y, want) < TOL
+    err = np.abs(y - want).max(axis=0) / (np.abs(want).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 def test_gemv5_deterministic_and_stream_order(tw):
     import torch
     n, k, m = 6144, 4096, 1
@@ -129,7 +142,7 @@ FULL = [(6144, 4096), (4096, 4096), (24576, 4096), (4096, 12288)]
 
 
 @pytest.mark.parametrize("n,k", FULL)
-@pytest.mark.parametrize("m", [1, 16])
+@pytest.mark.parametrize("m", [1, 8, 16])
 def test_gemv5_full_size_sampled_rows(tw, n, k, m):
     lv, lo, hi, x = gen(n, k, m, seed=n + k + m)
     y = host(tw.tern5_gemv(gpu_pack(tw, lv, lo, hi), n, k, dev(x)))
@@ -209,6 +222,32 @@ def test_gemv5_i8_full_size_sampled_rows(tw, n, k, m):
     y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx)))
     rng = np.random.default_rng(n + 1)
     rows = np.unique(np.concatenate([rng.choice(n, 48, replace=False), [0, 15, 16, n - 1]]))
+    _, want, _ = fv5.gemv_i8_levels(lv[rows], lo[rows], hi[rows], q, sx)
+    assert rel_l2(y[:, rows], want) < TOL
+
+
+@pytest.mark.parametrize("n,k,m", [(37, 12288, 13), (100, 12288, 16), (40, 16384, 14)])
+def test_gemv5_i8_two_phase_block_sums_exact(tw, n, k, m):
+    """int8 activations larger than LDS: the two-phase kernel; per-block sums
+    of each magnitude bit exact."""
+    import torch
+    assert tw.tern_gemv_config(n, k, m, "fv5_int8_phased") is not None
+    lv, lo, hi, _ = gen(n, k, 1, seed=9 * n + m)
+    q, sx = gen_q(m, k, seed=n + 3 * m)
+    acc = torch.empty((m, n, k // 256, 2), dtype=torch.int32, device="cuda")
+    y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx), acc=acc))
+    acc64, y64, _ = fv5.gemv_i8_levels(lv, lo, hi, q, sx)
+    assert np.array_equal(host(acc).astype(np.int64), acc64)
+    assert rel_l2(y, y64) < TOL
+
+
+@pytest.mark.parametrize("m", [13, 16])
+def test_gemv5_i8_down_full_size_two_phase(tw, m):
+    n, k = 4096, 12288
+    lv, lo, hi, _ = gen(n, k, 1, seed=m)
+    q, sx = gen_q(m, k, seed=m + 1)
+    y = host(tw.tern5_gemv_i8(gpu_pack(tw, lv, lo, hi), n, k, dev(q), dev(sx)))
+    rows = np.unique(np.concatenate([np.random.default_rng(m).choice(n, 48, replace=False), [0, 15, n - 1]]))
     _, want, _ = fv5.gemv_i8_levels(lv[rows], lo[rows], hi[rows], q, sx)
     assert rel_l2(y[:, rows], want) < TOL
 

@@ -52,16 +52,17 @@ def test_picker_invariants(kind):
     assert taken > 100
 
 
-@pytest.mark.parametrize("kind", ["ternary_bf16_phased", "ternary_int8_phased"])
+@pytest.mark.parametrize("kind", ["ternary_bf16_phased", "ternary_int8_phased", "fv5_bf16_phased",
+                                  "fv5_int8_phased"])
 def test_phased_picker_invariants(kind):
     """The two-phase configuration: taken only where no one-pass one fits; one
     row tile per workgroup, nkt / 2 waves with two units each (unit i in half
     i of K), half of the activations staged at a time."""
-    i8 = kind.startswith("ternary_int8")
+    i8 = "int8" in kind
     taken = 0
     for n, k, m in itertools.product(NS, KS, MS):
         c = tw.tern_gemv_config(n, k, m, kind)
-        one = tw.tern_gemv_config(n, k, m, "ternary_int8" if i8 else "ternary_bf16")
+        one = tw.tern_gemv_config(n, k, m, kind[:-len("_phased")])
         if c is None:
             continue
         taken += 1
@@ -72,15 +73,20 @@ def test_phased_picker_invariants(kind):
         assert c["grid"] == (n + 15) // 16 and c["MT"] == 16, where
         pk = c["waves"] * 512
         xrow = pk + 16 if i8 else (pk + 8) * 2
-        assert c["lds"] == m * xrow + (nkt + 1) * 4 * 64 * 4 + 32 <= CU_LDS, where   # + a dummy staging slot
+        slots = nkt + 1 if kind.startswith("ternary") else nkt         # partials (+ a spare in the ternary kernel)
+        assert c["lds"] == m * xrow + slots * 4 * 64 * 4 + 32 <= CU_LDS, where   # + a dummy staging slot
         chunk = 32 if i8 else 16
         assert c["XC"] * 64 * c["waves"] * chunk >= m * pk * (1 if i8 else 2), where   # a half fully staged
         assert c["XC"] <= (4 if i8 else 8), where
     assert taken > 0
-    # the shape it exists for: bf16 down (4096 x 12288) at M = 7 and 8
+    # the shapes it exists for: down (4096 x 12288) at bf16 M = 7 and 8 and, five-level, int8 M = 16
+    fam = kind.split("_")[0]
     for m in (7, 8):
-        c = tw.tern_gemv_config(4096, 12288, m, "ternary_bf16_phased")
+        c = tw.tern_gemv_config(4096, 12288, m, fam + "_bf16_phased")
         assert c is not None and c["waves"] == 12 and c["XC"] == 8   # M chunks per thread, rounded up to 8
+    if fam == "fv5":
+        c = tw.tern_gemv_config(4096, 12288, 16, "fv5_int8_phased")
+        assert c is not None and c["waves"] == 12 and c["XC"] == 4
 
 
 def test_picker_8b_decode_shapes():
@@ -109,5 +115,5 @@ def test_picker_argument_errors():
     out = (ctypes.c_int64 * 8)()
     assert L.tern_gemv_config(16, 512, 1, 0, None) == -1
     assert L.tern_gemv_config(16, 512, 17, 0, out) == -2
-    assert L.tern_gemv_config(16, 512, 1, 6, out) == -2
+    assert L.tern_gemv_config(16, 512, 1, 8, out) == -2
     assert L.tern_gemv_config(0, 512, 1, 0, out) == -2
