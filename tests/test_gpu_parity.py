@@ -316,6 +316,46 @@ def test_prefill_full_shape_sampled(tw, proj, m):
     assert oracle.rel_l2(y[m - 12:m - 4], y8) <= TOL
 
 
+@pytest.mark.parametrize("n,k,m", [(40, 512, 128), (256, 1536, 130), (300, 2048, 300), (1000, 4096, 257),
+                                   (17, 2560, 640)])
+def test_prefill_no_debug_matches_oracle(tw, n, k, m):
+    """The kernel instance without the debug accumulators (the one the
+    benchmark times): several workgroup tiles, ragged in M and N, against the
+    fp64 oracle, and bit for bit the same y as the instance that also writes
+    the block sums."""
+    import torch
+    t, s, x = gen(n, k, m, seed=3 * n + m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
+    _, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0, want_acc=False)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    yi = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    assert np.array_equal(y, yi)
+
+
+def test_prefill_exact_on_power_of_two_scales(tw):
+    """Block scales from {1/4, 1/2, 1, 2}: every scaled block sum and every
+    partial sum of the fold is a multiple of 1/4 below 2^22, so fp32 holds it
+    exactly and y must equal fl32(s_x * sum_b scale_b * acc_b) bit for bit,
+    with acc the oracle's exact block sums."""
+    n, k, m = 300, 4096, 200
+    rng = np.random.default_rng(8)
+    t = synth.gen_ternary(rng, n, k)
+    s = rng.choice(np.array([0.25, 0.5, 1.0, 2.0], np.float16), size=(n, k // 128)).view(np.uint16)
+    q0 = rng.integers(-127, 128, size=(m, k)).astype(np.int8)
+    s0 = rng.uniform(0.001, 0.01, m).astype(np.float32)
+    y = host(tw.tern_gemm_prefill(gpu_pack(tw, t, s), n, k, dev(q0), dev(s0)))
+    acc0, _, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    exact = (acc0.astype(np.float64) * s.view(np.float16).astype(np.float64)[None]).sum(axis=2)
+    assert np.abs(exact).max() < 2 ** 22 and np.array_equal(exact, exact.astype(np.float32).astype(np.float64))
+    want = s0[:, None] * exact.astype(np.float32)
+    assert np.array_equal(y, want)
+
+
 def test_prefill_large_tiles_exact(tw):
     """A shape that takes the 256 x 128 workgroup tiles (M >= 1024), ragged
     in M: int32 block accumulators bit for bit."""
