@@ -456,6 +456,27 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
         if (M >= 1024) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
         return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
     }
+    // Below M = 128 the prefill kernel's time is set by its per-block latency
+    // (about 0.62 us per 128-k block on the 8B shapes, nearly independent of
+    // M and N), while the int8 GEMV reads the weights once per 16 activation
+    // rows (about 4 us of fixed time plus the weight bytes at 5.3 TB/s per
+    // launch).  Take the cheaper by that measured model: 8B down at M = 64
+    // 61 us -> 31 us in four GEMV launches; 8B gate at M = 16/32/48 23-24 us
+    // -> 7/13/19 us, at M = 64 a tie (the prefill kernel stays).
+    {
+        const double pf_us = 0.62 * (double)(K / kBlockK);
+        const double gemv_us = 4.0 + (double)N * (double)K * (0.265625 / 5.3e6);
+        const int64_t chunks = (M + 15) / 16;
+        if ((double)chunks * gemv_us < pf_us) {
+            for (int64_t m0 = 0; m0 < M; m0 += 16) {
+                const int64_t mc = M - m0 < 16 ? M - m0 : 16;
+                const hipError_t e = launch_gemv_i8(packed, N, K, q + m0 * K, s_x + m0, mc, y + m0 * N,
+                                                    acc ? acc + m0 * N * (K / kBlockK) : nullptr, stream);
+                if (e != hipSuccess) return e;
+            }
+            return hipSuccess;
+        }
+    }
     // wave tile 64 (m) x 16 (n), two workgroups per CU: measured best among the
     // tile shapes that fit 256 VGPRs without spills (8B gate, M = 2048: 259 us vs
     // 355-398 us for 32x32 and 64x16 at two waves per workgroup)

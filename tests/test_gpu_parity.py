@@ -356,6 +356,36 @@ def test_prefill_exact_on_power_of_two_scales(tw):
     assert np.array_equal(y, want)
 
 
+@pytest.mark.parametrize("n,k,m", [(300, 8192, 64), (100, 4096, 37), (37, 12288, 17)])
+def test_prefill_small_m_through_gemv_slices(tw, n, k, m):
+    """Below M = 128 with many 128-k blocks the call runs the int8 GEMV on
+    16-row slices of q (ragged last slice): block sums bit for bit, y against
+    the oracle."""
+    import torch
+    t, s, x = gen(n, k, m, seed=n + 7 * m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
+    y2 = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
+    assert oracle.rel_l2(y2, y64) <= TOL
+
+
+def test_prefill_down_m64_sampled(tw):
+    """The 8B down shape at M = 64 (four GEMV slices): sampled rows."""
+    n, k = synth.SHAPES_8B["down"]
+    m = 64
+    t, s, x = gen(n, k, m, seed=64)
+    q0, s0 = oracle.quantize_i8(x)
+    y = host(tw.tern_gemm_prefill(gpu_pack(tw, t, s), n, k, dev(q0), dev(s0)))
+    rows = np.random.default_rng(5).choice(n, 64, replace=False)
+    _, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0, rows=rows, want_acc=False)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+
+
 def test_prefill_large_tiles_exact(tw):
     """A shape that takes the 256 x 128 workgroup tiles (M >= 1024), ragged
     in M: int32 block accumulators bit for bit."""
