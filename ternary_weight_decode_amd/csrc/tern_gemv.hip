@@ -749,7 +749,13 @@ static hipError_t launch_phased(const uint8_t* packed, int64_t N, int64_t K, con
 {
     OneShot c;
     if (!pick_phased(N, K, M, kI8, c)) return hipErrorNotSupported;
-#define TERN_PHASED_CASE(XX)                                                                                       if (c.XC == XX) {                                                                                                  if (!oneshot_resident(gemv_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;                           gemv_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(                           packed, N, K, x, s_x, (int)M, y, acc);                                                                     return hipGetLastError();                                                                                  }
+#define TERN_PHASED_CASE(XX)                                                                      \
+    if (c.XC == XX) {                                                                             \
+        if (!oneshot_resident(gemv_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;       \
+        gemv_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(  \
+            packed, N, K, x, s_x, (int)M, y, acc);                                                \
+        return hipGetLastError();                                                                 \
+    }
     TERN_PHASED_CASE(1) TERN_PHASED_CASE(2) TERN_PHASED_CASE(4)
     if constexpr (!kI8) {
         TERN_PHASED_CASE(8)   // int8 needs M / 4 <= 4 chunks per thread
