@@ -789,6 +789,18 @@ hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const u
         if (M <= 4) return launch_fast_mt<4>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
         return launch_fast_mt<16>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
     }
+    // More than 8 activation rows that fit none of the kernels above: two
+    // calls on row halves take the one-pass or two-phase kernels, which read
+    // the weights twice but finish sooner than the k-chunked kernel (8B down
+    // at M = 16: 20.9 us as one k-chunked launch, 2 x 7.5 us as two).
+    if (M > 8 && K % kTileK == 0) {
+        OneShot c;
+        if (gemv_oneshot_config(N, K, 8, false, c) || gemv_phased_config(N, K, 8, false, c)) {
+            const hipError_t e = launch_gemv_bf16(packed, N, K, x, 8, y, stream);
+            if (e != hipSuccess) return e;
+            return launch_gemv_bf16(packed, N, K, x + 8 * K, M - 8, y + 8 * N, stream);
+        }
+    }
     // general path: activations staged in k-chunks
     const dim3 grid((unsigned)((N + 15) / 16));
     const int nwc = pick_waves(nkt);

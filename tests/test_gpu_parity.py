@@ -456,6 +456,21 @@ def test_gemv_bf16_two_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12)])
+def test_gemv_bf16_row_halves(tw, n, k, m):
+    """bf16 activations of more than 8 rows that fit no one-pass or
+    two-phase configuration: the call runs on rows 0..7 and 8..M-1 through
+    those kernels; every output against the oracle."""
+    assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased") is None
+    assert tw.tern_gemv_config(n, k, 8, "ternary_bf16_phased") is not None
+    t, s, x = gen(n, k, m, seed=2 * n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 @pytest.mark.parametrize("n,k,m", [(4096, 12288, 13), (1005, 12288, 16)])
 def test_gemv_i8_two_phase(tw, n, k, m):
     """int8 activations too large for LDS (M >= 13 at K = 12288): block
