@@ -119,7 +119,9 @@ int tern_quantize_i8(const uint16_t* x, int64_t M, int64_t K, int8_t* q, float* 
  *   x       bf16 bits [M][K], 1 <= M <= TERN_MAX_M_GEMV
  *   y       fp32 [M][N]
  * Accuracy: fp32 accumulation; relative L2 error against the exact value is
- * ~1e-7 (any summation order). */
+ * ~1e-7 (any summation order).  A call may enqueue more than one kernel (more
+ * than 8 activation rows whose activations fit no one-pass or two-phase
+ * split run as two calls on row halves); every kernel goes to `stream`. */
 int tern_gemv(const void* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y, void* stream);
 
 /* Ternary GEMV / small-M GEMM with int8 activations (q, s_x from
