@@ -139,15 +139,16 @@ int tern_gemv_i8(const void* packed, int64_t N, int64_t K, const int8_t* q, cons
  * the unembedding runs on the DRAM roofline, [P2] section "뉴트리노 엔진:
  * 토큰 하나의 시간은 어디로 가는가"):
  *   logits[m][v] = row_scale[v] * sum_k W[v][k] * x[m][k]
- *   W  int8 [V][K] (K % 16 == 0);  row_scale fp32 [V];  x bf16 bits [M][K];
- *   logits fp32 [M][V];  1 <= M <= TERN_MAX_M_GEMV. */
+ *   W  int8 [V][K] (K % 128 == 0, else TERN_E_SHAPE);  row_scale fp32 [V];
+ *   x bf16 bits [M][K];  logits fp32 [M][V];  1 <= M <= TERN_MAX_M_GEMV. */
 int i8_head_gemv(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x, int64_t M,
                  float* logits, void* stream);
 
 /* int8 output head with int8 activations:
  *   acc[m][v] = sum_k W[v][k] * q[m][k] (exact int32),
  *   logits[m][v] = row_scale[v] * s_x[m] * acc[m][v]
- *   acc_dbg NULL or int32 [M][V]. */
+ *   W int8 [V][K] (K % 128 == 0, else TERN_E_SHAPE);  q int8 [M][K];
+ *   s_x fp32 [M];  acc_dbg NULL or int32 [M][V]. */
 int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
                     const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
 

@@ -57,7 +57,8 @@ def test_shape_errors_before_any_device_call():
     assert L.tern_gemv(p, 16, 128, p, 17, p, s) == E_SHAPE         # M > 16
     assert L.tern_gemv(p, 16, 128, p, -1, p, s) == E_SHAPE
     assert L.tern_gemv_i8(p, 16, 128, p, p, 17, p, None, s) == E_SHAPE
-    assert L.i8_head_gemv(p, p, 100, 96, p, 1, p, s) == E_SHAPE
+    assert L.i8_head_gemv(p, p, 100, 96, p, 1, p, s) == E_SHAPE            # K % 128 (as tern.h states)
+    assert L.i8_head_gemv_i8(p, p, 100, 96, p, p, 1, p, None, s) == E_SHAPE   # K % 128
     assert L.i8_head_gemv_i8(p, p, 100, 128, p, p, 20, p, None, s) == E_SHAPE
     assert L.tern_gemm_prefill(p, 16, 200, p, p, 64, p, None, s) == E_SHAPE
     assert L.tern_gemm_prefill(p, 16, 128, p, p, -5, p, None, s) == E_SHAPE

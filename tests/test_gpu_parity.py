@@ -133,7 +133,7 @@ def test_gemv_i8_one_pass_configs(tw, n, k, m):
     q0, s0 = oracle.quantize_i8(x)
     p = gpu_pack(tw, t, s)
     full = n * k * m <= 64 * 1024 * 1024
-    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda") if full else None
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
     y = host(tw.tern_gemv_i8(p, n, k, dev(q0), dev(s0), acc=acc))
     assert y.shape == (m, n) and np.isfinite(y).all()
     if full:
@@ -144,7 +144,11 @@ def test_gemv_i8_one_pass_configs(tw, n, k, m):
         rng = np.random.default_rng(n)
         rows = np.unique(np.concatenate([rng.choice(n, 300, replace=False), np.arange(n - 48, n)]))
         acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+        # the block sums of the sampled rows bit for bit (the one-pass int8
+        # kernel on the 8B down shape at M = 8 and on 24576 x 4096 at M = 2)
+        assert np.array_equal(host(acc)[:, rows], acc0)
         assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    # the instance without the debug accumulators (the production one) gives the same bytes
     assert np.array_equal(y, host(tw.tern_gemv_i8(p, n, k, dev(q0), dev(s0))))
 
 
@@ -398,6 +402,70 @@ def test_prefill_large_tiles_exact(tw):
     acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
     assert np.array_equal(host(acc), acc0)
     assert oracle.rel_l2(y, y64) <= TOL
+
+
+def test_stats_noncanonical_hand_built(tw):
+    """tern_stats on the hand-derived blob of tests/golden/stats_noncanonical.txt
+    (three non-canonical sign bits in real rows, eight in a padding row that
+    must not count), and the bf16 GEMV on it: non-canonical bits decode to 0."""
+    from test_oracle import read_noncanonical_blob
+    blob, n, k, counts, y_want = read_noncanonical_blob()
+    p = dev(blob)
+    assert host(tw.tern_stats(p, n, k)).astype(np.int64).tolist() == counts == [34, 3, 3]
+    x = synth.f32_to_bf16_bits((np.arange(k) % 7 - 3).astype(np.float32)[None, :])
+    y = host(tw.tern_gemv(p, n, k, dev(x)))
+    assert np.array_equal(y[0], y_want.astype(np.float32))
+
+
+@pytest.mark.parametrize("n,k", [(5, 256), (100, 2560), (3000, 4096)])
+def test_stats_random_bytes(tw, n, k):
+    """tern_stats on blobs of uniformly random bytes (about a quarter of all
+    sign bits non-canonical) against the oracle's bit-by-bit count."""
+    blob = np.random.default_rng(n + k).integers(0, 256, size=oracle.packed_bytes(n, k), dtype=np.uint8)
+    c = host(tw.tern_stats(dev(blob), n, k)).astype(np.int64).tolist()
+    want = oracle.stats(blob, n, k).astype(np.int64).tolist()
+    assert c == want and want[2] > 0
+
+
+FUSED_06B = {"qkv": (4096, 1024), "gateup": (6144, 1024)}
+
+
+@pytest.mark.parametrize("shape", list(synth.SHAPES_06B) + list(FUSED_06B))
+def test_06b_shapes_m1(tw, shape):
+    """Every Qwen3-0.6B linear shape at M = 1 (and the fused q|k|v and
+    gate|up launches of that model) in the benchmark's launch configuration:
+    every output row against the oracle."""
+    n, k = synth.SHAPES_06B[shape] if shape in synth.SHAPES_06B else FUSED_06B[shape]
+    t, s, x = gen(n, k, 1, seed=n + 3 * k)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL, oracle.rel_l2(y, y64)
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max() + 1e-30)
+    assert err.max() < 1e-5
+
+
+@pytest.mark.parametrize("proj", ["gate", "up"])
+def test_prefill_gate_up_m64_sampled(tw, proj):
+    """The 8B gate and up shapes (12288 x 4096) at M = 64, which run the
+    small-M prefill kernel: block sums of sampled output rows bit for bit
+    (all 64 activation rows), y against the oracle on those rows, and the
+    production instance (no debug output) bit for bit the same y."""
+    import torch
+    n, k = synth.SHAPES_8B[proj]
+    m = 64
+    lin = synth.Linear(2, 0, proj, n, k, synth.P_ZERO, synth.P_PLUS)
+    t, s, _ = synth.linear_inputs(lin)
+    x = synth.gen_x_bf16(np.random.default_rng(640 + len(proj)), m, k)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    rng = np.random.default_rng(3)
+    rows = np.unique(np.concatenate([rng.choice(n, 96, replace=False), np.arange(n - 16, n), [0]]))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+    assert np.array_equal(host(acc)[:, rows], acc0)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
 
 
 @pytest.mark.parametrize("proj", list(synth.PROJ))

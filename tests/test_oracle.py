@@ -318,3 +318,53 @@ def test_generator_statistics():
     assert s.min() >= 0.0099 and s.max() <= 0.0501
     assert synth.f32_to_bf16_bits(np.array([1.00390625], np.float32))[0] == 0x3F80   # tie -> even
     assert synth.f32_to_bf16_bits(np.array([1.01171875], np.float32))[0] == 0x3F82   # tie -> even (up)
+
+
+NONCANON = os.path.join(os.path.dirname(__file__), "golden", "stats_noncanonical.txt")
+
+
+def read_noncanonical_blob():
+    """The hand-built blob of tests/golden/stats_noncanonical.txt: (blob uint8,
+    N, K, expected counts, expected y with x[k] = (k mod 7) - 3)."""
+    blob, n, k, counts, ys = None, 0, 0, None, {}
+    for line in open(NONCANON):
+        line = line.split("#", 1)[0].strip()
+        if not line:
+            continue
+        tok = line.split()
+        if tok[0] == "blob":
+            n, k = int(tok[2]), int(tok[4])
+            blob = np.zeros(int(tok[6]), np.uint8)
+        elif tok[0] == "byte":
+            blob[int(tok[1])] = int(tok[2], 16)
+        elif tok[0] == "counts":
+            counts = [int(v) for v in tok[1:4]]
+        elif tok[0] == "y":
+            ys[int(tok[1])] = float(tok[2])
+    y = np.zeros(n)
+    for r, v in ys.items():
+        y[r] = v
+    return blob, n, k, counts, y
+
+
+def test_stats_noncanonical_hand_built():
+    """Counts of nonzero, -1 and non-canonical bits on a hand-derived blob
+    (three non-canonical sign bits in real rows, eight more in a padding row
+    that must not count), and the decoding of that blob: non-canonical bits
+    decode to 0, so unpack and the GEMV see only the canonical weights."""
+    blob, n, k, counts, y_want = read_noncanonical_blob()
+    assert blob.size == oracle.packed_bytes(n, k)
+    assert oracle.stats(blob, n, k).astype(np.int64).tolist() == counts == [34, 3, 3]
+    t, s = oracle.unpack(blob, n, k)
+    want = np.zeros((n, k), np.int8)
+    want[0, [0, 2]] = -1
+    want[4, 224:256] = 1
+    want[4, 225] = -1
+    assert np.array_equal(t, want)
+    x = synth.f32_to_bf16_bits((np.arange(k) % 7 - 3).astype(np.float32)[None, :])
+    y64, _ = oracle.gemv_bf16(blob, n, k, x)
+    assert np.array_equal(y64[0], y_want)
+    # the canonical blob of the same weights and scales has the same output and no bad bits
+    canon = oracle.pack(t, s)
+    assert oracle.stats(canon, n, k).astype(np.int64).tolist() == [34, 3, 0]
+    assert np.array_equal(oracle.gemv_bf16(canon, n, k, x)[0], y64)
