@@ -47,12 +47,16 @@ def parse():
                     help="chain: one persistent tern_gemv_chain launch per step; graph: one launch per linear")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="token mode: skip the config-0 single linear and the 0.6B token-equivalent")
     ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
                     help="--mode prefill: run only this shape and M (e.g. gate:2048)")
-    ap.add_argument("--mode", default="token", choices=["token", "smallm", "prefill", "head", "fv5", "sweep", "copy"],
+    ap.add_argument("--mode", default="token",
+                    choices=["token", "smallm", "prefill", "head", "fv5", "sweep", "copy", "peak"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
-                         "copy: plain 256 MiB device copies (reference for memory-counter scaling)")
+                         "copy: plain 256 MiB device copies (reference for memory-counter scaling); "
+                         "peak: the matrix-core throughput probe (int8 16x16x64 and bf16 16x16x32)")
     return ap.parse_args()
 
 
@@ -63,11 +67,12 @@ def log(msg):
 class Step:
     """Device-resident inputs of one token-equivalent and the launch list."""
 
-    def __init__(self, tw, synth, config: int, compose: str):
+    def __init__(self, tw, synth, config: int, compose: str, quiet: bool = False):
         import torch
         self.torch = torch
         self.tw = tw
         lins = synth.model_linears(config)
+        log_ = (lambda msg: None) if quiet else log
         self.launches = []          # (kind, packed/W, n, k, x, y, bytes, label)
         t0 = time.time()
 
@@ -98,7 +103,7 @@ class Step:
                 nbytes = tw.tern_packed_bytes(n, k) + 2 * k + 4 * n
                 self.launches.append(("tern", packed, n, k, x_dev, y_dev, nbytes, label))
             if gi % 6 == 5:
-                log(f"generated and packed {gi + 1}/{len(groups)} layers ({time.time() - t0:.1f}s)")
+                log_(f"generated and packed {gi + 1}/{len(groups)} layers ({time.time() - t0:.1f}s)")
         w, rs, xh = synth.head_inputs(config)
         v, k = w.shape
         self.head = (torch.from_numpy(w).cuda(), torch.from_numpy(rs).cuda(),
@@ -108,8 +113,18 @@ class Step:
         self.tern_bytes = sum(l[6] for l in self.launches)
         self.bytes = self.tern_bytes + self.head_bytes
         torch.cuda.synchronize()
-        log(f"inputs resident: {self.bytes / 1e9:.3f} GB algorithmic per step, "
-            f"{len(self.launches)} ternary launches + head ({time.time() - t0:.1f}s)")
+        log_(f"inputs resident: {self.bytes / 1e9:.3f} GB algorithmic per step, "
+             f"{len(self.launches)} ternary launches + head ({time.time() - t0:.1f}s)")
+
+    def clone(self):
+        """A second copy of every device buffer (same values, distinct memory)."""
+        c = object.__new__(Step)
+        c.torch, c.tw = self.torch, self.tw
+        c.launches = [(kind, p.clone(), n, k, x.clone(), y.clone(), b, lab)
+                      for (kind, p, n, k, x, y, b, lab) in self.launches]
+        c.head = tuple(t.clone() for t in self.head)
+        c.head_bytes, c.tern_bytes, c.bytes = self.head_bytes, self.tern_bytes, self.bytes
+        return c
 
     def run_tern(self, label=None):
         tw = self.tw
@@ -160,16 +175,46 @@ def capture(torch, fn):
     return g
 
 
-def time_replays(torch, g, reps: int) -> float:
-    """Mean milliseconds per replay from HIP events on the replay stream."""
+class ProfilerRegion:
+    """roctx profiler resume / pause around a region: under `rocprofv3 --selected-regions`
+    only the launches inside such regions are traced or counted; otherwise these calls do
+    nothing.  The roctx library ships with ROCm; without it the region is a no-op."""
+
+    def __init__(self):
+        import ctypes
+        self.lib = None
+        root = os.environ.get("ROCM_PATH", "/opt/rocm")
+        for name in ("librocprofiler-sdk-roctx.so.1", "librocprofiler-sdk-roctx.so"):
+            try:
+                self.lib = ctypes.CDLL(os.path.join(root, "lib", name))
+                break
+            except OSError:
+                continue
+
+    def resume(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerResume(0)
+
+    def pause(self):
+        if self.lib is not None:
+            self.lib.roctxProfilerPause(0)
+
+
+def time_replays(torch, g, reps: int, region: ProfilerRegion | None = None) -> float:
+    """Mean milliseconds per replay from HIP events on the replay stream.  With a region,
+    exactly the timed replays run inside it."""
     g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    if region is not None:
+        region.resume()
     e0.record()
     for _ in range(reps):
         g.replay()
     e1.record()
     torch.cuda.synchronize()
+    if region is not None:
+        region.pause()
     return e0.elapsed_time(e1) / reps
 
 
@@ -256,28 +301,70 @@ def measured_chain_traffic(root: str, compose: str):
     return int(float(m.group(1)) * 1e6)
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(synth, oracle, target_s: float):
-    """The fp64 oracle's bf16 GEMV over the seven linears of one 8B layer (the
-    same generated inputs as the GPU step's layer 0, packed by the oracle),
-    repeated until target_s of CPU time is spent."""
+    """The fp64 oracle (a correctness reference, not a tuned CPU kernel) on
+    the host cores in this process's affinity mask: its bf16 GEMV over the
+    seven linears of one 8B layer (the same generated inputs as the GPU step's
+    layer 0, packed by the oracle), repeated until target_s of CPU time is
+    spent; per linear the median of 3 timed calls; and the single 3072 x 1024
+    linear of the smallest configuration on one core."""
+    cores = len(os.sched_getaffinity(0))
+    used = oracle.set_threads(cores)
     lins = [l for l in synth.model_linears(2) if l.layer == 0]
     work = []
     for lin in lins:
         t, s, x = synth.linear_inputs(lin)
-        work.append((oracle.pack(t, s), lin.n, lin.k, x))
+        work.append((lin.proj, oracle.pack(t, s), lin.n, lin.k, x))
+    per_linear = {}
     done_bytes, t_used, reps = 0, 0.0, 0
-    while t_used < target_s:
-        for (p, n, k, x) in work:
+    times = {proj: [] for (proj, *_rest) in work}
+    while t_used < target_s or reps < 3:
+        for (proj, p, n, k, x) in work:
             t0 = time.perf_counter()
             oracle.gemv_bf16(p, n, k, x)
-            t_used += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            t_used += dt
+            times[proj].append(dt)
             done_bytes += p.size + 2 * k + 4 * n
         reps += 1
-    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+    for (proj, p, n, k, x) in work:
+        med = float(np.median(times[proj][:3]))
+        per_linear[proj] = {"n_k": [n, k], "ms_median3": round(med * 1e3, 2),
+                            "GB/s": round((p.size + 2 * k + 4 * n) / med / 1e9, 4)}
+    layer_ms = sum(v["ms_median3"] for v in per_linear.values())
+    # config 0 on one core
+    t0_, s0_, x0_ = synth.config0_inputs()
+    p0 = oracle.pack(t0_, s0_)
+    oracle.set_threads(1)
+    c0 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.gemv_bf16(p0, 3072, 1024, x0_)
+        c0.append(time.perf_counter() - t0)
+    oracle.set_threads(used)
+    c0_ms = float(np.median(c0)) * 1e3
+    return {"value": round(done_bytes / t_used / 1e9, 4), "unit": "GB/s", "cores": used,
             "kind": "oracle",
             "sample": f"fp64 oracle bf16 GEMV over the 7 linears of one 8B layer, {reps} pass(es), "
                       f"{done_bytes / 1e6:.1f} MB algorithmic in {t_used:.1f} s",
-            "seconds": round(t_used, 2)}
+            "seconds": round(t_used, 2),
+            "affinity_cores": cores, "cpu_model": cpu_model(),
+            "per_linear_median3": per_linear,
+            "layer_ms_median3": round(layer_ms, 2),
+            "token_equiv_ternary_ms_estimate": round(36 * layer_ms, 1),
+            "c0_single_core_ms_median3": round(c0_ms, 2),
+            "c0_single_core_GB/s": round(849_920 / (c0_ms * 1e-3) / 1e9, 4),
+            "note": "correctness reference (naive bit-by-bit unpack, fp64 accumulation), not a tuned CPU kernel"}
 
 
 INT8_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA, TOP/s
@@ -297,6 +384,63 @@ def rotate_copies(torch, packed, total_bytes=1 << 30):
     """Distinct copies of a packed matrix so consecutive launches stream from HBM."""
     reps = max(1, min(256, total_bytes // max(1, packed.numel())))
     return [packed] + [packed.clone() for _ in range(reps - 1)]
+
+
+def measure_c0(tw, synth, torch, reps: int):
+    """The smallest configuration: one 3072 x 1024 ternary linear (seed 0), M = 1, as a
+    hipGraph over distinct packed copies totalling >= 1 GB, so every launch reads HBM."""
+    t, s, x = synth.config0_inputs()
+    n, k = t.shape
+    packed = tw.tern_pack(torch.from_numpy(t).cuda(), torch.from_numpy(s.view(np.int16)).cuda())
+    copies = [packed] + [packed.clone() for _ in range(max(1, (1 << 30) // packed.numel()))]
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    y = torch.empty((1, n), dtype=torch.float32, device="cuda")
+    g = capture(torch, lambda: [tw.tern_gemv(c, n, k, xd, y=y) for c in copies])
+    ms = time_replays(torch, g, reps) / len(copies)
+    nbytes = tw.tern_packed_bytes(n, k) + 2 * k + 4 * n
+    del g, copies
+    return {"workload": "config 0: one 3072x1024 ternary linear (0.6B gate shape), M=1, seed 0, bf16",
+            "copies_rotated": int((1 << 30) // packed.numel()) + 1, "us_per_launch": round(ms * 1e3, 3),
+            "bytes_per_launch": nbytes, "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+            "pct_hbm_peak": round(100 * nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2)}
+
+
+def measure_c1(tw, synth, torch, compose: str, reps: int):
+    """The 0.6B shapes: 196 ternary linears (fused: 112 launches) and the tied int8 head
+    151936 x 1024, M = 1, one token-equivalent per step; two copies of the model (distinct
+    memory, 2 x 274 MB, beyond the 256 MB last-level cache) are replayed alternately."""
+    steps = [Step(tw, synth, 1, compose, quiet=True)]
+    steps.append(steps[0].clone())
+    graphs = [capture(torch, st.run) for st in steps]
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        for g in graphs:
+            g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / (2 * reps) * 1e3
+    tern_graphs = [capture(torch, st.run_tern) for st in steps]
+    e0.record()
+    for _ in range(reps):
+        for g in tern_graphs:
+            g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    tern_us = e0.elapsed_time(e1) / (2 * reps) * 1e3
+    st = steps[0]
+    out = {"workload": "qwen3-0.6b-shapes token-equivalent: 196 ternary GEMVs (28 layers x q,k,v,o,gate,up,down) "
+                       "+ tied int8 head 151936x1024, M=1, two model copies alternated",
+           "compose": compose, "launches_per_step": len(st.launches) + 1, "bytes_per_step": int(st.bytes),
+           "us_per_token_equiv": round(us, 2), "GB/s": round(st.bytes / (us * 1e-6) / 1e9, 1),
+           "pct_hbm_peak": round(100 * st.bytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+           "ternary_us_per_token_equiv": round(tern_us, 2),
+           "ternary_us_per_launch": round(tern_us / len(st.launches), 3)}
+    del graphs, tern_graphs, steps
+    return out
 
 
 def mode_smallm(args, tw, synth, torch):
@@ -339,12 +483,13 @@ def mode_prefill(args, tw, synth, torch):
         cases = [(proj, int(m))]
     for proj in dict.fromkeys(p for p, _ in cases):
         n, k, packed, _ = shape_inputs(tw, synth, torch, proj, 1)
+        copies = [packed] + [packed.clone() for _ in range(15)]   # 16 x 13.4 MB: beyond the last-level cache
         for m in [m for p, m in cases if p == proj]:
             x = torch.from_numpy(synth.gen_x_bf16(np.random.default_rng(m), m, k).view(np.int16)).cuda()
             q, sx = tw.tern_quantize_i8(x)
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
-            g = capture(torch, lambda: [tw.tern_gemm_prefill(packed, n, k, q, sx, y=y) for _ in range(10)])
-            ms = time_replays(torch, g, 5) / 10
+            g = capture(torch, lambda: [tw.tern_gemm_prefill(c, n, k, q, sx, y=y) for c in copies])
+            ms = time_replays(torch, g, 5) / len(copies)
             ops = 2.0 * m * n * k
             tops = ops / (ms * 1e-3) / 1e12
             nbytes = tw.tern_packed_bytes(n, k) + m * (k + 4) + 4 * m * n
@@ -352,7 +497,37 @@ def mode_prefill(args, tw, synth, torch):
                         "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1),
                         "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
             del g
-    print(json.dumps({"mode": "prefill", "peak_tops": INT8_PEAK_TOPS, "rows": out}), flush=True)
+        del copies
+    print(json.dumps({"mode": "prefill", "peak_tops": INT8_PEAK_TOPS,
+                      "weights": "16 distinct packed copies per shape, replayed in turn", "rows": out}), flush=True)
+
+
+def mode_peak(args, tw, synth, torch):
+    """What the matrix cores sustain: the probe's independent MFMA chains on registers (no
+    memory traffic), 2048 workgroups of 4 waves, timed with HIP events over repeated launches;
+    the median of 5 timings against the published dense peaks."""
+    out = []
+    grid = 2048
+    sink = torch.empty(tw.lib().tern_mfma_peak_sink_bytes(grid) // 4, dtype=torch.int32, device="cuda")
+    for kind, iters, peak in (("int8", 20000, INT8_PEAK_TOPS), ("bf16", 20000, 2500.0)):
+        ops = tw.tern_mfma_peak(kind, iters, grid, sink)        # warm-up launch
+        torch.cuda.synchronize()
+        rates = []
+        for _ in range(5):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(4):
+                tw.tern_mfma_peak(kind, iters, grid, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            rates.append(4 * ops / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        med = float(np.median(rates))
+        out.append({"mfma": "v_mfma_i32_16x16x64_i8" if kind == "int8" else "v_mfma_f32_16x16x32_bf16",
+                    "T_ops_per_s_median": round(med, 1), "T_ops_per_s_runs": [round(r, 1) for r in rates],
+                    "published_dense_peak": peak, "pct_of_published": round(100 * med / peak, 1),
+                    "grid": grid, "iters": iters})
+        log(f"peak {kind}: {med:.0f} T/s ({100 * med / peak:.1f}% of {peak:.0f})")
+    print(json.dumps({"mode": "peak", "rows": out}), flush=True)
 
 
 def mode_head(args, tw, synth, torch):
@@ -526,6 +701,8 @@ def main():
         return mode_fv5(args, tw, synth, torch)
     if args.mode == "sweep":
         return mode_sweep(args, tw, synth, torch)
+    if args.mode == "peak":
+        return mode_peak(args, tw, synth, torch)
     if args.mode == "copy":
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -558,6 +735,11 @@ def main():
     for _ in range(args.warmup):
         one()
     torch.cuda.synchronize()
+    if graph is not None:
+        # every launch of the step ran once eagerly before capture, then W warmup replays
+        nt = len(step.launches)
+        log(f"dispatch window of the timed region: ternary GEMV launches [{nt * (1 + args.warmup)}, "
+            f"{nt * (1 + args.warmup + args.steps)}) of this process ({nt} per step)")
     t0 = time.perf_counter()
     for _ in range(args.steps):
         one()
@@ -579,8 +761,10 @@ def main():
     if chain:
         tern_ms = time_calls(torch, lambda: step.run_chain(ws, n_chain), reps)
     else:
+        # the only profiler region of the run: rocprofv3 --selected-regions traces exactly these
+        # reps x n_tern launches, the ones the roofline's average is taken over
         g_tern = capture(torch, step.run_tern)
-        tern_ms = time_replays(torch, g_tern, reps)
+        tern_ms = time_replays(torch, g_tern, reps, ProfilerRegion())
     achieved = step.tern_bytes / (tern_ms * 1e-3) / 1e9
     g_head = capture(torch, step.run_head)
     head_ms = time_replays(torch, g_head, reps)
@@ -598,6 +782,18 @@ def main():
                              "GB/s": round(b / (ms * 1e-3) / 1e9, 1),
                              "pct_peak": round(100 * b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 1)}
     layer_us = tern_ms / (n_tern / (4 if args.compose == "fused" else 7)) * 1e3
+    roof = roofline(root, args, achieved, tern_ms, n_tern, step)
+    bytes_step, tern_bytes, head_bytes = step.bytes, step.tern_bytes, step.head_bytes
+
+    used_graph = graph is not None
+    extra = {}
+    if args.config == 2 and not chain and not args.no_extra_configs:
+        del g_tern, g_head, graph, step
+        torch.cuda.empty_cache()
+        log("config 0 (one 3072x1024 linear, weights rotated over >= 1 GB) ...")
+        extra["config0"] = measure_c0(tw, synth, torch, reps)
+        log("config 1 (0.6B token-equivalent, two model copies alternated) ...")
+        extra["config1"] = measure_c1(tw, synth, torch, args.compose, reps)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -623,18 +819,19 @@ def main():
                                 "down) + int8 head 151936x4096, M=1" if args.config == 2 else
                                 "qwen3-0.6b-shapes token-equivalent: 196 ternary GEMVs + tied int8 head "
                                 "151936x1024, M=1"),
-                   "engine": args.engine, "compose": args.compose, "graph": graph is not None,
-                   "bytes_per_step": int(step.bytes)},
+                   "engine": args.engine, "compose": args.compose, "graph": used_graph,
+                   "bytes_per_step": int(bytes_step)},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
         "us_per_token_equiv": round(ms_per_step * 1e3, 2),
         "ternary_us_per_token_equiv": round(tern_ms * 1e3, 2),
         "us_per_layer": round(layer_us, 2),
         "head": {"us": round(head_ms * 1e3, 2),
-                 "GB/s": round(step.head_bytes / (head_ms * 1e-3) / 1e9, 1)},
+                 "GB/s": round(head_bytes / (head_ms * 1e-3) / 1e9, 1)},
         "per_shape": shapes,
-        "roofline": roofline(root, args, achieved, tern_ms, n_tern, step),
+        "roofline": roof,
         "cpu_baseline": cpu,
     }
+    out.update(extra)
     print(json.dumps(out), flush=True)
 
 

@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 8
+#define TERN_ABI_VERSION 9
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -368,6 +368,25 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * -TERN_E_SHAPE for a NULL out or a shape outside 1 <= M <= TERN_MAX_M_GEMV,
  * N, K >= 1, kind 0..7.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
+
+/* ---- matrix-core throughput probe (a measurement aid; no operation of the method) ----
+ *
+ * The contraction of tern_gemm_prefill runs on the int8 matrix cores and the
+ * GEMVs on the bf16 ones; their throughput targets are fractions of the
+ * chip's dense matrix-core peak.  This probe measures what the chip
+ * sustains: `grid` workgroups of 4 waves, each wave running 8 independent
+ * chains of `iters` MFMAs on registers (no memory traffic in the loop).
+ *   kind 0: v_mfma_i32_16x16x64_i8 (2*16*16*64 operations each)
+ *   kind 1: v_mfma_f32_16x16x32_bf16 (2*16*16*32 operations each)
+ * tern_mfma_peak_ops gives the operations one launch executes (-1 for a bad
+ * argument); the caller times the launch.  sink: device memory of
+ * tern_mfma_peak_sink_bytes(grid) bytes, 16-byte aligned, overwritten with
+ * the final accumulators (so no MFMA is optimised away).
+ * Errors: TERN_E_SHAPE for kind outside {0, 1}, iters < 0 or grid outside
+ * [1, 2^31 - 1]; TERN_E_NULL / TERN_E_ALIGN for sink. */
+double tern_mfma_peak_ops(int kind, int64_t iters, int64_t grid);
+int64_t tern_mfma_peak_sink_bytes(int64_t grid);
+int tern_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

@@ -57,6 +57,8 @@ def lib():
                         ("oracle_head_bf16", 10), ("oracle_head_i8", 12)]:
             getattr(L, name).restype = ctypes.c_int
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -210,6 +212,11 @@ def greedy_argmax(logits):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_threads(n: int) -> int:
+    """OpenMP threads of the oracle's loops from now on; returns the count in effect."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 def rel_l2(y, y_ref) -> float:

@@ -340,3 +340,15 @@ int oracle_num_threads(void)
     return 1;
 #endif
 }
+
+/* threads of the OpenMP loops from now on (n >= 1); returns the count in effect */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+    return omp_get_max_threads();
+#else
+    (void)n;
+    return 1;
+#endif
+}

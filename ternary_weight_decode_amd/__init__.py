@@ -30,11 +30,11 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
-           "tern_gemv_config")
+           "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
-               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed")
+               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -89,6 +89,11 @@ def lib():
                                              _p]
         L.tern_gemv_config.restype = ctypes.c_int
         L.tern_gemv_config.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i64)]
+        L.tern_mfma_peak_ops.restype = ctypes.c_double
+        L.tern_mfma_peak_ops.argtypes = [ctypes.c_int, _i64, _i64]
+        L.tern_mfma_peak_sink_bytes.restype = _i64
+        L.tern_mfma_peak_sink_bytes.argtypes = [_i64]
+        L.tern_mfma_peak.argtypes = [ctypes.c_int, _i64, _i64, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -488,3 +493,22 @@ def tern_gemv_config(n: int, k: int, m: int, kind: str = "ternary_bf16"):
         return None
     keys = ("R", "waves", "U", "XC", "grid", "lds", "rounds", "MT")
     return dict(zip(keys, (int(v) for v in out)))
+
+
+MFMA_PEAK_KINDS = {"int8": 0, "bf16": 1}
+
+
+def tern_mfma_peak(kind: str, iters: int, grid: int, sink=None, stream=None):
+    """Matrix-core throughput probe (measurement aid): enqueue one launch of
+    `grid` workgroups running independent MFMA chains of `iters` steps
+    ("int8": 16x16x64 i8, "bf16": 16x16x32 bf16).  Returns the operations the
+    launch executes; time it with events on the same stream."""
+    import torch
+    k = MFMA_PEAK_KINDS[kind]
+    ops = float(lib().tern_mfma_peak_ops(k, iters, grid))
+    if ops < 0:
+        _check("tern_mfma_peak", 2)
+    if sink is None:
+        sink = torch.empty(int(lib().tern_mfma_peak_sink_bytes(grid)) // 4, dtype=torch.int32, device="cuda")
+    _check("tern_mfma_peak", lib().tern_mfma_peak(k, iters, grid, _ptr(sink), _stream(stream)))
+    return ops

@@ -19,7 +19,7 @@ OUT = os.path.join(HERE, "libtern.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["tern_api.hip", "tern_pack.hip", "tern_quant.hip", "tern_gemv.hip", "tern_head.hip", "tern_prefill.hip", "tern_chain.hip", "tern5.hip"]
+SOURCES = ["tern_api.hip", "tern_pack.hip", "tern_quant.hip", "tern_gemv.hip", "tern_head.hip", "tern_prefill.hip", "tern_chain.hip", "tern5.hip", "tern_peak.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 

@@ -510,3 +510,29 @@ int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out)
 }
 
 }  // extern "C"
+
+extern "C" {
+
+double tern_mfma_peak_ops(int kind, int64_t iters, int64_t grid)
+{
+    if ((kind != 0 && kind != 1) || iters < 0 || grid < 0) return -1.0;
+    return tern::mfma_peak_ops(kind, iters, grid);
+}
+
+int64_t tern_mfma_peak_sink_bytes(int64_t grid)
+{
+    if (grid < 0) return -1;
+    return tern::mfma_peak_sink_ints(grid) * 4;
+}
+
+int tern_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, void* stream)
+{
+    if ((kind != 0 && kind != 1) || iters < 0 || grid < 1 || grid > 0x7FFFFFFF) return TERN_E_SHAPE;
+    if (!sink) return TERN_E_NULL;
+    if (!aligned16(sink)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_mfma_peak(kind, iters, grid, sink, (hipStream_t)stream));
+}
+
+}  // extern "C"

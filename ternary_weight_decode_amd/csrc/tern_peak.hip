@@ -1,0 +1,68 @@
+// tern_peak.hip — matrix-core throughput probe: independent MFMA chains on
+// registers with no memory traffic inside the loop, so the achieved rate is
+// the chip's sustained matrix-core rate for that instruction.  It is the
+// denominator check for the prefill contraction (int8 16x16x64) and the
+// GEMV's bf16 16x16x32 steps; it computes nothing of the method.
+#include "tern_device.h"
+#include "tern_launch.h"
+
+namespace tern {
+
+constexpr int kPeakChains = 8;      // independent accumulators per wave (covers the MFMA latency)
+constexpr int kPeakWaves = 4;       // waves per workgroup
+
+// Each wave runs kPeakChains dependent chains of `iters` MFMAs.  Operands
+// depend on the lane and the loop counter stays opaque to the compiler, so
+// no MFMA is folded away; every accumulator is stored at the end.
+template <int kKind>
+__global__ __launch_bounds__(64 * kPeakWaves) void mfma_peak_kernel(int64_t iters, int32_t* __restrict__ sink)
+{
+    const int lane = threadIdx.x & 63;
+    const uint32_t a0 = 0x01010101u * (uint32_t)(lane + 1), b0 = 0x02030405u ^ (uint32_t)lane;
+    u32x4 a = {a0, a0 ^ 1u, a0 ^ 2u, a0 ^ 3u}, b = {b0, b0 + 1u, b0 + 2u, b0 + 3u};
+    if constexpr (kKind == 0) {
+        i32x4 c[kPeakChains];
+#pragma unroll
+        for (int j = 0; j < kPeakChains; ++j) c[j] = i32x4{j, 0, 0, 0};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kPeakChains; ++j) c[j] = mfma_i8(a, b, c[j]);
+        }
+        i32x4 s = c[0];
+#pragma unroll
+        for (int j = 1; j < kPeakChains; ++j) s += c[j];
+        *(i32x4*)(sink + ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4) = s;
+    } else {
+        // bf16 operands kept finite and small: exponent bits of 1.0 with lane-dependent mantissas
+        a = (a & 0x007F007Fu) | 0x3F803F80u;
+        b = (b & 0x007F007Fu) | 0x3F803F80u;
+        f32x4 c[kPeakChains];
+#pragma unroll
+        for (int j = 0; j < kPeakChains; ++j) c[j] = f32x4{(float)j, 0.f, 0.f, 0.f};
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < kPeakChains; ++j) c[j] = mfma_bf16(a, b, c[j]);
+        }
+        f32x4 s = c[0];
+#pragma unroll
+        for (int j = 1; j < kPeakChains; ++j) s += c[j];
+        *(f32x4*)(sink + ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4) = s;
+    }
+}
+
+double mfma_peak_ops(int kind, int64_t iters, int64_t grid)
+{
+    const double per_mfma = kind == 0 ? 2.0 * 16 * 16 * 64 : 2.0 * 16 * 16 * 32;
+    return per_mfma * (double)iters * kPeakChains * kPeakWaves * (double)grid;
+}
+
+int64_t mfma_peak_sink_ints(int64_t grid) { return grid * 64 * kPeakWaves * 4; }
+
+hipError_t launch_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, hipStream_t stream)
+{
+    if (kind == 0) mfma_peak_kernel<0><<<dim3((unsigned)grid), dim3(64 * kPeakWaves), 0, stream>>>(iters, sink);
+    else mfma_peak_kernel<1><<<dim3((unsigned)grid), dim3(64 * kPeakWaves), 0, stream>>>(iters, sink);
+    return hipGetLastError();
+}
+
+}  // namespace tern

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 8
+    assert L.tern_abi_version() == 9
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -256,3 +256,17 @@ def test_chain_run_argument_errors():
     assert L.tern_gemv_chain(ctypes.c_void_p(0x100010), 1, None) == E_ALIGN
     assert L.tern_gemv_chain(ctypes.c_void_p(0x100000), -1, None) == E_SHAPE
     assert L.tern_gemv_chain(ctypes.c_void_p(0x100000), 0, None) == E_OK
+
+
+def test_mfma_peak_probe_validation():
+    """The matrix-core probe's operation count and its argument checks (no device call)."""
+    L = tw.lib()
+    assert L.tern_mfma_peak_ops(0, 1000, 1024) == 2.0 * 16 * 16 * 64 * 1000 * 8 * 4 * 1024
+    assert L.tern_mfma_peak_ops(1, 10, 3) == 2.0 * 16 * 16 * 32 * 10 * 8 * 4 * 3
+    assert L.tern_mfma_peak_ops(2, 10, 3) == -1.0
+    assert L.tern_mfma_peak_sink_bytes(5) == 5 * 256 * 16
+    assert L.tern_mfma_peak(2, 10, 1, ALIGNED, None) == E_SHAPE
+    assert L.tern_mfma_peak(0, 10, 0, ALIGNED, None) == E_SHAPE
+    assert L.tern_mfma_peak(0, -1, 1, ALIGNED, None) == E_SHAPE
+    assert L.tern_mfma_peak(0, 10, 1, None, None) == E_NULL
+    assert L.tern_mfma_peak(0, 10, 1, MISALIGNED, None) == E_ALIGN
