@@ -23,10 +23,11 @@ __global__ __launch_bounds__(64 * kPeakWaves) void mfma_peak_kernel(int64_t iter
     if constexpr (kKind == 0) {
         i32x4 c[kPeakChains];
 #pragma unroll
-        for (int j = 0; j < kPeakChains; ++j) c[j] = i32x4{j, 0, 0, 0};
+        for (int j = 0; j < kPeakChains; ++j) c[j] = i32x4{lane + j, lane ^ j, 3 * lane + j, lane - j};
         for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
             for (int j = 0; j < kPeakChains; ++j) c[j] = mfma_i8(a, b, c[j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         i32x4 s = c[0];
 #pragma unroll
@@ -38,10 +39,12 @@ __global__ __launch_bounds__(64 * kPeakWaves) void mfma_peak_kernel(int64_t iter
         b = (b & 0x007F007Fu) | 0x3F803F80u;
         f32x4 c[kPeakChains];
 #pragma unroll
-        for (int j = 0; j < kPeakChains; ++j) c[j] = f32x4{(float)j, 0.f, 0.f, 0.f};
+        for (int j = 0; j < kPeakChains; ++j)
+            c[j] = f32x4{(float)(lane + j), (float)(lane ^ j), (float)(3 * lane + j), (float)(lane - j)};
         for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
             for (int j = 0; j < kPeakChains; ++j) c[j] = mfma_bf16(a, b, c[j]);
+            __builtin_amdgcn_sched_barrier(0);
         }
         f32x4 s = c[0];
 #pragma unroll
