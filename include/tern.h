@@ -181,6 +181,20 @@ int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_
                       const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
                       void* stream);
 
+/* i8_head_argmax without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same inputs, outputs, limits and result
+ * as i8_head_argmax (bf16 x); the argmax keys live in a device array the
+ * library owns, 2 MiB per device (held until the process ends):
+ * i8_head_argmax_workspace_bytes(V, M) must not exceed 2097152 bytes, i.e.
+ * ceil(V/16) * M <= 262144 (V = 151936 allows every M up to
+ * TERN_MAX_M_GEMV), else TERN_E_SHAPE and nothing is launched.  Nothing is
+ * allocated or freed.  Every call on a device shares that array: calls that
+ * overlap in time on one device (other streams, other threads) race and
+ * must be ordered by the caller. */
+int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                           int64_t M, int32_t* idx, float* val, float* logits, void* stream);
+
 /* Prefill-size ternary GEMM with int8 activations (batched prefill, [P2]
  * section "실행해보기: pip부터 llama.cpp 포크까지"; batched verify is
  * compute-bound, section "노트북에서는 이야기가 다르다"),

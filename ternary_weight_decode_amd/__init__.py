@@ -30,11 +30,13 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
-           "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak")
+           "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
+           "i8_head_argmax_noalloc")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
-               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak")
+               "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak",
+               "i8_head_argmax_noalloc")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -75,6 +77,7 @@ def lib():
         L.i8_head_argmax_workspace_bytes.argtypes = [_i64, _i64]
         L.i8_head_argmax.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.i8_head_argmax_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
+        L.i8_head_argmax_noalloc.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p]
         L.tern5_packed_bytes.restype = _i64
         L.tern5_packed_bytes.argtypes = [_i64, _i64]
         L.tern5_pack.argtypes = [_p, _p, _p, _i64, _i64, _p, _p]
@@ -242,6 +245,20 @@ def i8_head_argmax(w, row_scale, x, workspace=None, logits=None, stream=None):
     val = torch.empty(m, dtype=torch.float32, device=x.device)
     _check("i8_head_argmax", lib().i8_head_argmax(_ptr(w), _ptr(row_scale), v, k, _ptr(x), m, _ptr(idx), _ptr(val),
                                                   _ptr(logits), _ptr(workspace), _stream(stream)))
+    return idx, val
+
+
+def i8_head_argmax_noalloc(w, row_scale, x, idx, val, logits=None, stream=None):
+    """i8_head_argmax with the keys in the library's own device array: allocates nothing, so the
+    caller passes idx (int32 [M]) and val (fp32 [M]); calls overlapping on one device race."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    v, k = w.shape
+    m = x.shape[0]
+    _check("i8_head_argmax_noalloc", lib().i8_head_argmax_noalloc(_ptr(w), _ptr(row_scale), v, k, _ptr(x), m,
+                                                                  _ptr(idx), _ptr(val), _ptr(logits),
+                                                                  _stream(stream)))
     return idx, val
 
 

@@ -182,11 +182,12 @@ int64_t i8_head_argmax_workspace_bytes(int64_t V, int64_t M)
 
 static int head_argmax_check(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const void* act,
                              const float* s_x, bool int8_act, int64_t M, int32_t* idx, float* val, float* logits,
-                             void* workspace)
+                             void* workspace, bool need_workspace = true)
 {
     if (bad_nk(V, K) || K == 0 || V < 1 || V > 0xFFFFFFF0ll || M < 1 || M > TERN_MAX_M_GEMV) return TERN_E_SHAPE;
     if (!tern::head_argmax_fits(K, M, int8_act)) return TERN_E_SHAPE;
-    if (!W || !row_scale || !act || !idx || !val || !workspace || (int8_act && !s_x)) return TERN_E_NULL;
+    if (!W || !row_scale || !act || !idx || !val || (need_workspace && !workspace) || (int8_act && !s_x))
+        return TERN_E_NULL;
     if (!aligned16(W) || !aligned16(act) || !aligned4(row_scale) || !aligned4(idx) || !aligned4(val) ||
         (logits && !aligned4(logits)) || (s_x && !aligned4(s_x)) || ((uintptr_t)workspace & 7))
         return TERN_E_ALIGN;
@@ -200,6 +201,19 @@ int i8_head_argmax(const int8_t* W, const float* row_scale, int64_t V, int64_t K
     if (rc) return rc;
     return finish(tern::launch_head_argmax_bf16(W, row_scale, V, K, x, M, logits, idx, val, workspace,
                                                 (hipStream_t)stream));
+}
+
+int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                           int64_t M, int32_t* idx, float* val, float* logits, void* stream)
+{
+    if (V >= 1 && M >= 1 && M <= TERN_MAX_M_GEMV && V <= 0xFFFFFFF0ll &&
+        i8_head_argmax_workspace_bytes(V, M) > tern::kHeadArgmaxScratchBytes)
+        return TERN_E_SHAPE;
+    // the checks of i8_head_argmax, without a workspace (the library's array holds the keys)
+    const int rc = head_argmax_check(W, row_scale, V, K, x, nullptr, false, M, idx, val, logits, nullptr, false);
+    if (rc) return rc;
+    return finish(tern::launch_head_argmax_bf16_noalloc(W, row_scale, V, K, x, M, logits, idx, val,
+                                                        (hipStream_t)stream));
 }
 
 int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,

@@ -14,6 +14,8 @@
 // the byte-select convert (exact) -> bf16 pair by taking the high halves
 // (exact: |w| <= 127 has 7 significant bits), then MFMA 16x16x32 bf16.
 // int8 path: bytes go straight into MFMA 16x16x64 i8.
+#include <mutex>
+
 #include "tern_device.h"
 #include "tern_launch.h"
 
@@ -489,6 +491,48 @@ hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, in
                                  hipStream_t stream)
 {
     return launch_head_argmax<true>(W, rs, V, K, q, s_x, M, y, idx, val, ws, stream);
+}
+
+// ---- the argmax keys in a library-owned array (for callers that cannot
+// allocate): every call on a device shares this array, which keeps the last
+// call's keys.  Every slot the finish kernel reads is written by the head
+// kernel of the same call first, so nothing needs clearing; calls that
+// overlap in time on one device race on it.
+static __device__ __align__(256) unsigned long long scratch[kHeadArgmaxScratchBytes / 8];
+
+// Device address of `scratch` on the current device, looked up once per
+// device (each device holds its own copy of the array at its own address).
+// Host code uses only this address: the array's name on the host is a
+// stand-in, not a device pointer.
+static hipError_t head_argmax_scratch(void** out)
+{
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDev] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDev) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+hipError_t launch_head_argmax_bf16_noalloc(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                           int64_t M, float* y, int32_t* idx, float* val, hipStream_t stream)
+{
+    if ((V + 15) / 16 * M * 8 > kHeadArgmaxScratchBytes) return hipErrorInvalidValue;   // the caller checked this
+    void* ws = nullptr;
+    const hipError_t e = head_argmax_scratch(&ws);
+    if (e != hipSuccess) return e;
+    return launch_head_argmax<false>(W, rs, V, K, x, nullptr, M, y, idx, val, ws, stream);
 }
 
 // ---- block-scaled (FV5B-style) head: x must fit in LDS (head_argmax_fits)

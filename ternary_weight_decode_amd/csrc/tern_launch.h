@@ -38,6 +38,11 @@ hipError_t launch_head_argmax_bf16(const int8_t* W, const float* rs, int64_t V, 
 hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                                  const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                  hipStream_t stream);
+// the bf16 head + argmax with its keys in a library-owned device array of
+// kHeadArgmaxScratchBytes (no workspace argument, nothing allocated)
+constexpr int64_t kHeadArgmaxScratchBytes = 2 << 20;
+hipError_t launch_head_argmax_bf16_noalloc(const int8_t* W, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                           int64_t M, float* y, int32_t* idx, float* val, hipStream_t stream);
 // ---- block-scaled (FV5B-style) head and embedding rows ----
 hipError_t launch_fv5b_head_bf16(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,
                                  int64_t M, float* y, hipStream_t stream);

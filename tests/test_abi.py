@@ -270,3 +270,17 @@ def test_mfma_peak_probe_validation():
     assert L.tern_mfma_peak(0, -1, 1, ALIGNED, None) == E_SHAPE
     assert L.tern_mfma_peak(0, 10, 1, None, None) == E_NULL
     assert L.tern_mfma_peak(0, 10, 1, MISALIGNED, None) == E_ALIGN
+
+
+def test_head_argmax_noalloc_validation():
+    """The allocation-free head argmax rejects, on the host, a head whose keys
+    exceed the library's 2 MiB array, and bad shapes or pointers like
+    i8_head_argmax does."""
+    L = tw.lib()
+    p = ALIGNED
+    assert L.i8_head_argmax_noalloc(p, p, 16 * 262144 + 16, 128, p, 1, p, p, None, None) == E_SHAPE
+    assert L.i8_head_argmax_noalloc(p, p, 16 * 16384 + 16, 128, p, 16, p, p, None, None) == E_SHAPE
+    assert L.i8_head_argmax_noalloc(p, p, 100, 96, p, 1, p, p, None, None) == E_SHAPE       # K % 128
+    assert L.i8_head_argmax_noalloc(p, p, 100, 128, p, 17, p, p, None, None) == E_SHAPE     # M > 16
+    assert L.i8_head_argmax_noalloc(p, p, 100, 128, p, 1, None, p, None, None) == E_NULL
+    assert L.i8_head_argmax_noalloc(p, p, 100, 128, MISALIGNED, 1, p, p, None, None) == E_ALIGN
