@@ -444,14 +444,14 @@ def measure_c1(tw, synth, torch, compose: str, reps: int):
 
 
 def mode_smallm(args, tw, synth, torch):
-    """Speculative-verify sweep: every 8B shape at M in {1,2,4,7,8}, bf16 and int8 activations;
-    weights rotate over >= 1 GB of copies so each launch reads HBM."""
+    """Speculative-verify sweep: every 8B shape at M in {1,2,4,7,8} (and 16, the largest batch a call
+    takes), bf16 and int8 activations; weights rotate over >= 1 GB of copies so each launch reads HBM."""
     out = []
     for proj in synth.PROJ:
-        n, k, packed, x8 = shape_inputs(tw, synth, torch, proj, 8)
+        n, k, packed, x16 = shape_inputs(tw, synth, torch, proj, 16)
         copies = rotate_copies(torch, packed)
-        for m in (1, 2, 4, 7, 8):
-            x = x8[:m].contiguous()
+        for m in (1, 2, 4, 7, 8, 16):
+            x = x16[:m].contiguous()
             q, sx = tw.tern_quantize_i8(x)
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
             for variant in ("bf16", "int8"):

@@ -372,7 +372,8 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * tern5_gemv (2) or tern5_gemv_i8 (3) takes for this shape, or the two-phase
  * configuration that tern_gemv / tern_gemv_i8 (kinds 4 and 5) or tern5_gemv /
  * tern5_gemv_i8 (6 and 7) take when no one-pass one fits (activations staged
- * in LDS one half of K at a time),
+ * in LDS one half of K at a time), or the three-phase configuration that
+ * tern_gemv takes when neither fits (kind 8: a third of K at a time),
  * computed on the host exactly as the launchers do (the CU count is the current device's, or
  * 256 without one; the launchers also confirm residency with the occupancy
  * query).  Returns 1 and fills out[8] = {row tiles per workgroup R, waves per
@@ -380,7 +381,7 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * dynamic LDS bytes, runs in several rounds (0/1), MFMA activation rows of the
  * kernel instance}; 0 when another kernel takes the shape; -TERN_E_NULL or
  * -TERN_E_SHAPE for a NULL out or a shape outside 1 <= M <= TERN_MAX_M_GEMV,
- * N, K >= 1, kind 0..7.  Touches no device memory. */
+ * N, K >= 1, kind 0..8.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
 
 /* ---- matrix-core throughput probe (a measurement aid; no operation of the method) ----

@@ -503,14 +503,16 @@ extern "C" {
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out)
 {
     if (!out) return -TERN_E_NULL;
-    if (kind < 0 || kind > 7 || N < 1 || K < 1 || M < 1 || M > TERN_MAX_M_GEMV) return -TERN_E_SHAPE;
+    if (kind < 0 || kind > 8 || N < 1 || K < 1 || M < 1 || M > TERN_MAX_M_GEMV) return -TERN_E_SHAPE;
     const bool i8 = (kind & 1) != 0;
     tern::OneShot c{};
     bool one;
     if (kind < 2) one = tern::gemv_oneshot_config(N, K, M, i8, c);
     else if (kind < 4) one = tern::gemv5_oneshot_config(N, K, M, i8, c);
     else if (kind < 6) one = !tern::gemv_oneshot_config(N, K, M, i8, c) && tern::gemv_phased_config(N, K, M, i8, c);
-    else one = !tern::gemv5_oneshot_config(N, K, M, i8, c) && tern::gemv5_phased_config(N, K, M, i8, c);
+    else if (kind < 8) one = !tern::gemv5_oneshot_config(N, K, M, i8, c) && tern::gemv5_phased_config(N, K, M, i8, c);
+    else one = !tern::gemv_oneshot_config(N, K, M, false, c) && !tern::gemv_phased_config(N, K, M, false, c) &&
+               tern::gemv_phased3_config(N, K, M, c);
     if (!one) return 0;
     out[0] = c.R;
     out[1] = c.nw;

@@ -505,6 +505,111 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     }
 }
 
+// Three-phase variant for bf16 activations of up to 16 rows whose halves of K
+// still exceed LDS (the 8B down projection, K = 12288, at M = 9..16): one row
+// tile per workgroup and nkt / 3 waves with three units each, unit i of every
+// wave in third i of K.  The first two thirds of x are loaded into two
+// register sets up front; each third is staged into LDS in turn, and the set
+// the first came from is refilled with the last third while the first is
+// computed.  The weights stream once for all M rows.  Partials are summed in
+// k-tile order (deterministic).
+template <int XC>
+__global__ __launch_bounds__(512) void gemv_phased3_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                           const uint16_t* __restrict__ x, int M,
+                                                           float* __restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = 4;
+    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = nkt / 3
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7), nkt = nb >> 2;
+    const int64_t rt = blockIdx.x;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    const int pk = nw * kTileK;                                      // k per third
+    const int xrow_bytes = (pk + 8) * 2;                             // staged bytes per activation row
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);            // [nkt][NI][64]
+    // chunk indices past the end store to a dummy slot after the partials
+    const int dummy = M * xrow_bytes + nkt * NI * 64 * 4;
+
+    const int row_chunks = (int)(K * 2 / 16);                        // 16-byte chunks per activation row
+    const int per_row = pk * 2 / 16, chunks = M * per_row;
+    int xsrc[XC], xdst[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int u = threadIdx.x + c * nthreads;
+        const int uc = u < chunks ? u : chunks - 1;
+        const int m = uc / per_row, cc = uc - m * per_row;
+        xsrc[c] = m * row_chunks + cc;
+        xdst[c] = u < chunks ? m * xrow_bytes + 16 * cc : dummy;
+    }
+    u32x4 xa[XC], xb[XC];
+    auto load_x = [&](int ph, u32x4 (&v)[XC]) {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) v[c] = xg[xsrc[c] + ph * per_row];
+    };
+    auto stage = [&](const u32x4 (&v)[XC]) {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) *(u32x4*)(smem + xdst[c]) = v[c];
+    };
+    PlaneTile t[3];
+    auto load_unit = [&](int i) {
+        const int kt = wave + i * nw;
+        const int64_t wb = tile_word_base(rt, kt, nb);
+        const int64_t sb = tile_scale_base(rt, kt, nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        t[i].sc = ld_nt8(scales + sb + r * 4);
+    };
+    const int mrow = r < M ? r : M - 1;
+    const uint8_t* xrow = smem + mrow * xrow_bytes + 64 * g;
+    auto compute = [&](int i) {
+        const int kt = wave + i * nw;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16_tile<16>(t[i], (const uint16_t*)xrow + wave * kTileK, 4, acc);
+#pragma unroll
+        for (int q = 0; q < NI; ++q) red[(kt * NI + q) * 64 + lane] = acc[q];
+    };
+
+    load_x(0, xa);
+    load_x(1, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    load_unit(0);
+    __builtin_amdgcn_sched_barrier(0);
+    stage(xa);
+    __syncthreads();
+    load_unit(1);
+    __builtin_amdgcn_sched_barrier(0);
+    load_unit(2);
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(2, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(0);
+    __syncthreads();                       // every wave has read the first third
+    stage(xb);
+    __syncthreads();
+    compute(1);
+    __syncthreads();
+    stage(xa);
+    __syncthreads();
+    compute(2);
+    __syncthreads();
+
+    const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
+    for (int e = threadIdx.x; e < NI * 64; e += nthreads) {
+        const int l = e & 63, q = e >> 6;
+        const int m = 4 * (l >> 4) + q, n = l & 15;
+        const int64_t row = rt * kTileRows + n;
+        if (l < lanes_used && m < M && row < N) {
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            y[(int64_t)m * N + row] = sum;
+        }
+    }
+}
+
 // ------------------------------------------------------------------ int8
 
 template <int MT>
@@ -769,6 +874,46 @@ bool gemv_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
     return pick_phased(N, K, M, i8, c);
 }
 
+// Three-phase configuration (gemv_phased3_kernel, bf16): one row tile per
+// workgroup, nkt / 3 waves of three units, a third of x in LDS at a time.
+static bool pick_phased3(int64_t N, int64_t K, int64_t M, OneShot& c)
+{
+    if (K % kTileK != 0 || M < 1 || M > 16 || N < 1) return false;
+    const int64_t nkt = K / kTileK;
+    if (nkt % 3 != 0 || nkt / 3 > 8 || nkt < 3) return false;
+    c.R = 1;
+    c.U = 3;
+    c.nw = (int)(nkt / 3);
+    c.grid = (N + 15) / 16;
+    c.rounds = true;
+    const int64_t pk = c.nw * kTileK;
+    const int64_t xc = (M * pk * 2 / 16 + 64 * c.nw - 1) / (64 * c.nw);
+    if (xc > 16) return false;
+    c.XC = xc <= 4 ? 4 : (xc <= 8 ? 8 : 16);
+    c.lds = (size_t)(M * (pk + 8) * 2) + (size_t)nkt * 4 * 64 * 4 + 16;   // + dummy slot
+    return c.lds <= (size_t)kCuLds;
+}
+
+bool gemv_phased3_config(int64_t N, int64_t K, int64_t M, OneShot& c) { return pick_phased3(N, K, M, c); }
+
+static hipError_t launch_phased3(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
+                                 hipStream_t stream)
+{
+    OneShot c;
+    if (!pick_phased3(N, K, M, c)) return hipErrorNotSupported;
+#define TERN_PHASED3_CASE(XX)                                                                            \
+    if (c.XC == XX) {                                                                                    \
+        if (!oneshot_resident(gemv_phased3_kernel<XX>, c)) return hipErrorNotSupported;                  \
+        gemv_phased3_kernel<XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, \
+                                                                                          (int)M, y);    \
+        return hipGetLastError();                                                                        \
+    }
+    TERN_PHASED3_CASE(4) TERN_PHASED3_CASE(8) TERN_PHASED3_CASE(16)
+#undef TERN_PHASED3_CASE
+    return hipErrorNotSupported;
+}
+
+
 hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const uint16_t* x, int64_t M, float* y,
                             hipStream_t stream)
 {
@@ -788,6 +933,12 @@ hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const u
         if (M == 2) return launch_fast_mt<2>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
         if (M <= 4) return launch_fast_mt<4>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
         return launch_fast_mt<16>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
+    }
+    // Activation halves beyond LDS but thirds within it (8B down at M = 9..16):
+    // the three-phase kernel reads the weights once for all rows.
+    {
+        const hipError_t e = launch_phased3(packed, N, K, x, M, y, stream);
+        if (e != hipErrorNotSupported) return e;
     }
     // More than 8 activation rows that fit none of the kernels above: two
     // calls on row halves take the one-pass or two-phase kernels, which read

@@ -524,13 +524,31 @@ def test_gemv_bf16_two_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
-@pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12)])
-def test_gemv_bf16_row_halves(tw, n, k, m):
-    """bf16 activations of more than 8 rows that fit no one-pass or
-    two-phase configuration: the call runs on rows 0..7 and 8..M-1 through
-    those kernels; every output against the oracle."""
+@pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12), (300, 12288, 13)])
+def test_gemv_bf16_three_phase(tw, n, k, m):
+    """bf16 activations of more than 8 rows whose halves of K exceed LDS (the
+    8B down shape at M = 9..16): x staged a third of K at a time, the weights
+    read once; every output against the oracle."""
     assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased") is None
-    assert tw.tern_gemv_config(n, k, 8, "ternary_bf16_phased") is not None
+    assert tw.tern_gemv_config(n, k, m, "ternary_bf16_phased3") is not None
+    t, s, x = gen(n, k, m, seed=5 * n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
+@pytest.mark.parametrize("n,k,m", [(1000, 8192, 16), (37, 8192, 11)])
+def test_gemv_bf16_row_halves(tw, n, k, m):
+    """bf16 activations of more than 8 rows that fit no one-pass, two-phase
+    or three-phase configuration (K = 8192 is not a multiple of 3 k-tiles):
+    the call runs on rows 0..7 and 8..M-1 through those kernels; every output
+    against the oracle."""
+    assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased") is None
+    assert tw.tern_gemv_config(n, k, m, "ternary_bf16_phased3") is None
+    assert (tw.tern_gemv_config(n, k, 8) is not None or
+            tw.tern_gemv_config(n, k, 8, "ternary_bf16_phased") is not None)
     t, s, x = gen(n, k, m, seed=2 * n + m)
     y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
     y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)

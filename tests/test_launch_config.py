@@ -20,7 +20,7 @@ KS = [512, 1024, 4096, 12288, 16384, 32768]
 MS = [1, 2, 3, 4, 5, 8, 12, 16]
 
 
-@pytest.mark.parametrize("kind", [k for k in tw.GEMV_KINDS if not k.endswith("phased")])
+@pytest.mark.parametrize("kind", [k for k in tw.GEMV_KINDS if "phased" not in k])
 def test_picker_invariants(kind):
     i8 = kind.endswith("int8")
     taken = 0
@@ -89,6 +89,33 @@ def test_phased_picker_invariants(kind):
         assert c is not None and c["waves"] == 12 and c["XC"] == 4
 
 
+def test_phased3_picker_invariants():
+    """The three-phase configuration (bf16): taken only where neither the
+    one-pass nor the two-phase one fits; one row tile per workgroup, nkt / 3
+    waves with three units each, a third of the activations staged at a
+    time; the 8B down shape at M = 9..16 takes it."""
+    taken = 0
+    for n, k, m in itertools.product(NS, KS, MS):
+        c = tw.tern_gemv_config(n, k, m, "ternary_bf16_phased3")
+        if c is None:
+            continue
+        taken += 1
+        where = (n, k, m, c)
+        assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased") is None
+        nkt = k // 512
+        assert c["R"] == 1 and c["U"] == 3 and c["waves"] * 3 == nkt and c["waves"] <= 8, where
+        assert c["grid"] == (n + 15) // 16 and c["MT"] == 16, where
+        pk = c["waves"] * 512
+        assert c["lds"] == m * (pk + 8) * 2 + nkt * 4 * 64 * 4 + 16 <= CU_LDS, where   # + a dummy staging slot
+        assert c["XC"] * 64 * c["waves"] * 16 >= m * pk * 2 and c["XC"] in (4, 8, 16), where   # a third staged
+    assert taken > 0
+    for m in range(9, 17):
+        c = tw.tern_gemv_config(4096, 12288, m, "ternary_bf16_phased3")
+        assert c is not None and c["waves"] == 8 and c["XC"] == 16, (m, c)
+    for m in range(1, 9):
+        assert tw.tern_gemv_config(4096, 12288, m, "ternary_bf16_phased3") is None, m
+
+
 def test_picker_8b_decode_shapes():
     """The configurations measured for the fused 8B linears at M = 1."""
     want = {(6144, 4096): (2, 8, 2, 192), (4096, 4096): (1, 8, 1, 256), (24576, 4096): (2, 8, 2, 768),
@@ -115,5 +142,5 @@ def test_picker_argument_errors():
     out = (ctypes.c_int64 * 8)()
     assert L.tern_gemv_config(16, 512, 1, 0, None) == -1
     assert L.tern_gemv_config(16, 512, 17, 0, out) == -2
-    assert L.tern_gemv_config(16, 512, 1, 8, out) == -2
+    assert L.tern_gemv_config(16, 512, 1, 9, out) == -2
     assert L.tern_gemv_config(0, 512, 1, 0, out) == -2
