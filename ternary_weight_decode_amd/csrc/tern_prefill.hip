@@ -13,6 +13,7 @@
 // permuted to the decoded byte order on the way in.  One barrier per block.
 #include "tern_device.h"
 #include "tern_launch.h"
+#include "tern_tile.h"
 
 namespace tern {
 
@@ -444,6 +445,240 @@ static hipError_t launch_pf(const uint8_t* packed, int64_t N, int64_t K, const i
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Small-M kernel (17 <= M <= 64, MG groups of 16 activation rows): the int8
+// one-pass GEMV's split of K across the waves of a workgroup, instead of one
+// serial pass over K per workgroup.  A workgroup owns R row tiles and R*nwr
+// waves; wave (rr, kw) takes k-tile kw of row tile rr in every phase, and
+// phase ph covers k-tiles [ph*nwr, (ph+1)*nwr), so unit ph of every wave lies
+// in phase ph.  The activations of a phase (MG*16 rows x nwr*512 bytes) are
+// staged in LDS in the decoded byte order, and the register set they came
+// from is refilled with the next phase's at once; each wave decodes its unit
+// once and reuses it
+// across the MG row groups (two int8 MFMAs per group and 128-k block, exact
+// int32 block sums folded in fp32 with the block scale).  Partials meet in
+// LDS and are summed in k-tile order (deterministic).  Rows past M repeat row
+// M-1 and rows past N a real row tile; their outputs are dropped.
+template <int MG, int XC, bool kDbg>
+__global__ __launch_bounds__(768) void prefill_small_kernel(const uint8_t* __restrict__ packed, int64_t N,
+                                                             int64_t K, const int8_t* __restrict__ q,
+                                                             const float* __restrict__ s_x, int M,
+                                                             float* __restrict__ y, int32_t* __restrict__ acc_dbg,
+                                                             int R)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int kRows = MG * 16;
+    const int nthreads = blockDim.x, nw = nthreads >> 6, nwr = nw / R;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int rr = wave % R, kw = wave / R;
+    const int nb = (int)(K >> 7), nkt = nb >> 2, nph = nkt / nwr;
+    const int64_t nrt = (N + 15) >> 4;
+    const int64_t rt_real = (int64_t)blockIdx.x * R + rr;
+    const int64_t rt = rt_real < nrt ? rt_real : nrt - 1;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+    const int kp = nwr * kTileK;                                     // k per phase
+    const int half = kp / 2;                                         // bytes of a row's first-half region
+    const int xrow = kp + 16;                                        // staged bytes per activation row
+
+    // Staging assignment: 32-byte word c of this thread is row (u / per_row), word (u % per_row)
+    // of the phase.  A staged row holds the first 16 bytes (in the decoded order) of its words
+    // in one region and their second 16 bytes in the next, so each staging write instruction
+    // covers consecutive 16-byte slots.  per_row = 16*nwr is a power of two.
+    const int per_row = kp / 32, lg = 31 - __builtin_clz((unsigned)per_row), chunks = kRows * per_row;
+    int xsrc[XC], xdst[XC];
+#pragma unroll
+    for (int c = 0; c < XC; ++c) {
+        const int u = threadIdx.x + c * nthreads;
+        const int uc = u < chunks ? u : chunks - 1;
+        const int m = uc >> lg, cc = uc & (per_row - 1);
+        const int mr = m < M ? m : M - 1;
+        xsrc[c] = (mr * (int)K + 32 * cc) >> 4;                      // in 16-byte units
+        xdst[c] = u < chunks ? m * xrow + 16 * cc : kRows * xrow;   // past the end: a dummy slot
+    }
+    const TERN_GLOBAL u32x4* qg = (const TERN_GLOBAL u32x4*)q;
+    auto load_x = [&](int ph, u32x4 (&v)[XC][2]) {
+        const int p = (ph < nph ? ph : nph - 1) * (kp >> 4);
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            v[c][0] = qg[xsrc[c] + p];
+            v[c][1] = qg[xsrc[c] + p + 1];
+        }
+    };
+    auto stage = [&](const u32x4 (&v)[XC][2]) {
+#pragma unroll
+        for (int c = 0; c < XC; ++c) {
+            const uint32_t Q[8] = {v[c][0][0], v[c][0][1], v[c][0][2], v[c][0][3],
+                                   v[c][1][0], v[c][1][1], v[c][1][2], v[c][1][3]};
+            u32x4 o0, o1;
+#pragma unroll
+            for (int d = 0; d < 4; ++d) o0[d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+            for (int d = 4; d < 8; ++d) o1[d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+            *(u32x4*)(smem + xdst[c]) = o0;
+            *(u32x4*)(smem + xdst[c] + half) = o1;
+        }
+    };
+    auto load_unit = [&](int ph, PlaneTile& t) {
+        const int kt = (ph < nph ? ph : nph - 1) * nwr + kw;
+        const int64_t wb = tile_word_base(rt, kt, nb);
+        const int64_t sb = tile_scale_base(rt, kt, nb);
+        t.nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t.sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        t.sc = ld_nt8(scales + sb + r * 4);
+    };
+
+    f32x4 acc[MG];
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) acc[mg] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const uint8_t* xw = smem + r * xrow + 16 * (kw * 16 + g);        // this lane's row r, the wave's k-tile
+    auto compute = [&](int ph, const PlaneTile& t) {
+        const int kt = ph * nwr + kw;
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq) {
+            u32x4 B[2];
+            decode_i8(t.nz[bq], t.sg[bq], B);
+            const float sc = tile_scale(t, bq) * (1.0f / 64.0f);     // decoded weights are 64*t
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg) {
+                const uint8_t* qa = xw + mg * 16 * xrow + bq * 64;     // word kw*16 + bq*4 + g
+                i32x4 d = {0, 0, 0, 0};
+                d = mfma_i8(*(const u32x4*)(qa), B[0], d);
+                d = mfma_i8(*(const u32x4*)(qa + half), B[1], d);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[mg][e] = __builtin_fmaf(sc, (float)d[e], acc[mg][e]);
+                if constexpr (kDbg) {
+                    const int64_t n = rt_real * kTileRows + r;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = mg * 16 + 4 * g + e;
+                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kt * 4 + bq] = d[e] >> 6;
+                    }
+                }
+            }
+        }
+    };
+
+    // one activation register set, refilled with the next phase right after it is staged
+    // (the next phase's load latency overlaps this phase's compute), and two unit slots.
+    // The loop body is one phase with no branch inside, so the refill stays where it is
+    // issued (its use is in the next iteration) instead of being sunk next to its use.
+    u32x4 xa[XC][2];
+    PlaneTile ta, tb;
+    load_x(0, xa);
+    __builtin_amdgcn_sched_barrier(0);
+    load_unit(0, ta);
+    load_unit(1, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    for (int ph = 0; ph < nph; ++ph) {
+        stage(xa);
+        __syncthreads();
+        load_x(ph + 1, xa);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ph, ta);
+        ta = tb;                           // the next phase's unit, loaded a phase earlier
+        load_unit(ph + 2, tb);
+        __syncthreads();                   // every wave has read this phase
+    }
+
+    // partials [wave][MG][4][64] in the staging area, summed over the nwr waves of each row tile
+    float* red = (float*)smem;
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) red[((wave * MG + mg) * 4 + e) * 64 + lane] = acc[mg][e];
+    __syncthreads();
+    const int nout = R * MG * 4 * 64;
+    for (int o = threadIdx.x; o < nout; o += nthreads) {
+        const int l = o & 63, e = (o >> 6) & 3, mg = (o >> 8) % MG, orr = (o >> 8) / MG;
+        const int m = mg * 16 + 4 * (l >> 4) + e;
+        const int64_t n = ((int64_t)blockIdx.x * R + orr) * kTileRows + (l & 15);
+        if (m < M && n < N) {
+            float sum = 0.f;
+            for (int w = 0; w < nwr; ++w) sum += red[(((w * R + orr) * MG + mg) * 4 + e) * 64 + l];
+            y[(int64_t)m * N + n] = s_x[m] * sum;
+        }
+    }
+}
+
+struct PfSmall {
+    int MG, R, nw, XC;
+    int64_t grid;
+    size_t lds;
+};
+
+// Launch configuration of prefill_small_kernel, or false when it does not
+// apply: nwr waves per row tile (the largest of 8, 4, 2 that divides the
+// k-tiles and lets a phase of MG*16 activation rows fit in LDS), R row tiles
+// per workgroup so that the grid covers the CUs about once (at most 12 waves,
+// so that every instance keeps its registers without spills).
+static bool pick_pf_small(int64_t N, int64_t K, int64_t M, PfSmall& c)
+{
+    if (K % kTileK != 0 || M < 17 || M > 64 || N < 1) return false;
+    c.MG = (int)((M + 15) / 16);
+    const int64_t nkt = K / kTileK, rows = 16 * c.MG;
+    const int64_t nrt = (N + 15) / 16, cus = device_cus();
+    for (int nwr : {8, 4, 2}) {
+        if (nkt % nwr != 0) continue;
+        const size_t stage_bytes = (size_t)rows * (nwr * kTileK + 16) + nwr * kTileK / 2 + 16;   // + dummy slot
+        if (stage_bytes > (size_t)150 * 1024) continue;
+        // about one workgroup per CU, and at least rows/32 row tiles per workgroup so that a
+        // thread stages at most 8 activation chunks of a phase (rows/(4R) of them)
+        int64_t R = (nrt + cus - 1) / cus;
+        if (R < (rows + 31) / 32) R = (rows + 31) / 32;
+        if (R * nwr > 12) continue;
+        c.R = (int)R;
+        c.nw = (int)(R * nwr);
+        c.grid = (nrt + R - 1) / R;
+        const int64_t chunks = rows * (nwr * kTileK / 32);
+        const int64_t xc = (chunks + 64 * c.nw - 1) / (64 * c.nw);
+        if (xc > 8) continue;
+        c.XC = xc <= 2 ? 2 : (xc <= 4 ? 4 : (xc <= 6 ? 6 : 8));
+        const size_t red_bytes = (size_t)c.nw * c.MG * 4 * 64 * 4;
+        c.lds = stage_bytes > red_bytes ? stage_bytes : red_bytes;
+        return c.lds <= (size_t)kCuLds;
+    }
+    return false;
+}
+
+template <int MG, int XC>
+static hipError_t launch_pf_small_x(const PfSmall& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
+                                    const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    if (acc)
+        prefill_small_kernel<MG, XC, true><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(
+            packed, N, K, q, s_x, (int)M, y, acc, c.R);
+    else
+        prefill_small_kernel<MG, XC, false><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(
+            packed, N, K, q, s_x, (int)M, y, acc, c.R);
+    return hipGetLastError();
+}
+
+template <int MG>
+static hipError_t launch_pf_small_mg(const PfSmall& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
+                                     const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    switch (c.XC) {
+    case 2: return launch_pf_small_x<MG, 2>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 4: return launch_pf_small_x<MG, 4>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 6: return launch_pf_small_x<MG, 6>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    default: return launch_pf_small_x<MG, 8>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    }
+}
+
+static hipError_t launch_pf_small(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
+                                  int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    PfSmall c;
+    if (!pick_pf_small(N, K, M, c)) return hipErrorNotSupported;
+    switch (c.MG) {
+    case 2: return launch_pf_small_mg<2>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 3: return launch_pf_small_mg<3>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    default: return launch_pf_small_mg<4>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    }
+}
+
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
@@ -455,6 +690,12 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
         // 51 us vs 59 us, down M = 512 65 us vs 132 us.
         if (M >= 1024) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
         return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
+    }
+    {   // 17 <= M <= 64: K split across the waves of a workgroup.  Measured on the 8B
+        // shapes against the paths below: gate M = 64 16.2 us vs 24.6 us, down M = 64
+        // 26.4 us vs 30.5 us, gate M = 32 10.6 us vs 12.5 us, gate M = 48 13.0 us vs 18.3 us.
+        const hipError_t e = launch_pf_small(packed, N, K, q, s_x, M, y, acc, stream);
+        if (e != hipErrorNotSupported) return e;
     }
     // Below M = 128 the prefill kernel's time is set by its per-block latency
     // (about 0.62 us per 128-k block on the 8B shapes, nearly independent of

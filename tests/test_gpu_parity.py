@@ -360,11 +360,32 @@ def test_prefill_exact_on_power_of_two_scales(tw):
     assert np.array_equal(y, want)
 
 
-@pytest.mark.parametrize("n,k,m", [(300, 8192, 64), (100, 4096, 37), (37, 12288, 17)])
+@pytest.mark.parametrize("n,k,m", [(300, 8192, 64), (100, 4096, 37), (37, 12288, 17), (1000, 4096, 48),
+                                   (5000, 12288, 33), (77, 1536, 64)])
+def test_prefill_small_m_split_k(tw, n, k, m):
+    """17 <= M <= 64 (K a multiple of 512): K split across the waves of a
+    workgroup, activations staged a phase at a time, each decoded weight tile
+    reused over the 16-row groups (ragged last group and last row tile):
+    block sums bit for bit, y against the oracle, and the production
+    instance (no block sums) the same bytes."""
+    import torch
+    t, s, x = gen(n, k, m, seed=n + 7 * m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
+    y2 = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
+    assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("n,k,m", [(300, 8192, 100), (100, 4096, 16), (37, 12288, 9)])
 def test_prefill_small_m_through_gemv_slices(tw, n, k, m):
-    """Below M = 128 with many 128-k blocks the call runs the int8 GEMV on
-    16-row slices of q (ragged last slice): block sums bit for bit, y against
-    the oracle."""
+    """Outside the split-K kernel's range with many 128-k blocks (M <= 16, or
+    65 <= M < 128) the call runs the int8 GEMV on 16-row slices of q (ragged
+    last slice): block sums bit for bit, y against the oracle."""
     import torch
     t, s, x = gen(n, k, m, seed=n + 7 * m)
     q0, s0 = oracle.quantize_i8(x)
