@@ -243,11 +243,12 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     const int nrt = (int)((N + 15) >> 4);
     // row tiles b, b + G, b + 2G, ... (G = grid): at any moment the
     // workgroups read neighbouring tiles, spread over all memory channels
-    const int rt0 = (int)blockIdx.x, G = (int)gridDim.x;
-    const int rn = (nrt - 1 - rt0) / G + 1;                 // row tiles of this workgroup
-    const int units = rn * nkt;
+    const int rt0 = (int)blockIdx.x;
+    int G = (int)gridDim.x;
+    // G comes from the dispatch's implicit arguments: read it together with
+    // the kernel arguments, not after the unit search below needs it
+    asm volatile("" : "+s"(G));
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
-    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
     const int xrow_bytes = kI8 ? (int)K + 16 : ((int)K + 8) * 2;   // staged bytes per activation row
     float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [unit + 1 spare][NI][64]
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     for (int c = 0; c < XC; ++c) {
         const int u = threadIdx.x + c * nthreads;
         const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, cc = uc - m * per_row;
+        const int m = MT == 1 ? 0 : uc / per_row, cc = uc - m * per_row;   // MT = 1 runs M = 1 only
 #pragma unroll
         for (int h = 0; h < kLoadsPerChunk; ++h)
             xv[c][h] = xg[((int64_t)m * per_row + cc) * kLoadsPerChunk + h];
@@ -271,24 +272,51 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     // keep the activation loads ahead of the unit loads: waiting for them
     // must not wait for the weights
     __builtin_amdgcn_sched_barrier(0);
+    // Unit j = wave + i*nw of this wave is (row tile lrt, k-tile kt) with
+    // j = lrt*nkt + kt, found by subtraction (j < 64: at most R - 1 steps, in
+    // scalar registers) so that no division sits between the kernel's start
+    // and its first loads.  A unit past the workgroup's last row tile loads
+    // k-tile nkt - 1 of its first row tile; its partial goes to the spare slot.
+    int ulrt[U], ukt[U];
+    bool uok[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        int lrt = 0, kt = wave + i * nw;
+        while (kt >= nkt) {
+            kt -= nkt;
+            ++lrt;
+        }
+        uok[i] = rt0 + lrt * G < nrt;
+        ulrt[i] = uok[i] ? lrt : 0;
+        ukt[i] = uok[i] ? kt : nkt - 1;
+    }
     PlaneTile t[U];
-    auto load_unit = [&](int i) {
-        int j = wave + i * nw;
-        j = j < units ? j : units - 1;
-        const int lrt = j / nkt, kt = j - lrt * nkt;
-        const int64_t wb = tile_word_base(rt0 + lrt * G, kt, nb);
-        const int64_t sb = tile_scale_base(rt0 + lrt * G, kt, nb);
+    // plane words first: the scale region's offset is computed after they are requested
+    auto load_words = [&](int i) {
+        const int64_t wb = tile_word_base(rt0 + ulrt[i] * G, ukt[i], nb);
         t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
         t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
-        t[i].sc = ld_nt8(scales + sb + r * 4);
+    };
+    auto load_scales = [&](int i) {
+        const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+        t[i].sc = ld_nt8(scales + tile_scale_base(rt0 + ulrt[i] * G, ukt[i], nb) + r * 4);
+    };
+    auto load_unit = [&](int i) {
+        load_words(i);
+        load_scales(i);
     };
     // Only the first unit is requested before the activations are staged:
     // requests queue in the memory system in issue order, and x (needed by
     // every unit) would otherwise wait behind all of the weights.  The
     // other units are requested right after the barrier and stream in while
     // the first one is computed.
-    load_unit(0);
+    load_words(0);
     __builtin_amdgcn_sched_barrier(0);
+    load_scales(0);
+    __builtin_amdgcn_sched_barrier(0);
+    int rn = 0;                                             // row tiles of this workgroup (at most R)
+    for (int rt = rt0; rt < nrt; rt += G) ++rn;
+    const int units = rn * nkt;
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         if constexpr (kI8) {
@@ -315,14 +343,12 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
 
     const int mrow = r < M ? r : M - 1;
     const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
-    // every unit is computed (a unit past the end repeats the last one and
+    // every unit is computed (a unit past the end repeats a real one and
     // leaves its partial in the spare slot after the real ones), so no load
     // is consumed behind a branch
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        const int j = wave + i * nw;
-        const int jc = j < units ? j : units - 1;
-        const int lrt = jc / nkt, kt = jc - lrt * nkt;
+        const int lrt = ulrt[i], kt = ukt[i];
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kI8) {
             const int64_t n = (int64_t)(rt0 + lrt * G) * kTileRows + r;
@@ -337,7 +363,7 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
                 const float sc = tile_scale(t[i], bq) * (1.0f / 64.0f);   // decoded weights are 64*t
 #pragma unroll
                 for (int q = 0; q < NI; ++q) acc[q] = __builtin_fmaf(sc, (float)d[q], acc[q]);
-                if (acc_dbg != nullptr && j < units) {
+                if (acc_dbg != nullptr && uok[i]) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const int m = 4 * g + q;
@@ -348,7 +374,7 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
         } else {
             bf16_tile<MT>(t[i], (const uint16_t*)xrow + kt * kTileK, 4, acc);
         }
-        const int slot = j < units ? j : units;
+        const int slot = uok[i] ? lrt * nkt + kt : units;
 #pragma unroll
         for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];   // all lanes: no branch
         __builtin_amdgcn_sched_barrier(0);   // unit i+1's decode waits for its own loads only
