@@ -396,6 +396,90 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     }
 }
 
+// M = 1, bf16 activations: the one-pass split (units of 16 rows x 512 k, R
+// row tiles per workgroup, U units per wave, partials summed in k-tile
+// order), but every wave stages only the activations of its own units.  A
+// unit's 512 bf16 of x are one 16-byte chunk per lane, requested just before
+// the unit's plane words and written to the wave's own LDS slot, so no
+// workgroup barrier stands between the loads and the compute: a wave
+// computes a unit as soon as its own slice and planes have arrived.  Only
+// the partial sums meet at a barrier.
+template <int U>
+__global__ __launch_bounds__(1024) void gemv_m1_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                       const uint16_t* __restrict__ x, float* __restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int kSlice = kTileK * 2;                                // bytes of x per unit
+    const int nw = (int)(blockDim.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7), nkt = nb >> 2;
+    const int nrt = (int)((N + 15) >> 4);
+    const int rt0 = (int)blockIdx.x;
+    int G = (int)gridDim.x;
+    asm volatile("" : "+s"(G));                                       // read with the kernel arguments
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    uint8_t* xs = smem + (size_t)wave * U * kSlice;                   // this wave's slices
+    float* red = (float*)(smem + (size_t)nw * U * kSlice);            // [unit + 1 spare][64]
+
+    // unit positions by subtraction, as in the one-pass kernel
+    int ulrt[U], ukt[U];
+    bool uok[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        int lrt = 0, kt = wave + i * nw;
+        while (kt >= nkt) {
+            kt -= nkt;
+            ++lrt;
+        }
+        uok[i] = rt0 + lrt * G < nrt;
+        ulrt[i] = uok[i] ? lrt : 0;
+        ukt[i] = uok[i] ? kt : nkt - 1;
+    }
+    PlaneTile t[U];
+    u32x4 xv[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        xv[i] = xg[ukt[i] * (kSlice / 16) + lane];
+        const int64_t wb = tile_word_base(rt0 + ulrt[i] * G, ukt[i], nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+        t[i].sc = ld_nt8(scales + tile_scale_base(rt0 + ulrt[i] * G, ukt[i], nb) + r * 4);
+    __builtin_amdgcn_sched_barrier(0);
+    int rn = 0;                                                       // row tiles of this workgroup
+    for (int rt = rt0; rt < nrt; rt += G) ++rn;
+    const int units = rn * nkt;
+
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        // a wave's LDS accesses run in order: its own write is seen by its reads below
+        *(u32x4*)(xs + i * kSlice + 16 * lane) = xv[i];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16_tile<1>(t[i], (const uint16_t*)(xs + i * kSlice + 64 * g), 4, acc);
+        const int slot = uok[i] ? ulrt[i] * nkt + ukt[i] : units;
+        red[slot * 64 + lane] = acc[0];
+        __builtin_amdgcn_sched_barrier(0);   // unit i+1's work waits for its own loads only
+    }
+    __syncthreads();
+
+    for (int e = threadIdx.x; e < rn * 16; e += (int)blockDim.x) {
+        const int n = e & 15, lrt = e >> 4;
+        const int64_t row = (int64_t)(rt0 + lrt * G) * kTileRows + n;
+        if (row < N) {
+            const float* pr = red + (int64_t)lrt * nkt * 64 + n;
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * 64];
+            y[row] = sum;
+        }
+    }
+}
+
 // Two-phase variant of the one-pass kernel for activations too large for
 // LDS (large K at M >= 5 bf16, or M >= 13 int8): one row tile per
 // workgroup, nw = nkt / 2 waves with two units each, unit i of every wave in
@@ -822,7 +906,8 @@ static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const u
 // for U = 1..4 (the occupancy query has the last word).
 static OneShotShape oneshot_shape(int64_t K, bool i8)
 {
-    return OneShotShape{i8 ? K + 16 : (K + 8) * 2, i8 ? K : 2 * K, i8 ? 32 : 16, {0, 8, 7, 6, 5}};
+    return OneShotShape{i8 ? K + 16 : (K + 8) * 2, i8 ? K : 2 * K, i8 ? 32 : 16, {0, 8, 7, 6, 5},
+                        i8 ? 0 : kTileK * 2};
 }
 
 // the one-pass path for M <= 16 when it applies; hipErrorNotSupported otherwise
@@ -831,11 +916,26 @@ bool gemv_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
     return pick_oneshot(N, K, M, oneshot_shape(K, i8), c);
 }
 
+static hipError_t m1_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
+                              const uint16_t* x, float* y)
+{
+#define TERN_M1_CASE(UU)                                                                                           \
+    if (c.U == UU) {                                                                                               \
+        if (!oneshot_resident(gemv_m1_kernel<UU>, c)) return hipErrorNotSupported;                                 \
+        gemv_m1_kernel<UU><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, y);        \
+        return hipGetLastError();                                                                                  \
+    }
+    TERN_M1_CASE(1) TERN_M1_CASE(2) TERN_M1_CASE(3) TERN_M1_CASE(4)
+#undef TERN_M1_CASE
+    return hipErrorNotSupported;
+}
+
 static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
                                  int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     OneShot c;
     if (!pick_oneshot(N, K, M, oneshot_shape(K, i8), c)) return hipErrorNotSupported;
+    if (!i8 && M == 1) return m1_dispatch(c, stream, packed, N, K, (const uint16_t*)x, y);
     const int m = (int)M;
     // 8 activation chunks per thread are instantiated for the MT = 16 kernel
     // only, which computes the same rows as MT = 4 (4 per lane group)

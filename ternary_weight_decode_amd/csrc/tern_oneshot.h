@@ -3,9 +3,10 @@
 //
 // A unit is one 16-row tile x one 512-k tile.  A workgroup owns R row tiles
 // (every R-th of the grid) and its waves take U units each, all loads issued
-// up front; activations are staged once in LDS and each unit leaves its fp32
-// partial in LDS, summed afterwards in k-tile order.  The whole grid must be
-// resident in one round where a split allows it.
+// up front; activations are staged once in LDS (at M = 1 in bf16: each wave
+// only the slices of its own units) and each unit leaves its fp32 partial in
+// LDS, summed afterwards in k-tile order.  The whole grid must be resident in
+// one round where a split allows it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -42,6 +43,8 @@ struct OneShotShape {
     int64_t x_src_bytes;      // bytes of one activation row in global memory
     int64_t chunk_bytes;      // activation bytes one thread loads per chunk
     int64_t waves_per_simd[5];// waves of U = 1..4 units that fit on a SIMD (registers)
+    int64_t m1_slice_bytes;   // > 0: at M = 1 every wave stages only the activation slices of its
+                              // own units (this many bytes per unit) instead of the whole row
 };
 
 // R row tiles per workgroup is chosen to minimise the largest number of
@@ -63,8 +66,12 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     const int64_t nkt = K / 512, nrt = (N + 15) / 16;
     const int64_t cus = device_cus();
     const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    const size_t x_lds = (size_t)(M * s.x_row_bytes);
-    auto lds_of = [&](int64_t units) { return x_lds + (size_t)(units + 1) * ni * 64 * 4; };
+    const bool slices = M == 1 && s.m1_slice_bytes > 0;
+    auto lds_of = [&](int64_t units) {
+        const int64_t U = oneshot_u(units), nw = (units + U - 1) / U;
+        const size_t x_lds = slices ? (size_t)(nw * U * s.m1_slice_bytes) : (size_t)(M * s.x_row_bytes);
+        return x_lds + (size_t)(units + 1) * ni * 64 * 4;
+    };
     int64_t best_max = -1, best_dist = 0;
     c.R = 0;
     for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
@@ -103,7 +110,7 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     c.U = (int)oneshot_u(units);
     c.nw = (int)((units + c.U - 1) / c.U);
     c.grid = (nrt + c.R - 1) / c.R;
-    const int64_t xc = (M * (s.x_src_bytes / s.chunk_bytes) + 64 * c.nw - 1) / (64 * c.nw);
+    const int64_t xc = slices ? 1 : (M * (s.x_src_bytes / s.chunk_bytes) + 64 * c.nw - 1) / (64 * c.nw);
     // 8 chunks run on the MT = 16 kernels, whose partials hold 4 rows per
     // lane group: not for M <= 2, whose partial area is sized for 1 or 2
     if (xc > 8 || (xc > 4 && M <= 2)) return false;

@@ -37,11 +37,15 @@ def test_picker_invariants(kind):
         assert c["waves"] * c["U"] >= units > (c["waves"] - 1) * c["U"], where   # every unit owned, no idle wave
         assert c["grid"] == (nrt + c["R"] - 1) // c["R"], where
         assert c["lds"] <= CU_LDS, where
-        xrow = k + 16 if i8 else (k + 8) * 2
         ni = 1 if m == 1 else (2 if m == 2 else 4)
-        assert c["lds"] == m * xrow + (units + 1) * ni * 64 * 4, where
-        chunk = 32 if i8 else 16
-        assert c["XC"] * 64 * c["waves"] * chunk >= m * k * (1 if i8 else 2), where       # x fully staged
+        if kind == "ternary_bf16" and m == 1:
+            # each wave stages the 1 KB activation slice of each of its units
+            assert c["XC"] == 1 and c["lds"] == c["waves"] * c["U"] * 1024 + (units + 1) * 64 * 4, where
+        else:
+            xrow = k + 16 if i8 else (k + 8) * 2
+            assert c["lds"] == m * xrow + (units + 1) * ni * 64 * 4, where
+            chunk = 32 if i8 else 16
+            assert c["XC"] * 64 * c["waves"] * chunk >= m * k * (1 if i8 else 2), where       # x fully staged
         assert c["MT"] >= m and (c["XC"] < 8 or c["MT"] == 16), where
         if c["XC"] == 8:
             assert m > 2, where          # the MT = 16 partial area needs 4 rows per lane group
