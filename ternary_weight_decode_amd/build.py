@@ -5,6 +5,12 @@
 Sources are compiled in parallel into ``_build/`` and linked into
 ``ternary_weight_decode_amd/libtern.so``.  Only gfx950 code is generated.
 Packed-FP32 VALU instructions are disabled for every device compile.
+Kernel arguments (with the dispatch's grid and workgroup sizes) are
+preloaded into scalar registers at wave launch, so a kernel's first
+instructions do not wait on a scalar memory load; each kernel also carries
+the compiler's fallback entry that loads them where the firmware does not
+preload.  On the 8B token-equivalent (145 dependent launches) this measured
+793.5 us against 834.1 us per step.
 """
 from __future__ import annotations
 
@@ -21,7 +27,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["tern_api.hip", "tern_pack.hip", "tern_quant.hip", "tern_gemv.hip", "tern_head.hip", "tern_prefill.hip", "tern_chain.hip", "tern5.hip", "tern_peak.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
-         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-mllvm", "-amdgpu-kernarg-preload-count=16"]
 
 
 def _compile(src: str) -> str:
