@@ -271,7 +271,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
                      "timing": "HIP events around back-to-back launches of the step's ternary chain"})
     else:
         base.update({"traffic": measured_traffic(root, args.compose),
-                     "kernel": "gemv_oneshot_kernel<false,1,*,*> (tern_gemv, M=1)",
+                     "kernel": "gemv_m1_kernel<U> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),
                      "launches_per_step": n_tern,
