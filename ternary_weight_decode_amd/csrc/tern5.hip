@@ -294,11 +294,12 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
 }
 
 // Two-phase variant for activations larger than LDS (large K at bf16
-// M >= 6, int8 M >= 13): one row tile per workgroup, nkt / 2 waves with two
-// units each, unit i of every wave in half i of K; both halves of x loaded
-// into registers up front, staged one half at a time (as the ternary
-// two-phase kernel).  16 MFMA activation rows.
-template <bool kI8, int XC>
+// M >= 6, int8 M >= 13): RT row tiles per workgroup (1, or 2 for bf16 when
+// one tile's waves would each stage more than 8 chunks), nkt / 2 waves per
+// row tile with two units each, unit i of every wave in half i of K; both
+// halves of x loaded into registers up front, staged one half at a time (as
+// the ternary two-phase kernel).  16 MFMA activation rows.
+template <bool kI8, int XC, int RT>
 __global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
                                                             const void* __restrict__ x, const float* __restrict__ s_x,
                                                             int M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
@@ -307,20 +308,24 @@ __global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __res
     constexpr int NI = 4;
     constexpr int kChunkBytes = kI8 ? 32 : 16;
     constexpr int kLoadsPerChunk = kChunkBytes / 16;
-    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = nkt / 2
+    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = RT * nkt / 2
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int nkt = (int)(K >> 9);
-    const int64_t rt = blockIdx.x;
+    const int nwh = nw / RT;                                          // waves per row tile (nkt / 2)
+    const int lrt = wave / nwh, lw = wave - lrt * nwh;               // this wave's row tile and local wave
+    // a row tile past the last one loads the workgroup's first tile and stores nothing
+    const int64_t rt_out = (int64_t)blockIdx.x * RT + lrt;
+    const int64_t rt = rt_out < (N + 15) / 16 ? rt_out : (int64_t)blockIdx.x * RT;
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint32_t* scales = (const TERN_GLOBAL uint32_t*)(packed + t5_plane_bytes(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
-    const int pk = nw * kTileK;                                      // k per half
+    const int pk = nwh * kTileK;                                     // k per half
     const int xrow_bytes = kI8 ? pk + 16 : (pk + 8) * 2;
-    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [nkt][NI][64]
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [RT * nkt][NI][64]
     // chunk indices past the end store to a slot after the partials (the
     // second half is staged after the first units' partials are written)
-    const int dummy = M * xrow_bytes + nkt * NI * 64 * 4;
+    const int dummy = M * xrow_bytes + RT * nkt * NI * 64 * 4;
 
     const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);
     const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
@@ -356,24 +361,24 @@ __global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __res
     const int mrow = r < M ? r : M - 1;
     const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
     auto compute = [&](int i) {
-        const int kt = wave + i * nw;
+        const int kt = lw + i * nwh;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kI8) {
-            const uint8_t* qt = xrow + wave * kTileK;
+            const uint8_t* qt = xrow + lw * kTileK;
             tile5_i8<16>(t[i], [&](int jj, int h) { return *(const u32x4*)(qt + kBlockK * jj + 16 * h); }, acc,
-                         acc_dbg, N, M, rt * kTileRows + r, (int)(K >> 8), 2 * kt, g);
+                         acc_dbg, N, M, rt_out * kTileRows + r, (int)(K >> 8), 2 * kt, g);
         } else {
-            tile5_bf16<16>(t[i], (const uint16_t*)xrow + wave * kTileK, acc);
+            tile5_bf16<16>(t[i], (const uint16_t*)xrow + lw * kTileK, acc);
         }
 #pragma unroll
-        for (int q = 0; q < NI; ++q) red[(kt * NI + q) * 64 + lane] = acc[q];
+        for (int q = 0; q < NI; ++q) red[((lrt * nkt + kt) * NI + q) * 64 + lane] = acc[q];
     };
 
-    t[0] = load_tile5(words, scales, rt, wave, nkt, r, g);
+    t[0] = load_tile5(words, scales, rt, lw, nkt, r, g);
     __builtin_amdgcn_sched_barrier(0);
     stage(0);
     __syncthreads();
-    t[1] = load_tile5(words, scales, rt, wave + nw, nkt, r, g);
+    t[1] = load_tile5(words, scales, rt, lw + nwh, nkt, r, g);
     __builtin_amdgcn_sched_barrier(0);
     compute(0);
     __syncthreads();                       // every wave has read half 0
@@ -383,13 +388,14 @@ __global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __res
     __syncthreads();
 
     const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
-    for (int e = threadIdx.x; e < NI * 64; e += nthreads) {
-        const int l = e & 63, q = e >> 6;
+    for (int e = threadIdx.x; e < RT * NI * 64; e += nthreads) {
+        const int l = e & 63, q = (e >> 6) % NI, et = (e >> 6) / NI;
         const int m = 4 * (l >> 4) + q, n = l & 15;
-        const int64_t row = rt * kTileRows + n;
+        const int64_t row = ((int64_t)blockIdx.x * RT + et) * kTileRows + n;
         if (l < lanes_used && m < M && row < N) {
+            const float* pr = red + ((int64_t)et * nkt * NI + q) * 64 + l;
             float sum = 0.f;
-            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * NI * 64];
             y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
         }
     }
@@ -497,24 +503,32 @@ bool gemv5_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
     return pick_oneshot(N, K, M, s, c);
 }
 
-// two-phase configuration (gemv5_phased_kernel); false when it does not apply
+// two-phase configuration (gemv5_phased_kernel); false when it does not
+// apply.  One row tile per workgroup, two (bf16) when one tile's waves would
+// each stage more than 8 chunks of a half of x (the 8B fused gate|up at
+// M = 9..16, whose x leaves no room for a one-pass split).
 bool gemv5_phased_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
 {
     if (K % kTileK != 0 || M < 1 || M > 16 || N < 1) return false;
     const int64_t nkt = K / kTileK;
     if (nkt % 2 != 0 || nkt / 2 > 16 || nkt < 2) return false;
-    c.R = 1;
-    c.U = 2;
-    c.nw = (int)(nkt / 2);
-    c.grid = (N + 15) / 16;
-    c.rounds = true;
-    const int64_t pk = c.nw * kTileK;
+    const int64_t pk = nkt / 2 * kTileK;
     const int64_t chunks = M * pk * (i8 ? 1 : 2) / (i8 ? 32 : 16);
-    const int64_t xc = (chunks + 64 * c.nw - 1) / (64 * c.nw);   // M (bf16) or M / 4 (int8)
-    if (xc > (i8 ? 4 : 8)) return false;
-    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
-    c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)nkt * 4 * 64 * 4 + 32;   // + dummy slot
-    return c.lds <= (size_t)kCuLds;
+    for (int R = 1; R <= (i8 ? 1 : 2); ++R) {
+        const int64_t nw = R * nkt / 2;
+        if (nw > 16) break;
+        const int64_t xc = (chunks + 64 * nw - 1) / (64 * nw);   // M / R (bf16) or M / 4 (int8)
+        if (xc > (i8 ? 4 : 8)) continue;
+        c.R = R;
+        c.U = 2;
+        c.nw = (int)nw;
+        c.grid = ((N + 15) / 16 + R - 1) / R;
+        c.rounds = true;
+        c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+        c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)R * nkt * 4 * 64 * 4 + 32;   // + dummy
+        return c.lds <= (size_t)kCuLds;
+    }
+    return false;
 }
 
 template <bool kI8>
@@ -523,16 +537,17 @@ static hipError_t launch_gemv5_phased(const uint8_t* packed, int64_t N, int64_t 
 {
     OneShot c;
     if (!gemv5_phased_config(N, K, M, kI8, c)) return hipErrorNotSupported;
-#define TERN5_PHASED_CASE(XX)                                                                                  \
-    if (c.XC == XX) {                                                                                          \
-        if (!oneshot_resident(gemv5_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;                  \
-        gemv5_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(              \
+#define TERN5_PHASED_CASE(XX, RR)                                                                              \
+    if (c.XC == XX && c.R == RR) {                                                                             \
+        if (!oneshot_resident(gemv5_phased_kernel<kI8, XX, RR>, c)) return hipErrorNotSupported;              \
+        gemv5_phased_kernel<kI8, XX, RR><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(          \
             packed, N, K, x, s_x, (int)M, y, acc);                                                             \
         return hipGetLastError();                                                                              \
     }
-    TERN5_PHASED_CASE(1) TERN5_PHASED_CASE(2) TERN5_PHASED_CASE(4)
+    TERN5_PHASED_CASE(1, 1) TERN5_PHASED_CASE(2, 1) TERN5_PHASED_CASE(4, 1)
     if constexpr (!kI8) {
-        TERN5_PHASED_CASE(8)
+        TERN5_PHASED_CASE(8, 1)
+        TERN5_PHASED_CASE(8, 2)   // two row tiles: only above 8 chunks for one
     }
 #undef TERN5_PHASED_CASE
     return hipErrorNotSupported;

@@ -481,13 +481,14 @@ __global__ __launch_bounds__(1024) void gemv_m1_kernel(const uint8_t* __restrict
 }
 
 // Two-phase variant of the one-pass kernel for activations too large for
-// LDS (large K at M >= 5 bf16, or M >= 13 int8): one row tile per
-// workgroup, nw = nkt / 2 waves with two units each, unit i of every wave in
-// half i of K.  Both halves of x are loaded into registers up front (first
-// in the memory queue, as in the one-pass kernel); half 0 is staged and its
-// units computed, then half 1 replaces it in LDS.  Partials are summed in
-// k-tile order (deterministic).  16 MFMA activation rows (any M <= 16).
-template <bool kI8, int XC>
+// LDS (large K at M >= 5 bf16, or M >= 13 int8): RT row tiles per workgroup
+// (1, or 2 when one tile's waves would each stage more than 8 activation
+// chunks), nkt / 2 waves per row tile with two units each, unit i of every
+// wave in half i of K.  Both halves of x are loaded into registers up front
+// (first in the memory queue, as in the one-pass kernel); half 0 is staged
+// and its units computed, then half 1 replaces it in LDS.  Partials are summed
+// in k-tile order (deterministic).  16 MFMA activation rows (any M <= 16).
+template <bool kI8, int XC, int RT>
 __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
                                                            const void* __restrict__ x, const float* __restrict__ s_x,
                                                            int M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
@@ -496,20 +497,25 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     constexpr int NI = 4;
     constexpr int kChunkBytes = kI8 ? 32 : 16;
     constexpr int kLoadsPerChunk = kChunkBytes / 16;
-    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = nkt / 2
+    const int nthreads = blockDim.x, nw = nthreads >> 6;   // nw = RT * nkt / 2
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int nb = (int)(K >> 7), nkt = nb >> 2;
-    const int64_t rt = blockIdx.x;
+    const int nwh = nw / RT;                                          // waves per row tile (nkt / 2)
+    const int lrt = wave / nwh, lw = wave - lrt * nwh;               // this wave's row tile and local wave
+    // rows of row tile rt_out; a tile past the last one (odd row-tile count)
+    // loads the workgroup's first tile and stores nothing
+    const int64_t rt_out = (int64_t)blockIdx.x * RT + lrt;
+    const int64_t rt = rt_out < (N + 15) / 16 ? rt_out : (int64_t)blockIdx.x * RT;
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
-    const int pk = nw * kTileK;                                      // k per half
+    const int pk = nwh * kTileK;                                     // k per half
     const int xrow_bytes = kI8 ? pk + 16 : (pk + 8) * 2;             // staged bytes per activation row
-    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [nkt + 1 spare][NI][64]
+    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [RT * nkt + 1 spare][NI][64]
     // chunk indices past the end store to a dummy slot after the partials:
     // the second half is staged after the first units' partials are written
-    const int dummy = M * xrow_bytes + (nkt + 1) * NI * 64 * 4;
+    const int dummy = M * xrow_bytes + (RT * nkt + 1) * NI * 64 * 4;
 
     const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);  // chunks per activation row in memory
     const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
@@ -530,7 +536,7 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     __builtin_amdgcn_sched_barrier(0);
     PlaneTile t[2];
     auto load_unit = [&](int i) {
-        const int kt = wave + i * nw;
+        const int kt = lw + i * nwh;
         const int64_t wb = tile_word_base(rt, kt, nb);
         const int64_t sb = tile_scale_base(rt, kt, nb);
         t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
@@ -557,17 +563,17 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     };
     const int mrow = r < M ? r : M - 1;
     const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
-    // unit i of this wave: k-tile wave + i*nw, at local k-tile `wave` of half i
+    // unit i of this wave: k-tile lw + i*nwh of its row tile, at local k-tile lw of half i
     auto compute = [&](int i) {
-        const int kt = wave + i * nw;
+        const int kt = lw + i * nwh;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (kI8) {
-            const int64_t n = rt * kTileRows + r;
+            const int64_t n = rt_out * kTileRows + r;
 #pragma unroll
             for (int bq = 0; bq < 4; ++bq) {
                 u32x4 B[2];
                 decode_i8(t[i].nz[bq], t[i].sg[bq], B);
-                const uint8_t* qa = xrow + (wave * 4 + bq) * kBlockK;
+                const uint8_t* qa = xrow + (lw * 4 + bq) * kBlockK;
                 i32x4 d = {0, 0, 0, 0};
                 d = mfma_i8(*(const u32x4*)(qa), B[0], d);
                 d = mfma_i8(*(const u32x4*)(qa + 16), B[1], d);
@@ -583,10 +589,10 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
                 }
             }
         } else {
-            bf16_tile<16>(t[i], (const uint16_t*)xrow + wave * kTileK, 4, acc);
+            bf16_tile<16>(t[i], (const uint16_t*)xrow + lw * kTileK, 4, acc);
         }
 #pragma unroll
-        for (int q = 0; q < NI; ++q) red[(kt * NI + q) * 64 + lane] = acc[q];
+        for (int q = 0; q < NI; ++q) red[((lrt * nkt + kt) * NI + q) * 64 + lane] = acc[q];
     };
 
     load_unit(0);
@@ -603,13 +609,14 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     __syncthreads();
 
     const int lanes_used = M <= 4 ? 16 : (M <= 8 ? 32 : 64);
-    for (int e = threadIdx.x; e < NI * 64; e += nthreads) {
-        const int l = e & 63, q = e >> 6;
+    for (int e = threadIdx.x; e < RT * NI * 64; e += nthreads) {
+        const int l = e & 63, q = (e >> 6) % NI, et = (e >> 6) / NI;
         const int m = 4 * (l >> 4) + q, n = l & 15;
-        const int64_t row = rt * kTileRows + n;
+        const int64_t row = ((int64_t)blockIdx.x * RT + et) * kTileRows + n;
         if (l < lanes_used && m < M && row < N) {
+            const float* pr = red + ((int64_t)et * nkt * NI + q) * 64 + l;
             float sum = 0.f;
-            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            for (int kt = 0; kt < nkt; ++kt) sum += pr[kt * NI * 64];
             y[(int64_t)m * N + row] = kI8 ? s_x[m] * sum : sum;
         }
     }
@@ -850,6 +857,15 @@ static void pick_fast(int64_t nkt, int& nw, int& tpw)
     tpw = 1;
 }
 
+// LDS of the bf16 persistent fast path: all of x plus two partial rows per wave
+static size_t fast_lds_bytes(int64_t K, int64_t M)
+{
+    int nw, tpw;
+    pick_fast((K / kBlockK + 3) / 4, nw, tpw);
+    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);   // accumulator rows of the instance (NI)
+    return (size_t)M * (K + 8) * 2 + (size_t)2 * nw * ni * 64 * 4;
+}
+
 // Workgroups that stay resident at once for this kernel instance (the grid of
 // the persistent fast path); falls back to one per row tile on any error.
 template <typename F>
@@ -954,24 +970,36 @@ static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int6
 
 // Two-phase configuration (gemv_phased_kernel): one row tile per workgroup,
 // nkt / 2 waves, half of x in LDS at a time; false when it does not apply.
+// R = 1 row tile per workgroup; R = 2 (bf16) when one tile's nkt / 2 waves
+// would each stage more than 8 chunks of a half of x and x does not fit the
+// persistent fast path either (K = 8192 at M = 9..15, which otherwise runs as
+// two row-half calls that read the weights twice).  Where the fast path fits
+// it is the faster one: 8B fused gate|up at M = 16, 14.1 us against 15.3 us
+// with two row tiles.
 static bool pick_phased(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
 {
     if (K % kTileK != 0 || M < 1 || M > 16 || N < 1) return false;
     const int64_t nkt = K / kTileK;
     if (nkt % 2 != 0 || nkt / 2 > 16 || nkt < 2) return false;
-    c.R = 1;
-    c.U = 2;
-    c.nw = (int)(nkt / 2);
-    c.grid = (N + 15) / 16;
-    c.rounds = true;
-    const int64_t pk = c.nw * kTileK;
+    const int64_t pk = nkt / 2 * kTileK;
     const int64_t chunk = i8 ? 32 : 16;
     const int64_t chunks = M * pk * (i8 ? 1 : 2) / chunk;
-    const int64_t xc = (chunks + 64 * c.nw - 1) / (64 * c.nw);   // M (bf16) or M / 4 (int8)
-    if (xc > (i8 ? 4 : 8)) return false;
-    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
-    c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)(nkt + 1) * 4 * 64 * 4 + 32;   // + dummy slot
-    return c.lds <= (size_t)kCuLds;
+    const int rmax = i8 || fast_lds_bytes(K, M) <= (size_t)kFastLds ? 1 : 2;
+    for (int R = 1; R <= rmax; ++R) {
+        const int64_t nw = R * nkt / 2;
+        if (nw > 16) break;
+        const int64_t xc = (chunks + 64 * nw - 1) / (64 * nw);   // M / R (bf16) or M / 4 (int8)
+        if (xc > (i8 ? 4 : 8)) continue;
+        c.R = R;
+        c.U = 2;
+        c.nw = (int)nw;
+        c.grid = ((N + 15) / 16 + R - 1) / R;
+        c.rounds = true;
+        c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+        c.lds = (size_t)(M * (i8 ? pk + 16 : (pk + 8) * 2)) + (size_t)(R * nkt + 1) * 4 * 64 * 4 + 32;   // + dummy
+        return c.lds <= (size_t)kCuLds;
+    }
+    return false;
 }
 
 template <bool kI8>
@@ -980,16 +1008,17 @@ static hipError_t launch_phased(const uint8_t* packed, int64_t N, int64_t K, con
 {
     OneShot c;
     if (!pick_phased(N, K, M, kI8, c)) return hipErrorNotSupported;
-#define TERN_PHASED_CASE(XX)                                                                      \
-    if (c.XC == XX) {                                                                             \
-        if (!oneshot_resident(gemv_phased_kernel<kI8, XX>, c)) return hipErrorNotSupported;       \
-        gemv_phased_kernel<kI8, XX><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(  \
-            packed, N, K, x, s_x, (int)M, y, acc);                                                \
-        return hipGetLastError();                                                                 \
+#define TERN_PHASED_CASE(XX, RR)                                                                      \
+    if (c.XC == XX && c.R == RR) {                                                                    \
+        if (!oneshot_resident(gemv_phased_kernel<kI8, XX, RR>, c)) return hipErrorNotSupported;       \
+        gemv_phased_kernel<kI8, XX, RR><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(  \
+            packed, N, K, x, s_x, (int)M, y, acc);                                                    \
+        return hipGetLastError();                                                                     \
     }
-    TERN_PHASED_CASE(1) TERN_PHASED_CASE(2) TERN_PHASED_CASE(4)
+    TERN_PHASED_CASE(1, 1) TERN_PHASED_CASE(2, 1) TERN_PHASED_CASE(4, 1)
     if constexpr (!kI8) {
-        TERN_PHASED_CASE(8)   // int8 needs M / 4 <= 4 chunks per thread
+        TERN_PHASED_CASE(8, 1)   // int8 needs M / 4 <= 4 chunks per thread
+        TERN_PHASED_CASE(8, 2)   // two row tiles: only above 8 chunks for one
     }
 #undef TERN_PHASED_CASE
     return hipErrorNotSupported;
@@ -1052,8 +1081,7 @@ hipError_t launch_gemv_bf16(const uint8_t* packed, int64_t N, int64_t K, const u
     const int64_t nkt = (K / kBlockK + 3) / 4;
     int nw, tpw;
     pick_fast(nkt, nw, tpw);
-    const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);   // accumulator rows of the instance (NI)
-    const size_t fast_lds = (size_t)M * (K + 8) * 2 + (size_t)2 * nw * ni * 64 * 4;
+    const size_t fast_lds = fast_lds_bytes(K, M);
     if (fast_lds <= (size_t)kFastLds) {
         if (M == 1) return launch_fast_mt<1>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);
         if (M == 2) return launch_fast_mt<2>(tpw, nw, fast_lds, stream, packed, N, K, x, (int)M, y);

@@ -122,6 +122,24 @@ def test_gemv5_two_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(12300, 4096, 16), (24576, 4096, 15)])
+def test_gemv5_two_phase_two_row_tiles(tw, n, k, m):
+    """bf16 M = 15..16 at K = 4096 beyond every one-pass split (the 8B fused
+    gate|up shape): the two-phase kernel with two row tiles per workgroup
+    (12300 rows: the last workgroup's second tile past the end); 12300 rows
+    against the oracle in full, the fused shape on sampled rows."""
+    c = tw.tern_gemv_config(n, k, m, "fv5_bf16_phased")
+    assert tw.tern_gemv_config(n, k, m, "fv5_bf16") is None and c is not None and c["R"] == 2
+    lv, lo, hi, x = gen(n, k, m, seed=9 * n + m)
+    y = host(tw.tern5_gemv(gpu_pack(tw, lv, lo, hi), n, k, dev(x)))
+    rows = np.arange(n) if n < 16000 else np.unique(np.r_[np.arange(0, 40), np.random.default_rng(5).choice(n, 300),
+                                                                np.arange(n - 40, n)])
+    want, _ = fv5.gemv_bf16_levels(lv[rows], lo[rows], hi[rows], x)
+    assert rel_l2(y[:, rows], want) < TOL
+    err = np.abs(y[:, rows] - want).max(axis=0) / (np.abs(want).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 def test_gemv5_deterministic_and_stream_order(tw):
     import torch
     n, k, m = 6144, 4096, 1

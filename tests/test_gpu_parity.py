@@ -545,6 +545,25 @@ def test_gemv_bf16_two_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(37, 8192, 11), (1000, 8192, 9), (4100, 8192, 15), (4096, 8192, 12)])
+def test_gemv_bf16_two_phase_two_row_tiles(tw, n, k, m):
+    """bf16 activations whose halves of K would need more than 8 chunks per
+    thread with one row tile per workgroup and whose x fits neither a
+    one-pass split nor the persistent fast path (K = 8192 at M = 9..15): the
+    two-phase kernel with two row tiles per workgroup, the weights read once.
+    37, 1000 and 4100 rows give odd row-tile counts, so the last workgroup's
+    second tile loads its first and stores nothing.  Every output against
+    the oracle."""
+    c = tw.tern_gemv_config(n, k, m, "ternary_bf16_phased")
+    assert tw.tern_gemv_config(n, k, m) is None and c is not None and c["R"] == 2
+    t, s, x = gen(n, k, m, seed=3 * n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 @pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12), (300, 12288, 13)])
 def test_gemv_bf16_three_phase(tw, n, k, m):
     """bf16 activations of more than 8 rows whose halves of K exceed LDS (the
@@ -560,12 +579,12 @@ def test_gemv_bf16_three_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
-@pytest.mark.parametrize("n,k,m", [(1000, 8192, 16), (37, 8192, 11)])
+@pytest.mark.parametrize("n,k,m", [(1000, 8192, 16), (37, 8192, 16)])
 def test_gemv_bf16_row_halves(tw, n, k, m):
     """bf16 activations of more than 8 rows that fit no one-pass, two-phase
-    or three-phase configuration (K = 8192 is not a multiple of 3 k-tiles):
-    the call runs on rows 0..7 and 8..M-1 through those kernels; every output
-    against the oracle."""
+    or three-phase configuration (K = 8192 at M = 16: half of x is 131 KB,
+    and K is not a multiple of 3 k-tiles): the call runs on rows 0..7 and
+    8..M-1 through those kernels; every output against the oracle."""
     assert tw.tern_gemv_config(n, k, m) is None and tw.tern_gemv_config(n, k, m, "ternary_bf16_phased") is None
     assert tw.tern_gemv_config(n, k, m, "ternary_bf16_phased3") is None
     assert (tw.tern_gemv_config(n, k, 8) is not None or

@@ -60,8 +60,9 @@ def test_picker_invariants(kind):
                                   "fv5_int8_phased"])
 def test_phased_picker_invariants(kind):
     """The two-phase configuration: taken only where no one-pass one fits; one
-    row tile per workgroup, nkt / 2 waves with two units each (unit i in half
-    i of K), half of the activations staged at a time."""
+    row tile per workgroup (two for bf16 when one tile's waves would each stage
+    more than 8 chunks), nkt / 2 waves per row tile with two units each (unit i
+    in half i of K), half of the activations staged at a time."""
     i8 = "int8" in kind
     taken = 0
     for n, k, m in itertools.product(NS, KS, MS):
@@ -73,15 +74,18 @@ def test_phased_picker_invariants(kind):
         where = (kind, n, k, m, c)
         assert one is None, where
         nkt = k // 512
-        assert c["R"] == 1 and c["U"] == 2 and c["waves"] * 2 == nkt and c["waves"] <= 16, where
-        assert c["grid"] == (n + 15) // 16 and c["MT"] == 16, where
-        pk = c["waves"] * 512
+        R = c["R"]
+        assert R in (1, 2) and c["U"] == 2 and c["waves"] * 2 == R * nkt and c["waves"] <= 16, where
+        assert c["grid"] == ((n + 15) // 16 + R - 1) // R and c["MT"] == 16, where
+        pk = nkt // 2 * 512
         xrow = pk + 16 if i8 else (pk + 8) * 2
-        slots = nkt + 1 if kind.startswith("ternary") else nkt         # partials (+ a spare in the ternary kernel)
+        slots = R * nkt + 1 if kind.startswith("ternary") else R * nkt   # partials (+ a spare in the ternary kernel)
         assert c["lds"] == m * xrow + slots * 4 * 64 * 4 + 32 <= CU_LDS, where   # + a dummy staging slot
         chunk = 32 if i8 else 16
         assert c["XC"] * 64 * c["waves"] * chunk >= m * pk * (1 if i8 else 2), where   # a half fully staged
         assert c["XC"] <= (4 if i8 else 8), where
+        if R == 2:   # only where one row tile's waves would stage more than 8 chunks each
+            assert not i8 and m * pk * 2 > 8 * 64 * (nkt // 2) * 16, where
     assert taken > 0
     # the shapes it exists for: down (4096 x 12288) at bf16 M = 7 and 8 and, five-level, int8 M = 16
     fam = kind.split("_")[0]
@@ -91,6 +95,21 @@ def test_phased_picker_invariants(kind):
     if fam == "fv5":
         c = tw.tern_gemv_config(4096, 12288, 16, "fv5_int8_phased")
         assert c is not None and c["waves"] == 12 and c["XC"] == 4
+    # two row tiles per workgroup: the five-level format on the 8B fused gate|up (24576 x 4096) at
+    # bf16 M = 15 and 16 (x beyond any one-pass split); the ternary one only where x does not fit the
+    # persistent fast path either (K = 8192 at M = 9..15), the fast path taking the fused gate|up
+    if fam == "fv5":
+        for m in (15, 16):
+            assert tw.tern_gemv_config(24576, 4096, m, "fv5_bf16") is None
+            c = tw.tern_gemv_config(24576, 4096, m, "fv5_bf16_phased")
+            assert c is not None and (c["R"], c["waves"], c["XC"], c["grid"]) == (2, 8, 8, 768), (m, c)
+    else:
+        assert tw.tern_gemv_config(24576, 4096, 16, "ternary_bf16_phased") is None
+        for m in (9, 15):
+            assert tw.tern_gemv_config(4096, 8192, m) is None
+            c = tw.tern_gemv_config(4096, 8192, m, "ternary_bf16_phased")
+            assert c is not None and (c["R"], c["waves"], c["XC"], c["grid"]) == (2, 16, 8, 128), (m, c)
+        assert tw.tern_gemv_config(4096, 8192, 16, "ternary_bf16_phased") is None   # half of x: 131 KB
 
 
 def test_phased3_picker_invariants():
