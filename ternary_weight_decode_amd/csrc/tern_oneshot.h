@@ -48,8 +48,12 @@ struct OneShotShape {
 };
 
 // R row tiles per workgroup is chosen to minimise the largest number of
-// units any CU receives (the critical path), and among equals to bring a
-// workgroup closest to 16 units; waves take 2 units each (1 when a workgroup
+// units any CU receives (the critical path), and among equals (at M > 1) to
+// run one workgroup per CU, which stages x once, while a wave keeps at most
+// two units (8B gate at M = 4: 6.32 -> 5.57 us with one workgroup of 12 waves
+// per CU instead of three of 8; two workgroups per CU, or three units per
+// wave, were slower on the fused gate|up), then to bring a workgroup
+// closest to 16 units; waves take 2 units each (1 when a workgroup
 // has at most 8), so the second unit's loads overlap the first unit's
 // compute.  Measured on the 8B ternary shapes at M = 1 (hipGraph of 36
 // launches, cold weights): 24576x4096 7.99 us with R = 2 / 8 waves vs 8.37 us
@@ -72,7 +76,7 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
         const size_t x_lds = slices ? (size_t)(nw * U * s.m1_slice_bytes) : (size_t)(M * s.x_row_bytes);
         return x_lds + (size_t)(units + 1) * ni * 64 * 4;
     };
-    int64_t best_max = -1, best_dist = 0;
+    int64_t best_max = -1, best_dist = 0, best_wg = 0;
     c.R = 0;
     for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
         const int64_t units = R * nkt, U = oneshot_u(units);
@@ -83,9 +87,15 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
         if ((size_t)per_cu * lds_of(units) > (size_t)kCuLds) continue;       // LDS of the workgroups on a CU
         const int64_t max_units = per_cu * units;
         const int64_t dist = units > 16 ? units - 16 : 16 - units;
-        if (best_max < 0 || max_units < best_max || (max_units == best_max && dist < best_dist)) {
+        // among equal critical paths: at M > 1 one workgroup per CU first (x, M*K
+        // elements, staged once per CU) as long as a wave keeps at most two units, then
+        // the workgroup closest to 16 units
+        const int64_t wg = M > 1 && per_cu == 1 && U <= 2 ? 0 : 1;
+        if (best_max < 0 || max_units < best_max ||
+            (max_units == best_max && (wg < best_wg || (wg == best_wg && dist < best_dist)))) {
             best_max = max_units;
             best_dist = dist;
+            best_wg = wg;
             c.R = R;
         }
         if (grid == 1) break;
