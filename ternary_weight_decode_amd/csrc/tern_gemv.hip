@@ -480,6 +480,89 @@ __global__ __launch_bounds__(1024) void gemv_m1_kernel(const uint8_t* __restrict
     }
 }
 
+// Small M (2..8), bf16 activations, one row tile per workgroup: the M = 1
+// kernel's per-wave activation slices for MR rows (MR = 2, 4 or 8 >= M; a
+// row past M repeats row M-1).  A unit's slice is MR rows of 512 bf16, one
+// 16-byte chunk per lane and row, rows 1040 bytes apart in LDS so that the A
+// reads of 16 rows fall in different banks.  With one row tile per workgroup
+// every wave's k-tiles are its own: the slices load the bytes the workgroup
+// staging did, and no workgroup barrier stands before the compute.
+template <int MT, int U>
+__global__ __launch_bounds__(1024) void gemv_slices_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                           const uint16_t* __restrict__ x, int M,
+                                                           float* __restrict__ y)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    constexpr int NI = MT < 4 ? MT : 4;
+    constexpr int MR = MT == 16 ? 8 : MT;                              // staged rows
+    constexpr int kRowB = kTileK * 2 + 16;                            // bytes per staged row
+    constexpr int kSlice = MR * kRowB;                                // bytes per unit
+    const int nw = (int)(blockDim.x >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7), nkt = nb >> 2;
+    const int64_t rt = blockIdx.x;
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
+    uint8_t* xs = smem + (size_t)wave * U * kSlice;                   // this wave's slices
+    float* red = (float*)(smem + (size_t)nw * U * kSlice);            // [nkt + 1 spare][NI][64]
+    const int row_chunks = (int)(K >> 3);                              // 16-byte chunks per row of x
+
+    int ukt[U];
+    bool uok[U];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int kt = wave + i * nw;
+        uok[i] = kt < nkt;
+        ukt[i] = uok[i] ? kt : nkt - 1;
+    }
+    PlaneTile t[U];
+    u32x4 xv[U][MR];
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            const int mr = m < M ? m : M - 1;
+            xv[i][m] = xg[mr * row_chunks + ukt[i] * (kTileK / 8) + lane];
+        }
+        const int64_t wb = tile_word_base(rt, ukt[i], nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+#pragma unroll
+    for (int i = 0; i < U; ++i) t[i].sc = ld_nt8(scales + tile_scale_base(rt, ukt[i], nb) + r * 4);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int mrow = r < M ? r : M - 1;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        // a wave's LDS accesses run in order: its own writes are seen by its reads below
+#pragma unroll
+        for (int m = 0; m < MR; ++m) *(u32x4*)(xs + i * kSlice + m * kRowB + 16 * lane) = xv[i][m];
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16_tile<MT>(t[i], (const uint16_t*)(xs + i * kSlice + mrow * kRowB + 64 * g), 4, acc);
+        const int slot = uok[i] ? ukt[i] : nkt;
+#pragma unroll
+        for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    const int lanes_used = M <= 4 ? 16 : 32;
+    for (int e = threadIdx.x; e < NI * 64; e += (int)blockDim.x) {
+        const int l = e & 63, q = e >> 6;
+        const int m = 4 * (l >> 4) + q, n = l & 15;
+        const int64_t row = rt * kTileRows + n;
+        if (l < lanes_used && m < M && row < N) {
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += red[(kt * NI + q) * 64 + l];
+            y[(int64_t)m * N + row] = sum;
+        }
+    }
+}
+
 // Two-phase variant of the one-pass kernel for activations too large for
 // LDS (large K at M >= 5 bf16, or M >= 13 int8): RT row tiles per workgroup
 // (1, or 2 when one tile's waves would each stage more than 8 activation
@@ -946,12 +1029,35 @@ static hipError_t m1_dispatch(const OneShot& c, hipStream_t stream, const uint8_
     return hipErrorNotSupported;
 }
 
+template <int MT>
+static hipError_t slices_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N, int64_t K,
+                                  const uint16_t* x, int M, float* y)
+{
+#define TERN_SLICES_CASE(UU)                                                                                       \
+    if (c.U == UU) {                                                                                               \
+        if (!oneshot_resident(gemv_slices_kernel<MT, UU>, c)) return hipErrorNotSupported;                         \
+        gemv_slices_kernel<MT, UU><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, x, M, \
+                                                                                              y);                  \
+        return hipGetLastError();                                                                                  \
+    }
+    TERN_SLICES_CASE(1) TERN_SLICES_CASE(2)
+#undef TERN_SLICES_CASE
+    return hipErrorNotSupported;
+}
+
 static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int64_t K, const void* x, const float* s_x,
                                  int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     OneShot c;
     if (!pick_oneshot(N, K, M, oneshot_shape(K, i8), c)) return hipErrorNotSupported;
     if (!i8 && M == 1) return m1_dispatch(c, stream, packed, N, K, (const uint16_t*)x, y);
+    if (!i8 && M <= 8 && c.R == 1 && c.U <= 2) {
+        // per-wave slices (the picker sized LDS for them)
+        const uint16_t* xb = (const uint16_t*)x;
+        if (M == 2) return slices_dispatch<2>(c, stream, packed, N, K, xb, (int)M, y);
+        if (M <= 4) return slices_dispatch<4>(c, stream, packed, N, K, xb, (int)M, y);
+        return slices_dispatch<16>(c, stream, packed, N, K, xb, (int)M, y);
+    }
     const int m = (int)M;
     // 8 activation chunks per thread are instantiated for the MT = 16 kernel
     // only, which computes the same rows as MT = 4 (4 per lane group)

@@ -70,10 +70,18 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     const int64_t nkt = K / 512, nrt = (N + 15) / 16;
     const int64_t cus = device_cus();
     const int ni = M == 1 ? 1 : (M == 2 ? 2 : 4);
-    const bool slices = M == 1 && s.m1_slice_bytes > 0;
-    auto lds_of = [&](int64_t units) {
+    // per-wave activation slices: at M = 1 (1 KiB per unit), and at M <= 8 with one row
+    // tile per workgroup and at most two units per wave (2, 4 or 8 rows of 1040 bytes
+    // per unit, held in registers until staged)
+    const int64_t mr = M <= 2 ? 2 : (M <= 4 ? 4 : 8);
+    auto slices_of = [&](int64_t R, int64_t U) {
+        return s.m1_slice_bytes > 0 && (M == 1 || (M <= 8 && R == 1 && U <= 2));
+    };
+    auto lds_of = [&](int64_t units, int64_t R) {
         const int64_t U = oneshot_u(units), nw = (units + U - 1) / U;
-        const size_t x_lds = slices ? (size_t)(nw * U * s.m1_slice_bytes) : (size_t)(M * s.x_row_bytes);
+        const size_t x_lds = !slices_of(R, U) ? (size_t)(M * s.x_row_bytes)
+                             : M == 1      ? (size_t)(nw * U * s.m1_slice_bytes)
+                                           : (size_t)(nw * U * mr * (s.m1_slice_bytes + 16));
         return x_lds + (size_t)(units + 1) * ni * 64 * 4;
     };
     int64_t best_max = -1, best_dist = 0, best_wg = 0;
@@ -84,7 +92,7 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
         const int64_t nw = (units + U - 1) / U;
         const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
         if (per_cu * nw > 4 * s.waves_per_simd[U]) continue;                  // not resident in one round
-        if ((size_t)per_cu * lds_of(units) > (size_t)kCuLds) continue;       // LDS of the workgroups on a CU
+        if ((size_t)per_cu * lds_of(units, R) > (size_t)kCuLds) continue;    // LDS of the workgroups on a CU
         const int64_t max_units = per_cu * units;
         const int64_t dist = units > 16 ? units - 16 : 16 - units;
         // among equal critical paths: at M > 1 one workgroup per CU first (x, M*K
@@ -106,7 +114,7 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
         int64_t best = -1;
         for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
             const int64_t units = R * nkt;
-            if (oneshot_u(units) > 4 || lds_of(units) > (size_t)kCuLds) break;
+            if (oneshot_u(units) > 4 || lds_of(units, R) > (size_t)kCuLds) break;
             const int64_t dist = units > 16 ? units - 16 : 16 - units;
             if (best < 0 || dist < best) {
                 best = dist;
@@ -120,12 +128,13 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     c.U = (int)oneshot_u(units);
     c.nw = (int)((units + c.U - 1) / c.U);
     c.grid = (nrt + c.R - 1) / c.R;
+    const bool slices = slices_of(c.R, c.U);
     const int64_t xc = slices ? 1 : (M * (s.x_src_bytes / s.chunk_bytes) + 64 * c.nw - 1) / (64 * c.nw);
     // 8 chunks run on the MT = 16 kernels, whose partials hold 4 rows per
     // lane group: not for M <= 2, whose partial area is sized for 1 or 2
     if (xc > 8 || (xc > 4 && M <= 2)) return false;
     c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
-    c.lds = lds_of(units);
+    c.lds = lds_of(units, c.R);
     return c.lds <= (size_t)kCuLds;
 }
 

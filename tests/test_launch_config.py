@@ -41,6 +41,11 @@ def test_picker_invariants(kind):
         if kind == "ternary_bf16" and m == 1:
             # each wave stages the 1 KB activation slice of each of its units
             assert c["XC"] == 1 and c["lds"] == c["waves"] * c["U"] * 1024 + (units + 1) * 64 * 4, where
+        elif kind == "ternary_bf16" and m <= 8 and c["R"] == 1 and c["U"] <= 2:
+            # each wave stages its units' slices: 2, 4 or 8 rows of 1040 bytes
+            mr = 2 if m <= 2 else (4 if m <= 4 else 8)
+            assert c["XC"] == 1, where
+            assert c["lds"] == c["waves"] * c["U"] * mr * 1040 + (units + 1) * ni * 64 * 4, where
         else:
             xrow = k + 16 if i8 else (k + 8) * 2
             assert c["lds"] == m * xrow + (units + 1) * ni * 64 * 4, where
