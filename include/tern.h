@@ -377,9 +377,11 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * computed on the host exactly as the launchers do (the CU count is the current device's, or
  * 256 without one; the launchers also confirm residency with the occupancy
  * query).  Returns 1 and fills out[8] = {row tiles per workgroup R, waves per
- * workgroup, 512-k units per wave U, activation chunks per thread, grid,
- * dynamic LDS bytes, runs in several rounds (0/1), MFMA activation rows of the
- * kernel instance}; 0 when another kernel takes the shape; -TERN_E_NULL or
+ * workgroup, 512-k units per wave U, activation chunks per thread (1 where
+ * every wave stages only its own units' activation slices: kind 0 at M = 1,
+ * and at M <= 8 with R = 1 and U <= 2), grid, dynamic LDS bytes, runs in
+ * several rounds (0/1), MFMA activation rows of the kernel instance}; 0 when
+ * another kernel takes the shape; -TERN_E_NULL or
  * -TERN_E_SHAPE for a NULL out or a shape outside 1 <= M <= TERN_MAX_M_GEMV,
  * N, K >= 1, kind 0..8.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
