@@ -466,7 +466,8 @@ def mode_smallm(args, tw, synth, torch):
                 act = m * (2 * k if variant == "bf16" else k + 4)
                 nbytes = tw.tern_packed_bytes(n, k) + act + 4 * m * n
                 out.append({"proj": proj, "n_k": [n, k], "M": m, "act": variant, "us": round(ms * 1e3, 2),
-                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1)})
+                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes})
+                print(f"smallm {proj} M={m} {variant}: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
                 del g
         del copies
     print(json.dumps({"mode": "smallm", "unit": "GB/s of weights+activations+outputs per launch, cold HBM",
@@ -664,7 +665,8 @@ def mode_fv5(args, tw, synth, torch):
                     gbs = nbytes / (ms * 1e-3) / 1e9
                     out.append({"unit": label, "format": fmt, "act": act, "n_k": [n, k], "M": m,
                                 "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
-                                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1)})
+                                "pct_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 1), "bytes": nbytes})
+                    print(f"fv5 {label} {fmt} M={m} {act}: {ms * 1e3:.2f} us", file=sys.stderr, flush=True)
                     if m == 1:
                         layer[f"{fmt}_{act}"][0] += ms * 1e3
                         layer[f"{fmt}_{act}"][1] += nbytes

@@ -489,6 +489,9 @@ static hipError_t gemv5_oneshot_dispatch(const OneShot& c, hipStream_t stream, c
     if constexpr (MT == 16) {
         TERN5_CASE(1, 8) TERN5_CASE(2, 8) TERN5_CASE(3, 8) TERN5_CASE(4, 8)
     }
+    if constexpr (MT == 16 && !kI8) {
+        TERN5_CASE(1, 16) TERN5_CASE(2, 16) TERN5_CASE(3, 16)
+    }
 #undef TERN5_CASE
     return hipErrorNotSupported;
 }

@@ -997,6 +997,9 @@ static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const u
     if constexpr (MT == 16) {
         TERN_ONESHOT_CASE(1, 8) TERN_ONESHOT_CASE(2, 8) TERN_ONESHOT_CASE(3, 8) TERN_ONESHOT_CASE(4, 8)
     }
+    if constexpr (MT == 16 && !kI8) {
+        TERN_ONESHOT_CASE(1, 16) TERN_ONESHOT_CASE(2, 16) TERN_ONESHOT_CASE(3, 16)
+    }
 #undef TERN_ONESHOT_CASE
     return hipErrorNotSupported;
 }

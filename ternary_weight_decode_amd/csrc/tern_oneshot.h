@@ -131,9 +131,12 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     const bool slices = slices_of(c.R, c.U);
     const int64_t xc = slices ? 1 : (M * (s.x_src_bytes / s.chunk_bytes) + 64 * c.nw - 1) / (64 * c.nw);
     // 8 chunks run on the MT = 16 kernels, whose partials hold 4 rows per
-    // lane group: not for M <= 2, whose partial area is sized for 1 or 2
-    if (xc > 8 || (xc > 4 && M <= 2)) return false;
-    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : 8));
+    // lane group: not for M <= 2, whose partial area is sized for 1 or 2;
+    // 16 chunks (bf16 rows at M > 8, x up to 128 KiB) only in one resident
+    // round, where every workgroup stages x once
+    const int64_t xc_max = s.chunk_bytes == 16 && M > 8 && !c.rounds && c.U <= 3 ? 16 : 8;
+    if (xc > xc_max || (xc > 4 && M <= 2)) return false;
+    c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : (xc <= 8 ? 8 : 16)));
     c.lds = lds_of(units, c.R);
     return c.lds <= (size_t)kCuLds;
 }

@@ -2,6 +2,8 @@
 
     python -m ternary_weight_decode_amd.rocprof_summary trace DIR [--kernel RE] [--window A:B]
     python -m ternary_weight_decode_amd.rocprof_summary pmc DIR [--kernel RE] [--window A:B]
+    python -m ternary_weight_decode_amd.rocprof_summary runs DIR [DIR ...] --bench OUT [--kernel RE] [--passes P]
+                                                             [--scale COUNTER=F ...]
 
 ``trace`` reads the kernel-trace CSV under DIR (``--kernel-trace -f csv``) and
 prints, per kernel and grid size, the dispatch count and the mean / median /
@@ -11,12 +13,25 @@ mean of every counter per dispatch.  ``--kernel`` keeps kernels whose name
 matches the regular expression; ``--window A:B`` keeps the matching
 dispatches with ordinal A <= i < B (in dispatch order over every kernel the
 expression keeps), e.g. the launches of a benchmark's timed region.
+
+``runs`` splits a sweep into its cases: consecutive kept dispatches of the
+same kernel and grid form one run, and the runs are matched in order with
+the ``rows`` of the sweep's JSON line (the last line of OUT holding one).
+Each run is P equal passes (an eager warm-up, then graph replays); the first
+is dropped and the median of the rest is printed.  Where a run has k times
+the dispatches of the smallest run of its unit, every call was k launches
+and k consecutive dispatches are summed.  DIR holds a kernel trace or a
+counter collection; for counters, ``--scale`` turns a counter's KiB into
+bytes (the factor from a copy of known size) and, with a row's ``bytes``,
+the ratio of measured to algorithmic bytes is printed; counters taken in
+separate runs of the same sweep (one directory each) are merged.
 """
 from __future__ import annotations
 
 import argparse
 import csv
 import glob
+import json
 import os
 import re
 import statistics
@@ -70,7 +85,8 @@ def load_trace(d: str, kernel: str | None, window: str | None):
             int(r.get("Grid_Size_Z", 1) or 1)
         wg = int(_col(r, "Workgroup_Size_X", "Workgroup_Size"))
         ns = int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))
-        out.append((int(_col(r, "Dispatch_Id")), name, grid, wg, ns))
+        vgpr = r.get("Arch_VGPR_Count") or r.get("VGPR_Count") or "0"
+        out.append((int(_col(r, "Dispatch_Id")), name, grid, wg, ns, int(vgpr)))
     out.sort()
     return _window(out, window)
 
@@ -78,7 +94,7 @@ def load_trace(d: str, kernel: str | None, window: str | None):
 def cmd_trace(args):
     rows = load_trace(args.dir, args.kernel, args.window)
     groups = {}
-    for (_, name, grid, wg, ns) in rows:
+    for (_, name, grid, wg, ns, _) in rows:
         groups.setdefault((name, grid, wg), []).append(ns)
     print(f"{'kernel':60s} {'grid':>9s} {'wg':>5s} {'calls':>6s} {'mean_us':>9s} {'median_us':>9s} "
           f"{'min_us':>8s} {'max_us':>8s}")
@@ -118,6 +134,105 @@ def cmd_pmc(args):
             print(f"  {cn:32s} median {statistics.median(v):16.1f}   mean {statistics.mean(v):16.1f}")
 
 
+def load_pmc(d: str, kernel: str | None):
+    """Per dispatch (in dispatch order): name, grid, workgroup size, {counter: value}."""
+    per = {}
+    for r in csv.DictReader(open(_find(d, "counter_collection.csv"))):
+        name = short_name(_col(r, "Kernel_Name"))
+        if kernel and not re.search(kernel, name):
+            continue
+        did = int(_col(r, "Dispatch_Id"))
+        e = per.setdefault(did, [name, int(_col(r, "Grid_Size")), int(_col(r, "Workgroup_Size")), {}])
+        cn = _col(r, "Counter_Name")
+        e[3][cn] = e[3].get(cn, 0.0) + float(_col(r, "Counter_Value"))
+    return [tuple(per[k]) for k in sorted(per)]
+
+
+def split_runs(disp):
+    """Consecutive dispatches with the same (name, grid, workgroup size): [(key, [payload, ...])]."""
+    runs = []
+    for name, grid, wg, payload in disp:
+        key = (name, grid, wg)
+        if runs and runs[-1][0] == key:
+            runs[-1][1].append(payload)
+        else:
+            runs.append((key, [payload]))
+    return runs
+
+
+def bench_rows(path: str):
+    rows = None
+    for line in open(path):
+        line = line.strip()
+        if line.startswith("{"):
+            try:
+                d = json.loads(line)
+            except ValueError:
+                continue
+            if isinstance(d.get("rows"), list):
+                rows = d["rows"]
+    if rows is None:
+        sys.exit(f"no JSON line with rows in {path}")
+    return rows
+
+
+def row_label(r: dict) -> str:
+    unit = r.get("proj", r.get("unit", "?"))
+    fmt = r.get("format", "")
+    return f"{unit:7s}{fmt:8s}{r.get('act', ''):5s} M={r.get('M', '?'):>2}"
+
+
+def _calls(vals, k, combine):
+    """Sum (combine) every k consecutive dispatches into one call."""
+    return [combine(vals[i:i + k]) for i in range(0, len(vals) - k + 1, k)]
+
+
+def cmd_runs(args):
+    rows = bench_rows(args.bench)
+    counters = glob.glob(os.path.join(args.dir[0], "**", "*counter_collection.csv"), recursive=True)
+    if counters:
+        # one counter per run of the sweep: the runs' dispatches are merged position by position
+        per_dir = [split_runs(load_pmc(d, args.kernel)) for d in args.dir]
+        runs = per_dir[0]
+        for other in per_dir[1:]:
+            if [(k, len(v)) for k, v in other] != [(k, len(v)) for k, v in runs]:
+                sys.exit("the counter runs do not hold the same sequence of dispatches")
+            runs = [(k, [{**a, **b} for a, b in zip(v, w)]) for (k, v), (_, w) in zip(runs, other)]
+    else:
+        if len(args.dir) != 1:
+            sys.exit("one kernel-trace directory at a time")
+        disp = [(n, g, w, (ns, vg)) for (_, n, g, w, ns, vg) in load_trace(args.dir[0], args.kernel, None)]
+        runs = split_runs(disp)
+    if len(runs) != len(rows):
+        sys.exit(f"{len(runs)} runs of dispatches but {len(rows)} rows in {args.bench}: the kernel filter or "
+                 f"the sweep does not match")
+    # the rows of one unit and weight format share their copies, hence their launches per pass
+    unit_of = lambda r: (r.get("proj", r.get("unit")), r.get("format"))
+    base = {}
+    for (key, v), r in zip(runs, rows):
+        base[unit_of(r)] = min(base.get(unit_of(r), len(v)), len(v))
+    scale = dict(s.split("=") for s in args.scale)
+    for (key, v), r in zip(runs, rows):
+        name, grid, wg = key
+        k = max(1, round(len(v) / base[unit_of(r)]))
+        v = v[len(v) // args.passes:]
+        kname = (name.split("<")[0] + (f" x{k}" if k > 1 else ""))[:26]
+        head = f"  {row_label(r)}  {kname:26s} {grid // wg:5d} x {wg:4d}"
+        if counters:
+            calls = _calls(v, k, lambda g: {c: sum(d[c] for d in g) for c in g[0]})
+            med = {c: statistics.median(d[c] for d in calls) for c in sorted(calls[0])}
+            text = "  ".join(f"{c} {m:10.1f} KiB" for c, m in med.items())
+            if all(c in scale for c in med) and "bytes" in r:
+                meas = sum(m * 1024 * float(scale[c]) for c, m in med.items())
+                text += f"  -> {meas / 1e6:8.3f} MB  algorithmic {r['bytes'] / 1e6:8.3f} MB  " \
+                        f"ratio {meas / r['bytes']:.3f}"
+            print(f"{head}  {text}")
+        else:
+            calls = _calls([ns for ns, _ in v], k, sum)
+            print(f"{head}  vgpr={v[0][1]:3d}  launches={len(v) * args.passes // (args.passes - 1):6d}  "
+                  f"median_us={statistics.median(calls) / 1e3:7.2f}")
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -126,8 +241,14 @@ def main(argv=None):
         p.add_argument("dir")
         p.add_argument("--kernel", default=None)
         p.add_argument("--window", default=None)
+    p = sub.add_parser("runs")
+    p.add_argument("dir", nargs="+", help="a kernel-trace directory, or counter directories of the same sweep")
+    p.add_argument("--bench", required=True, help="the sweep's output (its JSON line with rows)")
+    p.add_argument("--kernel", default=None)
+    p.add_argument("--passes", type=int, default=7, help="equal passes per run; the first is dropped")
+    p.add_argument("--scale", action="append", default=[], help="COUNTER=F: bytes per counted KiB / 1024")
     args = ap.parse_args(argv)
-    (cmd_trace if args.cmd == "trace" else cmd_pmc)(args)
+    {"trace": cmd_trace, "pmc": cmd_pmc, "runs": cmd_runs}[args.cmd](args)
 
 
 if __name__ == "__main__":

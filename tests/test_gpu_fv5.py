@@ -122,6 +122,22 @@ def test_gemv5_two_phase(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(1000, 4096, 9), (4100, 4096, 16), (12288, 4096, 13)])
+def test_gemv5_sixteen_chunks(tw, n, k, m):
+    """bf16 activations of 9..16 rows that fit a CU's LDS only with 16 staged
+    chunks per thread (the one-pass kernel in one resident round, where the
+    occupancy allows it; the two-phase kernel otherwise): every output
+    against the oracle."""
+    c = tw.tern_gemv_config(n, k, m, "fv5_bf16")
+    assert c is not None and c["XC"] == 16
+    lv, lo, hi, x = gen(n, k, m, seed=11 * n + m)
+    y = host(tw.tern5_gemv(gpu_pack(tw, lv, lo, hi), n, k, dev(x)))
+    want, _ = fv5.gemv_bf16_levels(lv, lo, hi, x)
+    assert rel_l2(y, want) < TOL
+    err = np.abs(y - want).max(axis=0) / (np.abs(want).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 @pytest.mark.parametrize("n,k,m", [(12300, 4096, 16), (24576, 4096, 15)])
 def test_gemv5_two_phase_two_row_tiles(tw, n, k, m):
     """bf16 M = 15..16 at K = 4096 beyond every one-pass split (the 8B fused

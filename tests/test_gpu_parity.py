@@ -564,6 +564,24 @@ def test_gemv_bf16_two_phase_two_row_tiles(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(1000, 4096, 9), (37, 4096, 12), (4100, 4096, 16), (12288, 4096, 13),
+                                   (2000, 2048, 16)])
+def test_gemv_bf16_sixteen_chunks(tw, n, k, m):
+    """bf16 activations of 9..16 rows whose x (up to 128 KiB) fits a CU's LDS
+    only with 16 staged chunks per thread: the one-pass kernel in one
+    resident round (4100 rows: two row tiles per workgroup, the last
+    workgroup's second tile past the end; 12288 rows: three row tiles and two
+    units per wave).  Every output against the oracle."""
+    c = tw.tern_gemv_config(n, k, m)
+    assert c is not None and c["XC"] == 16 and not c["rounds"]
+    t, s, x = gen(n, k, m, seed=7 * n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    y64, _ = oracle.gemv_bf16(oracle.pack(t, s), n, k, x)
+    assert oracle.rel_l2(y, y64) <= TOL
+    err = np.abs(y - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 @pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12), (300, 12288, 13)])
 def test_gemv_bf16_three_phase(tw, n, k, m):
     """bf16 activations of more than 8 rows whose halves of K exceed LDS (the

@@ -32,7 +32,10 @@ def test_picker_invariants(kind):
         nrt, nkt = (n + 15) // 16, k // 512
         units = c["R"] * nkt
         where = (kind, n, k, m, c)
-        assert 1 <= c["U"] <= 4 and c["XC"] in (1, 2, 4, 8), where
+        assert 1 <= c["U"] <= 4 and c["XC"] in (1, 2, 4, 8, 16), where
+        if c["XC"] == 16:
+            # 16 chunks: bf16 rows above 8, in one resident round, at most three units per wave
+            assert not i8 and m > 8 and not c["rounds"] and c["U"] <= 3, where
         assert 64 * c["waves"] <= 1024, where
         assert c["waves"] * c["U"] >= units > (c["waves"] - 1) * c["U"], where   # every unit owned, no idle wave
         assert c["grid"] == (nrt + c["R"] - 1) // c["R"], where
