@@ -52,11 +52,12 @@ def parse():
     ap.add_argument("--prefill-case", default=None, metavar="PROJ:M",
                     help="--mode prefill: run only this shape and M (e.g. gate:2048)")
     ap.add_argument("--mode", default="token",
-                    choices=["token", "smallm", "prefill", "head", "fv5", "sweep", "copy", "peak"],
+                    choices=["token", "smallm", "prefill", "head", "fv5", "sweep", "copy", "peak", "floor"],
                     help="token: the headline step; smallm: speculative-verify M sweep on the 8B shapes; "
                          "prefill: int8-MFMA contraction at M in {64, 512, 2048}; "
                          "copy: plain 256 MiB device copies (reference for memory-counter scaling); "
-                         "peak: the matrix-core throughput probe (int8 16x16x64 and bf16 16x16x32)")
+                         "peak: the matrix-core throughput probe (int8 16x16x64 and bf16 16x16x32); "
+                         "floor: per-launch cost of near-empty dependent launches and the streaming read rate")
     return ap.parse_args()
 
 
@@ -443,6 +444,36 @@ def measure_c1(tw, synth, torch, compose: str, reps: int):
     return out
 
 
+def measure_floor(tw, torch, reps: int, n_tern: int = 0, tern_bytes: int = 0, tern_us: float = 0.0):
+    """What a GEMV launch at M = 1 sits on: the cost per launch of dependent launches in a hipGraph (an
+    empty kernel; 256 workgroups x 512 threads storing one float each; the same after one 16-byte load
+    per thread from a distinct, cold 2 MiB buffer) and the rate of a plain streaming read of 1 GiB.  With
+    the step's launch count and ternary bytes: the floor-plus-read model of the ternary part of a step
+    (launches x cold-load floor + bytes at the read rate) beside its measured time."""
+    launches = 256
+    bufs = [torch.zeros(256 * 512 * 16, dtype=torch.uint8, device="cuda") for _ in range(launches)]
+    sink = torch.zeros(1 << 14, dtype=torch.float32, device="cuda")
+    out = {}
+    for name, kind, grid in (("empty_us", "empty", 1), ("store_256x512_us", "store", 256),
+                             ("cold_load_256x512_us", "load", 256)):
+        g = capture(torch, lambda: [tw.tern_launch_probe(kind, grid, src=b if kind == "load" else None, sink=sink)
+                                    for b in bufs])
+        out[name] = round(time_replays(torch, g, reps) / launches * 1e3, 3)
+        del g
+    del bufs
+    big = torch.zeros(1 << 30, dtype=torch.uint8, device="cuda")
+    ms = time_calls(torch, lambda: tw.tern_launch_probe("read", 4096, src=big, sink=sink), reps)
+    read_gbs = big.numel() / (ms * 1e-3) / 1e9
+    out["read_1GiB_GB/s"] = round(read_gbs, 1)
+    del big
+    if n_tern:
+        model = n_tern * out["cold_load_256x512_us"] + tern_bytes / (read_gbs * 1e9) * 1e6
+        out["ternary_model_us"] = round(model, 1)
+        out["ternary_measured_us"] = round(tern_us, 1)
+        out["model_over_measured"] = round(model / tern_us, 3)
+    return out
+
+
 def mode_smallm(args, tw, synth, torch):
     """Speculative-verify sweep: every 8B shape at M in {1,2,4,7,8} (and 16, the largest batch a call
     takes), bf16 and int8 activations; weights rotate over >= 1 GB of copies so each launch reads HBM."""
@@ -705,6 +736,9 @@ def main():
         return mode_sweep(args, tw, synth, torch)
     if args.mode == "peak":
         return mode_peak(args, tw, synth, torch)
+    if args.mode == "floor":
+        print(json.dumps({"mode": "floor", **measure_floor(tw, torch, 10)}), flush=True)
+        return
     if args.mode == "copy":
         src = torch.ones(1 << 28, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -796,6 +830,8 @@ def main():
         extra["config0"] = measure_c0(tw, synth, torch, reps)
         log("config 1 (0.6B token-equivalent, two model copies alternated) ...")
         extra["config1"] = measure_c1(tw, synth, torch, args.compose, reps)
+        log("launch floor and read ceiling ...")
+        extra["launch_floor"] = measure_floor(tw, torch, reps, n_tern, tern_bytes, tern_ms * 1e3)
 
     cpu = None
     if not args.no_cpu_baseline:

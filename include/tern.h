@@ -405,6 +405,26 @@ double tern_mfma_peak_ops(int kind, int64_t iters, int64_t grid);
 int64_t tern_mfma_peak_sink_bytes(int64_t grid);
 int tern_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, void* stream);
 
+/* ---- launch floor and read ceiling probe (a measurement aid; no operation of the method) ----
+ *
+ * A GEMV launch at M = 1 costs about what a launch that does almost nothing
+ * costs, plus its bytes at the rate a plain streaming read reaches.  This
+ * probe enqueues one launch of:
+ *   kind 0: an empty kernel (`grid` workgroups of 64 threads);
+ *   kind 1: `grid` workgroups of 512 threads, each storing one float of sink;
+ *   kind 2: as kind 1, every thread first loading 16 bytes of src (thread i
+ *           reads bytes [16i, 16i + 16), clamped to the last 16 bytes);
+ *   kind 3: `grid` workgroups of 256 threads reading all src_bytes of src once
+ *           (16-byte loads, eight in flight per thread).
+ * The caller times the launches (in a graph, one after another, for the
+ * floor; one large src for the read rate).  sink: device memory of at least
+ * `grid` floats (kinds 1-3; kind 3 writes it only if the bytes it read XOR
+ * to 0x9E3779B9, so pass zero-filled src); src: device memory, 16-byte
+ * aligned, src_bytes a positive multiple of 16 (kinds 2 and 3).
+ * Errors: TERN_E_SHAPE for kind outside [0, 3], grid outside [1, 2^31 - 1]
+ * or a bad src_bytes; TERN_E_NULL / TERN_E_ALIGN for sink and src. */
+int tern_launch_probe(int kind, int64_t grid, const void* src, int64_t src_bytes, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

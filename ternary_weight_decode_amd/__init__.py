@@ -31,12 +31,12 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
            "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
-           "i8_head_argmax_noalloc")
+           "tern_launch_probe", "i8_head_argmax_noalloc")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
                "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak",
-               "i8_head_argmax_noalloc")
+               "tern_launch_probe", "i8_head_argmax_noalloc")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -97,6 +97,7 @@ def lib():
         L.tern_mfma_peak_sink_bytes.restype = _i64
         L.tern_mfma_peak_sink_bytes.argtypes = [_i64]
         L.tern_mfma_peak.argtypes = [ctypes.c_int, _i64, _i64, _p, _p]
+        L.tern_launch_probe.argtypes = [ctypes.c_int, _i64, _p, _i64, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -511,6 +512,24 @@ def tern_gemv_config(n: int, k: int, m: int, kind: str = "ternary_bf16"):
         return None
     keys = ("R", "waves", "U", "XC", "grid", "lds", "rounds", "MT")
     return dict(zip(keys, (int(v) for v in out)))
+
+
+LAUNCH_PROBE_KINDS = {"empty": 0, "store": 1, "load": 2, "read": 3}
+
+
+def tern_launch_probe(kind: str, grid: int, src=None, sink=None, stream=None):
+    """Launch-floor / read-ceiling probe (measurement aid): enqueue one launch
+    ("empty", "store": one float per workgroup, "load": one 16-byte load of
+    src per thread first, "read": all of src read once by `grid` workgroups of
+    256 threads).  src: a zero-filled device tensor (16-byte aligned); sink:
+    at least `grid` floats (allocated when None)."""
+    import torch
+    if sink is None and kind != "empty":
+        sink = torch.empty(grid, dtype=torch.float32, device="cuda")
+    nbytes = 0 if src is None else src.numel() * src.element_size()
+    _check("tern_launch_probe", lib().tern_launch_probe(LAUNCH_PROBE_KINDS[kind], grid, _ptr(src), nbytes,
+                                                         _ptr(sink), _stream(stream)))
+    return sink
 
 
 MFMA_PEAK_KINDS = {"int8": 0, "bf16": 1}

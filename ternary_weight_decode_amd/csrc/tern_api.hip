@@ -551,4 +551,18 @@ int tern_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, void* s
     return finish(tern::launch_mfma_peak(kind, iters, grid, sink, (hipStream_t)stream));
 }
 
+int tern_launch_probe(int kind, int64_t grid, const void* src, int64_t src_bytes, float* sink, void* stream)
+{
+    if (kind < 0 || kind > 3 || grid < 1 || grid > 0x7FFFFFFF) return TERN_E_SHAPE;
+    if (kind >= 1 && !sink) return TERN_E_NULL;
+    if (kind >= 2) {
+        if (!src) return TERN_E_NULL;
+        if (!aligned16(src)) return TERN_E_ALIGN;
+        if (src_bytes < 16 || src_bytes % 16 != 0) return TERN_E_SHAPE;
+    }
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_probe(kind, grid, src, src_bytes, sink, (hipStream_t)stream));
+}
+
 }  // extern "C"

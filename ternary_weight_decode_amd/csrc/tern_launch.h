@@ -110,6 +110,7 @@ hipError_t launch_gemv5_i8(const uint8_t* packed, int64_t N, int64_t K, const in
 double mfma_peak_ops(int kind, int64_t iters, int64_t grid);
 int64_t mfma_peak_sink_ints(int64_t grid);
 hipError_t launch_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink, hipStream_t stream);
+hipError_t launch_probe(int kind, int64_t grid, const void* src, int64_t src_bytes, float* sink, hipStream_t stream);
 
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream);

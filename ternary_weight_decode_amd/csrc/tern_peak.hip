@@ -1,8 +1,15 @@
-// tern_peak.hip — matrix-core throughput probe: independent MFMA chains on
-// registers with no memory traffic inside the loop, so the achieved rate is
-// the chip's sustained matrix-core rate for that instruction.  It is the
-// denominator check for the prefill contraction (int8 16x16x64) and the
-// GEMV's bf16 16x16x32 steps; it computes nothing of the method.
+// tern_peak.hip — measurement probes; they compute nothing of the method.
+//
+// Matrix-core throughput: independent MFMA chains on registers with no
+// memory traffic inside the loop, so the achieved rate is the chip's
+// sustained matrix-core rate for that instruction.  It is the denominator
+// check for the prefill contraction (int8 16x16x64) and the GEMV's bf16
+// 16x16x32 steps.
+//
+// Launch floor and read ceiling: the cost of one dependent launch of a
+// kernel that does (almost) nothing, and the rate at which a plain streaming
+// read moves bytes out of HBM; a GEMV launch at M = 1 costs about the floor
+// of a launch with one cold load plus its bytes at the read ceiling.
 #include "tern_device.h"
 #include "tern_launch.h"
 
@@ -65,6 +72,57 @@ hipError_t launch_mfma_peak(int kind, int64_t iters, int64_t grid, int32_t* sink
 {
     if (kind == 0) mfma_peak_kernel<0><<<dim3((unsigned)grid), dim3(64 * kPeakWaves), 0, stream>>>(iters, sink);
     else mfma_peak_kernel<1><<<dim3((unsigned)grid), dim3(64 * kPeakWaves), 0, stream>>>(iters, sink);
+    return hipGetLastError();
+}
+
+// ---- launch floor / read ceiling -------------------------------------------
+
+__global__ __launch_bounds__(64) void probe_empty_kernel() {}
+
+// one float per workgroup
+__global__ __launch_bounds__(512) void probe_store_kernel(float* __restrict__ sink)
+{
+    if (threadIdx.x == 0) sink[blockIdx.x] = (float)blockIdx.x;
+}
+
+// one 16-byte load per thread (index clamped to the buffer), then one float per workgroup
+__global__ __launch_bounds__(512) void probe_load_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                         float* __restrict__ sink)
+{
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const u32x4 v = src[i < n16 ? i : n16 - 1];
+    const uint32_t a = v[0] ^ v[1] ^ v[2] ^ v[3];
+    // never true for the zero-filled buffers the probe is given; keeps the load
+    if (a == 0x9E3779B9u) sink[blockIdx.x] = -1.0f;
+    if (threadIdx.x == 0) sink[blockIdx.x] = (float)blockIdx.x;
+}
+
+// the whole buffer read once: grid-stride 16-byte loads, eight in flight per thread
+__global__ __launch_bounds__(256) void probe_read_kernel(const u32x4* __restrict__ src, int64_t n16,
+                                                         float* __restrict__ sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    uint32_t a = 0;
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; base < n16; base += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int64_t i = base + j * stride;
+            v[j] = src[i < n16 ? i : n16 - 1];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) a ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    if (a == 0x9E3779B9u) sink[blockIdx.x] = -1.0f;
+}
+
+hipError_t launch_probe(int kind, int64_t grid, const void* src, int64_t src_bytes, float* sink, hipStream_t stream)
+{
+    const dim3 g((unsigned)grid);
+    if (kind == 0) probe_empty_kernel<<<g, 64, 0, stream>>>();
+    else if (kind == 1) probe_store_kernel<<<g, 512, 0, stream>>>(sink);
+    else if (kind == 2) probe_load_kernel<<<g, 512, 0, stream>>>((const u32x4*)src, src_bytes / 16, sink);
+    else probe_read_kernel<<<g, 256, 0, stream>>>((const u32x4*)src, src_bytes / 16, sink);
     return hipGetLastError();
 }
 

@@ -1,5 +1,8 @@
 """The C ABI loads, exports every declared symbol, and rejects bad arguments
-on the host before any HIP call (runs without a GPU)."""
+on the host before any HIP call (runs without a GPU).  Every call below
+passes bogus device addresses, so each must fail validation (or be an empty
+problem): one that passed would launch a kernel on those addresses on a
+machine with a GPU."""
 import ctypes
 import os
 import re
@@ -114,7 +117,9 @@ def test_head_argmax_workspace_and_argument_errors():
     assert f(p, p, 100, 128, p, 0, p, p, None, p, None) == E_SHAPE         # M = 0
     assert f(p, p, 100, 128, p, 17, p, p, None, p, None) == E_SHAPE        # M > 16
     assert f(p, p, 100, 8192, p, 16, p, p, None, p, None) == E_SHAPE       # bf16 x of 16 x 8192 does not fit LDS
-    assert fi(p, p, 100, 8192, p, p, 16, p, p, None, p, None) != E_SHAPE   # int8 q of the same shape does
+    # int8 q of the same shape fits: the shape check passes and the missing workspace is reported (a
+    # complete argument list would launch on the bogus addresses wherever a GPU is present)
+    assert fi(p, p, 100, 8192, p, p, 16, p, p, None, None, None) == E_NULL
     assert f(p, p, 100, 128, p, 1, p, p, None, None, None) == E_NULL       # workspace
     assert f(p, p, 100, 128, p, 1, None, p, None, p, None) == E_NULL       # idx
     assert fi(p, p, 100, 128, p, None, 1, p, p, None, p, None) == E_NULL   # s_x
@@ -165,7 +170,7 @@ def test_fv5b_argument_errors():
     assert h(p, p, 0, 256, p, 1, p, None) == E_SHAPE                   # V = 0
     assert h(p, p, 100, 256, p, 17, p, None) == E_SHAPE                # M > 16
     assert h(p, p, 100, 8192, p, 16, p, None) == E_SHAPE               # x does not fit in LDS
-    assert hi(p, p, 100, 8192, p, p, 16, p, None, None) != E_SHAPE     # int8 q of that shape does
+    assert hi(p, p, 100, 8192, p, p, 16, None, None, None) == E_NULL   # int8 q of that shape fits (no launch)
     assert h(p, None, 100, 256, p, 1, p, None) == E_NULL
     assert h(p, p, 100, 256, p, 1, None, None) == E_NULL
     assert hi(p, p, 100, 256, p, None, 1, p, None, None) == E_NULL     # s_x
@@ -270,6 +275,19 @@ def test_mfma_peak_probe_validation():
     assert L.tern_mfma_peak(0, -1, 1, ALIGNED, None) == E_SHAPE
     assert L.tern_mfma_peak(0, 10, 1, None, None) == E_NULL
     assert L.tern_mfma_peak(0, 10, 1, MISALIGNED, None) == E_ALIGN
+
+
+def test_launch_probe_validation():
+    """The launch-floor / read probe's argument checks (no device call)."""
+    L = tw.lib()
+    assert L.tern_launch_probe(4, 1, ALIGNED, 16, ALIGNED, None) == E_SHAPE
+    assert L.tern_launch_probe(-1, 1, ALIGNED, 16, ALIGNED, None) == E_SHAPE
+    assert L.tern_launch_probe(0, 0, None, 0, None, None) == E_SHAPE
+    assert L.tern_launch_probe(1, 1, None, 0, None, None) == E_NULL
+    assert L.tern_launch_probe(2, 1, None, 16, ALIGNED, None) == E_NULL
+    assert L.tern_launch_probe(3, 1, MISALIGNED, 16, ALIGNED, None) == E_ALIGN
+    assert L.tern_launch_probe(3, 1, ALIGNED, 0, ALIGNED, None) == E_SHAPE
+    assert L.tern_launch_probe(2, 1, ALIGNED, 24, ALIGNED, None) == E_SHAPE
 
 
 def test_head_argmax_noalloc_validation():
