@@ -229,7 +229,7 @@ def cmd_runs(args):
             print(f"{head}  {text}")
         else:
             calls = _calls([ns for ns, _ in v], k, sum)
-            print(f"{head}  vgpr={v[0][1]:3d}  launches={len(v) * args.passes // (args.passes - 1):6d}  "
+            print(f"{head}  launches={len(v) * args.passes // (args.passes - 1):6d}  "
                   f"median_us={statistics.median(calls) / 1e3:7.2f}")
 
 
