@@ -215,15 +215,15 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     const int per_row = (int)(K * (kI8 ? 1 : 2) / kChunkBytes), chunks = M * per_row;
     u32x4 xv[XC][kLoadsPerChunk];
     int xdst[XC];
+    ChunkWalk cw((int)threadIdx.x, nthreads, per_row);
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         const int u = threadIdx.x + c * nthreads;
         const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, cc = uc - m * per_row;
 #pragma unroll
-        for (int h = 0; h < kLoadsPerChunk; ++h)
-            xv[c][h] = xg[((int64_t)m * per_row + cc) * kLoadsPerChunk + h];
-        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : M * xrow_bytes;
+        for (int h = 0; h < kLoadsPerChunk; ++h) xv[c][h] = xg[(int64_t)uc * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? cw.q * xrow_bytes + kChunkBytes * cw.r : M * xrow_bytes;
+        cw.next();
     }
     __builtin_amdgcn_sched_barrier(0);
     Tile5 t[U];
@@ -328,20 +328,21 @@ __global__ __launch_bounds__(1024) void gemv5_phased_kernel(const uint8_t* __res
     const int dummy = M * xrow_bytes + RT * nkt * NI * 64 * 4;
 
     const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);
-    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
+    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes;
     u32x4 xv[2][XC][kLoadsPerChunk];
     int xdst[XC];
+    ChunkWalk cw((int)threadIdx.x, nthreads, per_row);
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-        const int u = threadIdx.x + c * nthreads;
-        const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, cc = uc - m * per_row;
+        const bool in = cw.q < M;                                    // chunk u = threadIdx.x + c * nthreads
+        const int m = in ? cw.q : M - 1, cc = in ? cw.r : per_row - 1;
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph)
 #pragma unroll
             for (int h = 0; h < kLoadsPerChunk; ++h)
                 xv[ph][c][h] = xg[((int64_t)m * row_chunks + ph * per_row + cc) * kLoadsPerChunk + h];
-        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : dummy;
+        xdst[c] = in ? m * xrow_bytes + kChunkBytes * cc : dummy;
+        cw.next();
     }
     __builtin_amdgcn_sched_barrier(0);
     Tile5 t[2];

@@ -42,6 +42,32 @@ __device__ __forceinline__ uint32_t bfi32(uint32_t mask, uint32_t a, uint32_t b)
     return (a & mask) | (b & ~mask);
 }
 
+// Row q and column r of the chunks u = first + c * stride (c = 0, 1, ...) of
+// rows of `per_row` chunks, without a division per chunk: one division for
+// the first chunk, the stride's quotient and remainder (uniform), then one
+// add with a carry per step.  Activation staging runs 2..16 chunks per
+// thread, and a division by a run-time value costs about 25 VALU
+// instructions (four of them quarter-rate multiplies).
+struct ChunkWalk {
+    int q, r, dq, dr, per_row;
+    __device__ __forceinline__ ChunkWalk(int first, int stride, int per_row_) : per_row(per_row_)
+    {
+        q = first / per_row;
+        r = first - q * per_row;
+        dq = stride / per_row;
+        dr = stride - dq * per_row;
+    }
+    __device__ __forceinline__ void next()
+    {
+        r += dr;
+        q += dq;
+        if (r >= per_row) {
+            r -= per_row;
+            ++q;
+        }
+    }
+};
+
 // Interleave one nonzero word N and sign word S (weight i at bit
 // 16*(i&1) + (i>>1) in both) into two code words whose adjacent bit pairs are
 // (nonzero, sign) of one weight:

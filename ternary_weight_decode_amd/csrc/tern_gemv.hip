@@ -163,10 +163,9 @@ __global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __r
     {
         const int per_row = (int)(K >> 3);
         const int units = M * per_row;
-        for (int u = threadIdx.x; u < units; u += blockDim.x) {
-            const int m = u / per_row, c8 = u - m * per_row;
-            *(u32x4*)(xs + m * xstride + 8 * c8) = *(const u32x4*)(x + (int64_t)m * K + 8 * c8);
-        }
+        ChunkWalk cw((int)threadIdx.x, (int)blockDim.x, per_row);
+        for (int u = threadIdx.x; u < units; u += blockDim.x, cw.next())
+            *(u32x4*)(xs + cw.q * xstride + 8 * cw.r) = *(const u32x4*)(x + (int64_t)cw.q * K + 8 * cw.r);
     }
     __syncthreads();
 
@@ -259,15 +258,15 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     const int per_row = (int)(K * (kI8 ? 1 : 2) / kChunkBytes), chunks = M * per_row;
     u32x4 xv[XC][kLoadsPerChunk];
     int xdst[XC];
+    ChunkWalk cw((int)threadIdx.x, nthreads, per_row);
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
         const int u = threadIdx.x + c * nthreads;
         const int uc = u < chunks ? u : chunks - 1;
-        const int m = MT == 1 ? 0 : uc / per_row, cc = uc - m * per_row;   // MT = 1 runs M = 1 only
 #pragma unroll
-        for (int h = 0; h < kLoadsPerChunk; ++h)
-            xv[c][h] = xg[((int64_t)m * per_row + cc) * kLoadsPerChunk + h];
-        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : M * xrow_bytes;
+        for (int h = 0; h < kLoadsPerChunk; ++h) xv[c][h] = xg[(int64_t)uc * kLoadsPerChunk + h];
+        xdst[c] = u < chunks ? cw.q * xrow_bytes + kChunkBytes * cw.r : M * xrow_bytes;
+        cw.next();
     }
     // keep the activation loads ahead of the unit loads: waiting for them
     // must not wait for the weights
@@ -601,20 +600,21 @@ __global__ __launch_bounds__(1024) void gemv_phased_kernel(const uint8_t* __rest
     const int dummy = M * xrow_bytes + (RT * nkt + 1) * NI * 64 * 4;
 
     const int row_chunks = (int)(K * (kI8 ? 1 : 2) / kChunkBytes);  // chunks per activation row in memory
-    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes, chunks = M * per_row;
+    const int per_row = pk * (kI8 ? 1 : 2) / kChunkBytes;
     u32x4 xv[2][XC][kLoadsPerChunk];
     int xdst[XC];
+    ChunkWalk cw((int)threadIdx.x, nthreads, per_row);
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-        const int u = threadIdx.x + c * nthreads;
-        const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, cc = uc - m * per_row;
+        const bool in = cw.q < M;                                    // chunk u = threadIdx.x + c * nthreads
+        const int m = in ? cw.q : M - 1, cc = in ? cw.r : per_row - 1;
 #pragma unroll
         for (int ph = 0; ph < 2; ++ph)
 #pragma unroll
             for (int h = 0; h < kLoadsPerChunk; ++h)
                 xv[ph][c][h] = xg[((int64_t)m * row_chunks + ph * per_row + cc) * kLoadsPerChunk + h];
-        xdst[c] = u < chunks ? m * xrow_bytes + kChunkBytes * cc : dummy;
+        xdst[c] = in ? m * xrow_bytes + kChunkBytes * cc : dummy;
+        cw.next();
     }
     __builtin_amdgcn_sched_barrier(0);
     PlaneTile t[2];
@@ -735,15 +735,16 @@ __global__ __launch_bounds__(512) void gemv_phased3_kernel(const uint8_t* __rest
     const int dummy = M * xrow_bytes + nkt * NI * 64 * 4;
 
     const int row_chunks = (int)(K * 2 / 16);                        // 16-byte chunks per activation row
-    const int per_row = pk * 2 / 16, chunks = M * per_row;
+    const int per_row = pk * 2 / 16;
     int xsrc[XC], xdst[XC];
+    ChunkWalk cw((int)threadIdx.x, nthreads, per_row);
 #pragma unroll
     for (int c = 0; c < XC; ++c) {
-        const int u = threadIdx.x + c * nthreads;
-        const int uc = u < chunks ? u : chunks - 1;
-        const int m = uc / per_row, cc = uc - m * per_row;
+        const bool in = cw.q < M;                                    // chunk u = threadIdx.x + c * nthreads
+        const int m = in ? cw.q : M - 1, cc = in ? cw.r : per_row - 1;
         xsrc[c] = m * row_chunks + cc;
-        xdst[c] = u < chunks ? m * xrow_bytes + 16 * cc : dummy;
+        xdst[c] = in ? m * xrow_bytes + 16 * cc : dummy;
+        cw.next();
     }
     u32x4 xa[XC], xb[XC];
     auto load_x = [&](int ph, u32x4 (&v)[XC]) {

@@ -187,6 +187,43 @@ def _calls(vals, k, combine):
     return [combine(vals[i:i + k]) for i in range(0, len(vals) - k + 1, k)]
 
 
+def simds_per_sq(d: str):
+    """SIMDs served by one SQ_BUSY_CYCLES instance (one per shader engine): Simd_Count / Num_Shader_Banks
+    of the GPU agent in the run's agent-info CSV, or None."""
+    hits = sorted(glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True))
+    for path in hits:
+        for r in csv.DictReader(open(path)):
+            try:
+                simds, ses = int(r.get("Simd_Count") or 0), int(r.get("Num_Shader_Banks") or 0)
+            except ValueError:
+                continue
+            if simds > 0 and ses > 0 and "gfx" in (r.get("Name") or ""):
+                return simds / ses
+    return None
+
+
+def sq_text(med: dict, per_sq) -> str:
+    """SQ counters of one case: instructions per wave, the share of wave time spent waiting, and, with the
+    SIMDs per shader engine (SQ_BUSY_CYCLES is summed over the engines, so per engine it is about the
+    kernel's duration in cycles), the matrix cores' busy share per SIMD (SQ_VALU_MFMA_BUSY_CYCLES) and
+    the VALU issue share per SIMD (4 cycles per wave64 VALU instruction)."""
+    waves = med["SQ_WAVES"]
+    out = [f"waves {waves:7.0f}"]
+    for c, lab in (("SQ_INSTS_VALU", "valu"), ("SQ_INSTS_MFMA", "mfma"), ("SQ_INSTS_LDS", "lds"),
+                   ("SQ_INSTS_SALU", "salu")):
+        if c in med:
+            out.append(f"{lab}/wave {med[c] / waves:7.1f}")
+    if "SQ_WAIT_INST_ANY" in med and med.get("SQ_WAVE_CYCLES"):
+        out.append(f"wait {100 * med['SQ_WAIT_INST_ANY'] / med['SQ_WAVE_CYCLES']:5.1f}%")
+    if per_sq and med.get("SQ_BUSY_CYCLES"):
+        simd_cycles = med["SQ_BUSY_CYCLES"] * per_sq
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in med:
+            out.append(f"mfma busy {100 * med['SQ_VALU_MFMA_BUSY_CYCLES'] / simd_cycles:5.1f}%")
+        if "SQ_INSTS_VALU" in med:
+            out.append(f"valu issue {100 * 4 * med['SQ_INSTS_VALU'] / simd_cycles:5.1f}%")
+    return "  ".join(out)
+
+
 def cmd_runs(args):
     rows = bench_rows(args.bench)
     counters = glob.glob(os.path.join(args.dir[0], "**", "*counter_collection.csv"), recursive=True)
@@ -212,6 +249,7 @@ def cmd_runs(args):
     for (key, v), r in zip(runs, rows):
         base[unit_of(r)] = min(base.get(unit_of(r), len(v)), len(v))
     scale = dict(s.split("=") for s in args.scale)
+    per_sq = simds_per_sq(args.dir[0]) if counters else None
     for (key, v), r in zip(runs, rows):
         name, grid, wg = key
         k = max(1, round(len(v) / base[unit_of(r)]))
@@ -221,7 +259,10 @@ def cmd_runs(args):
         if counters:
             calls = _calls(v, k, lambda g: {c: sum(d[c] for d in g) for c in g[0]})
             med = {c: statistics.median(d[c] for d in calls) for c in sorted(calls[0])}
-            text = "  ".join(f"{c} {m:10.1f} KiB" for c, m in med.items())
+            if "SQ_WAVES" in med:
+                text = sq_text(med, per_sq)
+            else:
+                text = "  ".join(f"{c} {m:10.1f} KiB" for c, m in med.items())
             if all(c in scale for c in med) and "bytes" in r:
                 meas = sum(m * 1024 * float(scale[c]) for c, m in med.items())
                 text += f"  -> {meas / 1e6:8.3f} MB  algorithmic {r['bytes'] / 1e6:8.3f} MB  " \

@@ -85,3 +85,30 @@ def test_runs_merges_counter_directories(tmp_path, capsys):
              "--passes", "2", "--scale", "FETCH_SIZE=1.0", "--scale", "WRITE_SIZE=1.0"])
     line = capsys.readouterr().out
     assert "FETCH_SIZE     1500.0 KiB" in line and "WRITE_SIZE      500.0 KiB" in line and "ratio 1.000" in line
+
+
+def test_runs_sq_counters_per_wave(tmp_path, capsys):
+    d = tmp_path / "sq" / "host"
+    d.mkdir(parents=True)
+    vals = {"SQ_WAVES": 8.0, "SQ_INSTS_VALU": 800.0, "SQ_INSTS_MFMA": 160.0, "SQ_WAIT_INST_ANY": 250.0,
+            "SQ_WAVE_CYCLES": 1000.0, "SQ_BUSY_CYCLES": 100.0, "SQ_VALU_MFMA_BUSY_CYCLES": 80.0}
+    with open(d / "run_counter_collection.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Workgroup_Size", "Counter_Name",
+                               "Counter_Value"])
+        w.writeheader()
+        for i in range(2):
+            for cn, v in vals.items():
+                w.writerow({"Dispatch_Id": i + 1, "Kernel_Name": "void gemv_a(int)", "Grid_Size": 512,
+                            "Workgroup_Size": 512, "Counter_Name": cn, "Counter_Value": v})
+    with open(d / "run_agent_info.csv", "w", newline="") as f:
+        w = csv.DictWriter(f, ["Name", "Simd_Count", "Num_Shader_Banks"])
+        w.writeheader()
+        w.writerow({"Name": "AMD EPYC", "Simd_Count": 0, "Num_Shader_Banks": 0})
+        w.writerow({"Name": "gfx950", "Simd_Count": 8, "Num_Shader_Banks": 2})
+    out = tmp_path / "bench.out"
+    out.write_text(json.dumps({"rows": [{"proj": "q", "act": "bf16", "M": 8}]}) + "\n")
+    rs.main(["runs", str(tmp_path / "sq"), "--bench", str(out), "--passes", "2"])
+    line = capsys.readouterr().out
+    assert "valu/wave   100.0" in line and "mfma/wave    20.0" in line
+    # busy 100 cycles summed over 2 engines of 4 SIMDs: 400 SIMD-cycles; 80 MFMA cycles, 800 VALU x 4
+    assert "wait  25.0%" in line and "mfma busy  20.0%" in line and "valu issue 800.0%" in line
