@@ -17,18 +17,28 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_traffic_figure_follows_the_kernel_sources(tmp_path):
-    # the committed summary was taken with the current GEMV sources: the figure applies
-    got = bench.measured_traffic(ROOT, "fused")
-    assert got is not None and 12.8e6 < got < 13.5e6
-    # other compositions have no counter figure
-    assert bench.measured_traffic(ROOT, "separate") is None
-    # a changed source voids it: copy the tree's summary and sources, edit one source
+    """The figure is read from the counter summary only while the GEMV sources hash to the value
+    recorded with the counters: a copy of the sources, a summary written for them, then one edit."""
+    import hashlib
     src_dir = tmp_path / "ternary_weight_decode_amd" / "csrc"
     src_dir.mkdir(parents=True)
     (tmp_path / "profiles").mkdir()
-    (tmp_path / bench.TRAFFIC_PROFILE).write_text(open(os.path.join(ROOT, bench.TRAFFIC_PROFILE)).read())
+    blob = b""
     for f in bench.GEMV_SOURCES:
-        (src_dir / f).write_bytes(open(os.path.join(ROOT, "ternary_weight_decode_amd", "csrc", f), "rb").read())
-    assert bench.measured_traffic(str(tmp_path), "fused") == got
-    (src_dir / bench.GEMV_SOURCES[0]).write_bytes((src_dir / bench.GEMV_SOURCES[0]).read_bytes() + b"\n")
+        data = open(os.path.join(ROOT, "ternary_weight_decode_amd", "csrc", f), "rb").read()
+        (src_dir / f).write_bytes(data)
+        blob += data
+    summary = ("ternary GEMV per launch (mean over the four launch kinds of a layer): HBM 13.023 MB, "
+               "algorithmic 12.863 MB, ratio 1.012\n"
+               f"kernel sources sha256 ({', '.join(bench.GEMV_SOURCES)}) at measurement: "
+               f"{hashlib.sha256(blob).hexdigest()}\n")
+    (tmp_path / bench.TRAFFIC_PROFILE).write_text(summary)
+    assert bench.measured_traffic(str(tmp_path), "fused") == 13023000
+    # other compositions have no counter figure
+    assert bench.measured_traffic(str(tmp_path), "separate") is None
+    # a changed source voids it
+    (src_dir / bench.GEMV_SOURCES[0]).write_bytes(blob[:10])
     assert bench.measured_traffic(str(tmp_path), "fused") is None
+    # and the committed summary names the same sources in the same form
+    text = open(os.path.join(ROOT, bench.TRAFFIC_PROFILE)).read()
+    assert f"kernel sources sha256 ({', '.join(bench.GEMV_SOURCES)}) at measurement:" in text
