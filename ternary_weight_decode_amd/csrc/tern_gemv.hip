@@ -225,7 +225,9 @@ __global__ __launch_bounds__(1024) void gemv_bf16_fast_kernel(const uint8_t* __r
 //              fp32 (and written to acc_dbg when it is given); y = s_x * sum.
 // XC = activation chunks per thread (16 bytes of bf16, or 32 bytes of int8
 // staged in the decoded byte order); the launcher checks that they cover x.
-template <bool kI8, int MT, int U, int XC>
+// kReuse: the partials overwrite x's LDS once every wave has computed (a
+// second barrier; x and the partials need not fit side by side).
+template <bool kI8, int MT, int U, int XC, bool kReuse = false>
 __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
                                                             const void* __restrict__ x, const float* __restrict__ s_x,
                                                             int M, float* __restrict__ y,
@@ -250,7 +252,7 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
     const int xrow_bytes = kI8 ? (int)K + 16 : ((int)K + 8) * 2;   // staged bytes per activation row
-    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [unit + 1 spare][NI][64]
+    float* red = (float*)(smem + (kReuse ? 0 : (size_t)M * xrow_bytes));   // [unit + 1 spare][NI][64]
 
     // activations first; a chunk index past the end re-loads the last chunk
     // and stores it to a dummy slot (the start of the partials, written only
@@ -345,6 +347,7 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
     // every unit is computed (a unit past the end repeats a real one and
     // leaves its partial in the spare slot after the real ones), so no load
     // is consumed behind a branch
+    f32x4 keep[kReuse ? U : 1];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int lrt = ulrt[i], kt = ukt[i];
@@ -373,10 +376,23 @@ __global__ __launch_bounds__(1024) void gemv_oneshot_kernel(const uint8_t* __res
         } else {
             bf16_tile<MT>(t[i], (const uint16_t*)xrow + kt * kTileK, 4, acc);
         }
-        const int slot = uok[i] ? lrt * nkt + kt : units;
+        if constexpr (kReuse) {
+            keep[i] = acc;
+        } else {
+            const int slot = uok[i] ? lrt * nkt + kt : units;
 #pragma unroll
-        for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];   // all lanes: no branch
+            for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];   // all lanes: no branch
+        }
         __builtin_amdgcn_sched_barrier(0);   // unit i+1's decode waits for its own loads only
+    }
+    if constexpr (kReuse) {
+        __syncthreads();                     // every wave is done with x
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int slot = uok[i] ? ulrt[i] * nkt + ukt[i] : units;
+#pragma unroll
+            for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = keep[i][q];
+        }
     }
     __syncthreads();
 
@@ -1005,6 +1021,23 @@ static hipError_t oneshot_dispatch(const OneShot& c, hipStream_t stream, const u
     return hipErrorNotSupported;
 }
 
+// the partials-over-x instances: bf16 rows above 8 whose x and partials do not fit side by side
+static hipError_t oneshot_reuse_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N,
+                                         int64_t K, const void* x, int M, float* y)
+{
+#define TERN_REUSE_CASE(UU, XX)                                                                                 \
+    if (c.U == UU && c.XC == XX) {                                                                              \
+        if (!oneshot_resident(gemv_oneshot_kernel<false, 16, UU, XX, true>, c)) return hipErrorNotSupported;    \
+        gemv_oneshot_kernel<false, 16, UU, XX, true><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds, stream>>>( \
+            packed, N, K, x, nullptr, M, y, nullptr);                                                           \
+        return hipGetLastError();                                                                               \
+    }
+    TERN_REUSE_CASE(2, 8) TERN_REUSE_CASE(3, 8) TERN_REUSE_CASE(4, 8)
+    TERN_REUSE_CASE(2, 16) TERN_REUSE_CASE(3, 16)
+#undef TERN_REUSE_CASE
+    return hipErrorNotSupported;
+}
+
 // The ternary instances with M <= 4 use 56-65, 62-70, 75-81 and 87-91 VGPRs
 // for U = 1..4 (the occupancy query has the last word).
 static OneShotShape oneshot_shape(int64_t K, bool i8)
@@ -1054,6 +1087,7 @@ static hipError_t launch_oneshot(bool i8, const uint8_t* packed, int64_t N, int6
 {
     OneShot c;
     if (!pick_oneshot(N, K, M, oneshot_shape(K, i8), c)) return hipErrorNotSupported;
+    if (c.reuse) return oneshot_reuse_dispatch(c, stream, packed, N, K, x, (int)M, y);
     if (!i8 && M == 1) return m1_dispatch(c, stream, packed, N, K, (const uint16_t*)x, y);
     if (!i8 && M <= 8 && c.R == 1 && c.U <= 2) {
         // per-wave slices (the picker sized LDS for them)

@@ -28,7 +28,8 @@ struct OneShot {
     int R, nw, U, XC;
     int64_t grid;
     size_t lds;
-    bool rounds;      // the grid runs in several rounds (no split fits one)
+    bool rounds = false;   // the grid runs in several rounds (no split fits one)
+    bool reuse = false;    // the partials overwrite x's LDS after the compute (x and partials exceed a CU side by side)
 };
 
 // units per wave for a workgroup of `units` units
@@ -84,29 +85,44 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
                                            : (size_t)(nw * U * mr * (s.m1_slice_bytes + 16));
         return x_lds + (size_t)(units + 1) * ni * 64 * 4;
     };
-    int64_t best_max = -1, best_dist = 0, best_wg = 0;
+    // bf16 rows above 8 in one resident round: the partials may overwrite x after the compute
+    // (x, the dummy slot of chunks past its end, and the partials, whichever is larger)
+    auto reuse_lds_of = [&](int64_t units) {
+        const size_t xs = (size_t)(M * s.x_row_bytes) + 16, ps = (size_t)(units + 1) * ni * 64 * 4;
+        return xs > ps ? xs : ps;
+    };
+    // the partials over x only where no split fits one round side by side
+    // (8B fused gate|up at M = 13..16, whose x alone is up to 128 KiB)
+    const bool can_reuse = s.chunk_bytes == 16 && s.m1_slice_bytes > 0 && M > 8;
     c.R = 0;
-    for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
-        const int64_t units = R * nkt, U = oneshot_u(units);
-        if (U > 4) break;
-        const int64_t nw = (units + U - 1) / U;
-        const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
-        if (per_cu * nw > 4 * s.waves_per_simd[U]) continue;                  // not resident in one round
-        if ((size_t)per_cu * lds_of(units, R) > (size_t)kCuLds) continue;    // LDS of the workgroups on a CU
-        const int64_t max_units = per_cu * units;
-        const int64_t dist = units > 16 ? units - 16 : 16 - units;
-        // among equal critical paths: at M > 1 one workgroup per CU first (x, M*K
-        // elements, staged once per CU) as long as a wave keeps at most two units, then
-        // the workgroup closest to 16 units
-        const int64_t wg = M > 1 && per_cu == 1 && U <= 2 ? 0 : 1;
-        if (best_max < 0 || max_units < best_max ||
-            (max_units == best_max && (wg < best_wg || (wg == best_wg && dist < best_dist)))) {
-            best_max = max_units;
-            best_dist = dist;
-            best_wg = wg;
-            c.R = R;
+    c.reuse = false;
+    for (int pass = 0; pass < (can_reuse ? 2 : 1) && c.R == 0; ++pass) {
+        const bool reuse = pass == 1;
+        int64_t best_max = -1, best_dist = 0, best_wg = 0;
+        for (int R = 1; R <= 64 && R * nkt <= 64; ++R) {
+            const int64_t units = R * nkt, U = oneshot_u(units);
+            if (U > 4) break;
+            const int64_t nw = (units + U - 1) / U;
+            const int64_t grid = (nrt + R - 1) / R, per_cu = (grid + cus - 1) / cus;
+            if (per_cu * nw > 4 * s.waves_per_simd[U]) continue;              // not resident in one round
+            const size_t lds = reuse ? reuse_lds_of(units) : lds_of(units, R);
+            if ((size_t)per_cu * lds > (size_t)kCuLds) continue;              // LDS of the workgroups on a CU
+            const int64_t max_units = per_cu * units;
+            const int64_t dist = units > 16 ? units - 16 : 16 - units;
+            // among equal critical paths: at M > 1 one workgroup per CU first (x, M*K
+            // elements, staged once per CU) as long as a wave keeps at most two units, then
+            // the workgroup closest to 16 units
+            const int64_t wg = M > 1 && per_cu == 1 && U <= 2 ? 0 : 1;
+            if (best_max < 0 || max_units < best_max ||
+                (max_units == best_max && (wg < best_wg || (wg == best_wg && dist < best_dist)))) {
+                best_max = max_units;
+                best_dist = dist;
+                best_wg = wg;
+                c.R = R;
+                c.reuse = reuse;
+            }
+            if (grid == 1) break;
         }
-        if (grid == 1) break;
     }
     c.rounds = false;
     if (c.R == 0) {
@@ -137,7 +153,9 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     const int64_t xc_max = s.chunk_bytes == 16 && M > 8 && !c.rounds && c.U <= 3 ? 16 : 8;
     if (xc > xc_max || (xc > 4 && M <= 2)) return false;
     c.XC = xc <= 1 ? 1 : (xc <= 2 ? 2 : (xc <= 4 ? 4 : (xc <= 8 ? 8 : 16)));
-    c.lds = lds_of(units, c.R);
+    // the partials-over-x instances: two to four units per wave, 8 or 16 chunks
+    if (c.reuse && (c.U < 2 || c.XC < 8 || (c.XC == 16 && c.U > 3))) return false;
+    c.lds = c.reuse ? reuse_lds_of(units) : lds_of(units, c.R);
     return c.lds <= (size_t)kCuLds;
 }
 

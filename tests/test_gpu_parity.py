@@ -582,6 +582,26 @@ def test_gemv_bf16_sixteen_chunks(tw, n, k, m):
     assert err.max() < 1e-4
 
 
+@pytest.mark.parametrize("n,k,m", [(21000, 4096, 14), (20001, 4096, 16), (24576, 4096, 16)])
+def test_gemv_bf16_partials_over_x(tw, n, k, m):
+    """bf16 activations of 9..16 rows whose x and the partials of a one-round
+    split do not fit a CU's LDS side by side (the 8B fused gate|up at M = 16):
+    the one-pass kernel writes the partials over x after a second barrier.
+    20001 rows: 16 staged chunks and a last workgroup with tiles past the end;
+    the fused shape on sampled rows, the others in full."""
+    c = tw.tern_gemv_config(n, k, m)
+    side = m * (k + 8) * 2 + (c["R"] * (k // 512) + 1) * 4 * 64 * 4
+    assert c is not None and not c["rounds"] and side > 160 * 1024 and c["lds"] < side
+    t, s, x = gen(n, k, m, seed=13 * n + m)
+    y = host(tw.tern_gemv(gpu_pack(tw, t, s), n, k, dev(x)))
+    rows = np.arange(n) if n < 24000 else np.unique(np.r_[np.arange(0, 40), np.random.default_rng(6).choice(n, 400),
+                                                           np.arange(n - 40, n)])
+    y64, _ = oracle.gemv_bf16(oracle.pack(t[rows], s[rows]), len(rows), k, x)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    err = np.abs(y[:, rows] - y64).max(axis=0) / (np.abs(y64).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
 @pytest.mark.parametrize("n,k,m", [(4096, 12288, 16), (1005, 12288, 9), (37, 12288, 12), (300, 12288, 13)])
 def test_gemv_bf16_three_phase(tw, n, k, m):
     """bf16 activations of more than 8 rows whose halves of K exceed LDS (the

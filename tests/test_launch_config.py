@@ -51,7 +51,13 @@ def test_picker_invariants(kind):
             assert c["lds"] == c["waves"] * c["U"] * mr * 1040 + (units + 1) * ni * 64 * 4, where
         else:
             xrow = k + 16 if i8 else (k + 8) * 2
-            assert c["lds"] == m * xrow + (units + 1) * ni * 64 * 4, where
+            side = m * xrow + (units + 1) * ni * 64 * 4
+            if c["lds"] != side:
+                # bf16 rows above 8 with no side-by-side split in one round: the partials
+                # overwrite x after the compute (x plus its dummy slot, or the partials)
+                assert kind == "ternary_bf16" and m > 8 and not c["rounds"], where
+                assert c["lds"] == max(m * xrow + 16, (units + 1) * ni * 64 * 4), where
+                assert 2 <= c["U"] and c["XC"] in (8, 16), where
             chunk = 32 if i8 else 16
             assert c["XC"] * 64 * c["waves"] * chunk >= m * k * (1 if i8 else 2), where       # x fully staged
         assert c["MT"] >= m and (c["XC"] < 8 or c["MT"] == 16), where
