@@ -184,8 +184,9 @@ __global__ void pack5_kernel(const int8_t* __restrict__ lv, const float* __restr
 // (the first before x is staged, the rest right after), partials are summed
 // in LDS in k-tile order.  kI8: int8 activations q with row scales s_x (staged
 // in the decoded byte order), y = s_x * sum.  XC = activation chunks per
-// thread (16 bytes of bf16, or 32 bytes of int8).
-template <bool kI8, int MT, int U, int XC>
+// thread (16 bytes of bf16, or 32 bytes of int8).  kReuse: the partials
+// overwrite x's LDS once every wave has computed (a second barrier).
+template <bool kI8, int MT, int U, int XC, bool kReuse = false>
 __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
                                                              const void* __restrict__ x,
                                                              const float* __restrict__ s_x, int M,
@@ -207,7 +208,7 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
     const TERN_GLOBAL uint32_t* scales = (const TERN_GLOBAL uint32_t*)(packed + t5_plane_bytes(N, K));
     const TERN_GLOBAL u32x4* xg = (const TERN_GLOBAL u32x4*)x;
     const int xrow_bytes = kI8 ? (int)K + 16 : ((int)K + 8) * 2;   // staged bytes per activation row
-    float* red = (float*)(smem + (size_t)M * xrow_bytes);           // [unit + 1 spare][NI][64]
+    float* red = (float*)(smem + (kReuse ? 0 : (size_t)M * xrow_bytes));   // [unit + 1 spare][NI][64]
 
     // activations first; a chunk index past the end re-loads the last chunk
     // and stores it to a dummy slot (the start of the partials, written only
@@ -257,6 +258,7 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
 
     const int mrow = r < M ? r : M - 1;
     const uint8_t* xrow = smem + mrow * xrow_bytes + (kI8 ? 32 : 64) * g;
+    f32x4 keep[kReuse ? U : 1];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int j = wave + i * nw;
@@ -271,10 +273,24 @@ __global__ __launch_bounds__(1024) void gemv5_oneshot_kernel(const uint8_t* __re
         } else {
             tile5_bf16<MT>(t[i], (const uint16_t*)xrow + kt * kTileK, acc);
         }
-        const int slot = j < units ? j : units;
+        if constexpr (kReuse) {
+            keep[i] = acc;
+        } else {
+            const int slot = j < units ? j : units;
 #pragma unroll
-        for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];
+            for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = acc[q];
+        }
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (kReuse) {
+        __syncthreads();                     // every wave is done with x
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int j = wave + i * nw;
+            const int slot = j < units ? j : units;
+#pragma unroll
+            for (int q = 0; q < NI; ++q) red[(slot * NI + q) * 64 + lane] = keep[i][q];
+        }
     }
     __syncthreads();
 
@@ -497,13 +513,30 @@ static hipError_t gemv5_oneshot_dispatch(const OneShot& c, hipStream_t stream, c
     return hipErrorNotSupported;
 }
 
+// the partials-over-x instances (bf16 rows above 8 whose x and partials do not fit side by side)
+static hipError_t gemv5_reuse_dispatch(const OneShot& c, hipStream_t stream, const uint8_t* packed, int64_t N,
+                                       int64_t K, const void* x, int M, float* y)
+{
+#define TERN5_REUSE_CASE(UU, XX)                                                                                \
+    if (c.U == UU && c.XC == XX) {                                                                              \
+        if (!oneshot_resident(gemv5_oneshot_kernel<false, 16, UU, XX, true>, c)) return hipErrorNotSupported;   \
+        gemv5_oneshot_kernel<false, 16, UU, XX, true><<<dim3((unsigned)c.grid), dim3(64 * c.nw), c.lds,         \
+                                                        stream>>>(packed, N, K, x, nullptr, M, y, nullptr);    \
+        return hipGetLastError();                                                                               \
+    }
+    TERN5_REUSE_CASE(2, 8) TERN5_REUSE_CASE(3, 8) TERN5_REUSE_CASE(4, 8)
+    TERN5_REUSE_CASE(2, 16) TERN5_REUSE_CASE(3, 16)
+#undef TERN5_REUSE_CASE
+    return hipErrorNotSupported;
+}
+
 // waves of U = 1..4 units per SIMD (registers: bf16 60, 77, 95-99 and
 // 111-115 VGPRs, int8 68, 74, 90 and 106; the occupancy query has the last
 // word)
 bool gemv5_oneshot_config(int64_t N, int64_t K, int64_t M, bool i8, OneShot& c)
 {
-    const OneShotShape s = i8 ? OneShotShape{K + 16, K, 32, {0, 7, 6, 5, 4}}
-                              : OneShotShape{(K + 8) * 2, 2 * K, 16, {0, 8, 6, 4, 4}};
+    const OneShotShape s = i8 ? OneShotShape{K + 16, K, 32, {0, 7, 6, 5, 4}, 0, false}
+                              : OneShotShape{(K + 8) * 2, 2 * K, 16, {0, 8, 6, 4, 4}, 0, true};
     return pick_oneshot(N, K, M, s, c);
 }
 
@@ -567,7 +600,9 @@ static hipError_t launch_gemv5(const uint8_t* packed, int64_t N, int64_t K, cons
         // 8 activation chunks per thread are instantiated for MT = 16 only
         const bool wide = M > 4 || c.XC == 8;
         hipError_t e;
-        if (wide) e = gemv5_oneshot_dispatch<kI8, 16>(c, stream, packed, N, K, x, s_x, m, y, acc);
+        // a partials-over-x configuration sized its LDS for that layout only
+        if (c.reuse) e = gemv5_reuse_dispatch(c, stream, packed, N, K, x, m, y);
+        else if (wide) e = gemv5_oneshot_dispatch<kI8, 16>(c, stream, packed, N, K, x, s_x, m, y, acc);
         else if (M == 1) e = gemv5_oneshot_dispatch<kI8, 1>(c, stream, packed, N, K, x, s_x, m, y, acc);
         else if (M == 2) e = gemv5_oneshot_dispatch<kI8, 2>(c, stream, packed, N, K, x, s_x, m, y, acc);
         else e = gemv5_oneshot_dispatch<kI8, 4>(c, stream, packed, N, K, x, s_x, m, y, acc);

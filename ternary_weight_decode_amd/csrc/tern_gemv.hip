@@ -1043,7 +1043,7 @@ static hipError_t oneshot_reuse_dispatch(const OneShot& c, hipStream_t stream, c
 static OneShotShape oneshot_shape(int64_t K, bool i8)
 {
     return OneShotShape{i8 ? K + 16 : (K + 8) * 2, i8 ? K : 2 * K, i8 ? 32 : 16, {0, 8, 7, 6, 5},
-                        i8 ? 0 : kTileK * 2};
+                        i8 ? 0 : kTileK * 2, !i8};
 }
 
 // the one-pass path for M <= 16 when it applies; hipErrorNotSupported otherwise

@@ -46,6 +46,7 @@ struct OneShotShape {
     int64_t waves_per_simd[5];// waves of U = 1..4 units that fit on a SIMD (registers)
     int64_t m1_slice_bytes;   // > 0: at M = 1 every wave stages only the activation slices of its
                               // own units (this many bytes per unit) instead of the whole row
+    bool reuse_ok;            // bf16 rows above 8: partials may overwrite x after the compute
 };
 
 // R row tiles per workgroup is chosen to minimise the largest number of
@@ -93,7 +94,7 @@ inline bool pick_oneshot(int64_t N, int64_t K, int64_t M, const OneShotShape& s,
     };
     // the partials over x only where no split fits one round side by side
     // (8B fused gate|up at M = 13..16, whose x alone is up to 128 KiB)
-    const bool can_reuse = s.chunk_bytes == 16 && s.m1_slice_bytes > 0 && M > 8;
+    const bool can_reuse = s.reuse_ok && s.chunk_bytes == 16 && M > 8;
     c.R = 0;
     c.reuse = false;
     for (int pass = 0; pass < (can_reuse ? 2 : 1) && c.R == 0; ++pass) {

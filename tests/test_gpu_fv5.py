@@ -138,12 +138,32 @@ def test_gemv5_sixteen_chunks(tw, n, k, m):
     assert err.max() < 1e-4
 
 
-@pytest.mark.parametrize("n,k,m", [(12300, 4096, 16), (24576, 4096, 15)])
+@pytest.mark.parametrize("n,k,m", [(12300, 4096, 16), (21000, 4096, 14), (24576, 4096, 16)])
+def test_gemv5_partials_over_x(tw, n, k, m):
+    """bf16 M = 14..16 at K = 4096 where x and the partials of a one-round
+    split do not fit side by side (the 8B fused gate|up shape): the one-pass
+    kernel with the partials written over x after a second barrier; 12300 and
+    21000 rows in full (the last workgroup with tiles past the end), the fused
+    shape on sampled rows."""
+    c = tw.tern_gemv_config(n, k, m, "fv5_bf16")
+    side = m * (k + 8) * 2 + (c["R"] * (k // 512) + 1) * 4 * 64 * 4
+    assert not c["rounds"] and side > 160 * 1024 and c["lds"] < side
+    lv, lo, hi, x = gen(n, k, m, seed=17 * n + m)
+    y = host(tw.tern5_gemv(gpu_pack(tw, lv, lo, hi), n, k, dev(x)))
+    rows = np.arange(n) if n < 24000 else np.unique(np.r_[np.arange(0, 40), np.random.default_rng(7).choice(n, 300),
+                                                           np.arange(n - 40, n)])
+    want, _ = fv5.gemv_bf16_levels(lv[rows], lo[rows], hi[rows], x)
+    assert rel_l2(y[:, rows], want) < TOL
+    err = np.abs(y[:, rows] - want).max(axis=0) / (np.abs(want).max(axis=0) + 1e-3)
+    assert err.max() < 1e-4
+
+
+@pytest.mark.parametrize("n,k,m", [(4000, 8192, 12), (6150, 8192, 10)])
 def test_gemv5_two_phase_two_row_tiles(tw, n, k, m):
-    """bf16 M = 15..16 at K = 4096 beyond every one-pass split (the 8B fused
-    gate|up shape): the two-phase kernel with two row tiles per workgroup
-    (12300 rows: the last workgroup's second tile past the end); 12300 rows
-    against the oracle in full, the fused shape on sampled rows."""
+    """bf16 M = 10..15 at K = 8192, x beyond LDS and a half of it more than 8
+    chunks per thread with one row tile per workgroup: the two-phase kernel
+    with two row tiles per workgroup (6150 rows: the last workgroup's second
+    tile past the end); every output against the oracle."""
     c = tw.tern_gemv_config(n, k, m, "fv5_bf16_phased")
     assert tw.tern_gemv_config(n, k, m, "fv5_bf16") is None and c is not None and c["R"] == 2
     lv, lo, hi, x = gen(n, k, m, seed=9 * n + m)

@@ -55,7 +55,7 @@ def test_picker_invariants(kind):
             if c["lds"] != side:
                 # bf16 rows above 8 with no side-by-side split in one round: the partials
                 # overwrite x after the compute (x plus its dummy slot, or the partials)
-                assert kind == "ternary_bf16" and m > 8 and not c["rounds"], where
+                assert kind in ("ternary_bf16", "fv5_bf16") and m > 8 and not c["rounds"], where
                 assert c["lds"] == max(m * xrow + 16, (units + 1) * ni * 64 * 4), where
                 assert 2 <= c["U"] and c["XC"] in (8, 16), where
             chunk = 32 if i8 else 16
@@ -109,14 +109,20 @@ def test_phased_picker_invariants(kind):
     if fam == "fv5":
         c = tw.tern_gemv_config(4096, 12288, 16, "fv5_int8_phased")
         assert c is not None and c["waves"] == 12 and c["XC"] == 4
-    # two row tiles per workgroup: the five-level format on the 8B fused gate|up (24576 x 4096) at
-    # bf16 M = 15 and 16 (x beyond any one-pass split); the ternary one only where x does not fit the
-    # persistent fast path either (K = 8192 at M = 9..15), the fast path taking the fused gate|up
+    # the 8B fused gate|up (24576 x 4096) at bf16 M = 15 and 16: the one-pass split with the partials
+    # over x (six row tiles per workgroup, one round); two row tiles per workgroup in the two-phase
+    # kernel where x exceeds LDS: the five-level format at K = 8192, M = 10..15, the ternary one only
+    # where x does not fit the persistent fast path either (K = 8192 at M = 9..15)
     if fam == "fv5":
         for m in (15, 16):
-            assert tw.tern_gemv_config(24576, 4096, m, "fv5_bf16") is None
-            c = tw.tern_gemv_config(24576, 4096, m, "fv5_bf16_phased")
-            assert c is not None and (c["R"], c["waves"], c["XC"], c["grid"]) == (2, 8, 8, 768), (m, c)
+            assert tw.tern_gemv_config(24576, 4096, m, "fv5_bf16_phased") is None
+            c = tw.tern_gemv_config(24576, 4096, m, "fv5_bf16")
+            assert c is not None and (c["R"], c["waves"], c["U"], c["XC"], c["grid"]) == (6, 16, 3, 8, 256), (m, c)
+            assert c["lds"] == max(m * (4096 + 8) * 2 + 16, 49 * 4 * 64 * 4), (m, c)
+        for m in (10, 12):
+            assert tw.tern_gemv_config(4000, 8192, m, "fv5_bf16") is None
+            c = tw.tern_gemv_config(4000, 8192, m, "fv5_bf16_phased")
+            assert c is not None and (c["R"], c["waves"], c["XC"], c["grid"]) == (2, 16, 8, 125), (m, c)
     else:
         assert tw.tern_gemv_config(24576, 4096, 16, "ternary_bf16_phased") is None
         for m in (9, 15):
