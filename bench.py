@@ -107,9 +107,14 @@ class Step:
                 log_(f"generated and packed {gi + 1}/{len(groups)} layers ({time.time() - t0:.1f}s)")
         w, rs, xh = synth.head_inputs(config)
         v, k = w.shape
-        self.head = (torch.from_numpy(w).cuda(), torch.from_numpy(rs).cuda(),
+        # the head is stored in its packed layout (row groups of 64, read workgroup-contiguously);
+        # the logits are those of the row-major head bit for bit
+        w_dev = torch.from_numpy(w).cuda()
+        self.head = (tw.i8_head_pack(w_dev), torch.from_numpy(rs).cuda(),
                      torch.from_numpy(xh.view(np.int16)).cuda(), torch.empty((1, v), dtype=torch.float32,
                                                                              device="cuda"))
+        del w_dev
+        self.head_vk = (v, k)
         self.head_bytes = v * k + 4 * v + 2 * k + 4 * v
         self.tern_bytes = sum(l[6] for l in self.launches)
         self.bytes = self.tern_bytes + self.head_bytes
@@ -124,6 +129,7 @@ class Step:
         c.launches = [(kind, p.clone(), n, k, x.clone(), y.clone(), b, lab)
                       for (kind, p, n, k, x, y, b, lab) in self.launches]
         c.head = tuple(t.clone() for t in self.head)
+        c.head_vk = self.head_vk
         c.head_bytes, c.tern_bytes, c.bytes = self.head_bytes, self.tern_bytes, self.bytes
         return c
 
@@ -134,8 +140,8 @@ class Step:
                 tw.tern_gemv(p, n, k, x, y=y)
 
     def run_head(self):
-        w, rs, xh, yh = self.head
-        self.tw.i8_head_gemv(w, rs, xh, y=yh)
+        wp, rs, xh, yh = self.head
+        self.tw.i8_head_gemv_packed(wp, rs, *self.head_vk, xh, y=yh)
 
     def run(self):
         self.run_tern()
@@ -578,9 +584,13 @@ def mode_head(args, tw, synth, torch):
     # block-scaled (FV5B-style) scales of the same rows: one fp32 per 256 weights
     S = torch.from_numpy(np.random.default_rng(11).uniform(0.002, 0.02, (v, k // 256)).astype(np.float32)).cuda()
     row_bytes, blk_bytes = v * k + 4 * v, v * k + 4 * v * (k // 256)
+    packed = [tw.i8_head_pack(c) for c in copies]
+    pk = {id(c): p for c, p in zip(copies, packed)}
     runs = {
         "head_bf16": (lambda c: tw.i8_head_gemv(c, RS, x, y=y), row_bytes),
         "head_int8": (lambda c: tw.i8_head_gemv_i8(c, RS, q, sx, y=y), row_bytes),
+        "head_bf16_packed": (lambda c: tw.i8_head_gemv_packed(pk[id(c)], RS, v, k, x, y=y), row_bytes),
+        "head_int8_packed": (lambda c: tw.i8_head_gemv_packed_i8(pk[id(c)], RS, v, k, q, sx, y=y), row_bytes),
         "head_argmax_bf16": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws), row_bytes),
         "head_argmax_bf16_with_logits": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws, logits=y), row_bytes),
         "head_argmax_int8": (lambda c: tw.i8_head_argmax_i8(c, RS, q, sx, workspace=ws), row_bytes),

@@ -66,7 +66,7 @@ typedef enum {
     TERN_E_DEVICE = 5   /* the current device is not gfx950 */
 } tern_status;
 
-#define TERN_ABI_VERSION 9
+#define TERN_ABI_VERSION 10
 #define TERN_MAX_M_GEMV 16   /* activation rows per tern_gemv / tern_gemv_i8 / i8_head_gemv call */
 
 /* Human-readable name of a tern_status value (static string). */
@@ -151,6 +151,37 @@ int i8_head_gemv(const int8_t* W, const float* row_scale, int64_t V, int64_t K, 
  *   s_x fp32 [M];  acc_dbg NULL or int32 [M][V]. */
 int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
                     const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
+
+/* The int8 head over a packed copy of W, for the logits of i8_head_gemv /
+ * i8_head_gemv_i8 (bit for bit those of the row-major single-pass kernel,
+ * which i8_head_argmax[_i8] and, up to 48 KiB of activations, i8_head_gemv
+ * run: every lane multiplies the same weights in the same order; the same
+ * accuracy otherwise) at a higher read rate: the head is the
+ * largest tensor of a decode step and runs on the DRAM roofline ([P2]
+ * section "뉴트리노 엔진: 토큰 하나의 시간은 어디로 가는가").
+ *
+ * i8_head_packed_bytes: bytes of the packed copy, ceil(V/64)*64*K, or -1
+ * when 1 <= V <= 0xFFFFFFF0 and 128 <= K <= 2^20 with K % 128 == 0 fail.
+ *
+ * i8_head_pack: W int8 [V][K] row-major -> packed (caller-allocated, 16-byte
+ * aligned, i8_head_packed_bytes long).  Layout: row groups of 64 (rows past V
+ * are zero); within a group, for each 128-k unit j, for each 16-row tile w of
+ * the group, 2048 bytes: at 16*l (l = r + 16*g, r < 16, g < 4) bytes
+ * 128j + 16g .. +15 of row 16w + r, at 1024 + 16*l bytes 128j + 64 + 16g ..
+ * +15.  Byte-exact; the packed copy is read-only afterwards and owned by the
+ * caller.
+ *
+ * i8_head_gemv_packed / i8_head_gemv_packed_i8: as i8_head_gemv /
+ * i8_head_gemv_i8 with W replaced by its packed copy; 1 <= M <=
+ * TERN_MAX_M_GEMV and the activations of all M rows must fit one CU's LDS
+ * (M*(2K+16) bytes for bf16, M*(K+16) for int8, at most 160 KiB), else
+ * TERN_E_SHAPE; the same shape errors as i8_head_packed_bytes. */
+int64_t i8_head_packed_bytes(int64_t V, int64_t K);
+int i8_head_pack(const int8_t* W, int64_t V, int64_t K, int8_t* packed, void* stream);
+int i8_head_gemv_packed(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                        int64_t M, float* logits, void* stream);
+int i8_head_gemv_packed_i8(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                           const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
 
 /* Greedy decode on the output head: the int8 head GEMV fused with an argmax
  * over the vocabulary (token identity is decided greedily on float32 logits,

@@ -15,8 +15,10 @@ Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
 (FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv[_i8]``, and the
 block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
-``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed``, and the
-launch-configuration view ``tern_gemv_config``.
+``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed``, the
+packed int8 head ``i8_head_packed_bytes``, ``i8_head_pack``,
+``i8_head_gemv_packed[_i8]``, and the launch-configuration view
+``tern_gemv_config``.
 """
 from __future__ import annotations
 
@@ -31,12 +33,14 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
            "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
-           "tern_launch_probe", "i8_head_argmax_noalloc")
+           "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_packed_bytes", "i8_head_pack",
+           "i8_head_gemv_packed", "i8_head_gemv_packed_i8")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
                "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak",
-               "tern_launch_probe", "i8_head_argmax_noalloc")
+               "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_pack", "i8_head_gemv_packed",
+               "i8_head_gemv_packed_i8")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -98,6 +102,11 @@ def lib():
         L.tern_mfma_peak_sink_bytes.argtypes = [_i64]
         L.tern_mfma_peak.argtypes = [ctypes.c_int, _i64, _i64, _p, _p]
         L.tern_launch_probe.argtypes = [ctypes.c_int, _i64, _p, _i64, _p, _p]
+        L.i8_head_packed_bytes.restype = _i64
+        L.i8_head_packed_bytes.argtypes = [_i64, _i64]
+        L.i8_head_pack.argtypes = [_p, _i64, _i64, _p, _p]
+        L.i8_head_gemv_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.i8_head_gemv_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -220,6 +229,47 @@ def i8_head_gemv_i8(w, row_scale, q, s_x, y=None, acc=None, stream=None):
         y = torch.empty((m, v), dtype=torch.float32, device=q.device)
     _check("i8_head_gemv_i8", lib().i8_head_gemv_i8(_ptr(w), _ptr(row_scale), v, k, _ptr(q), _ptr(s_x), m, _ptr(y),
                                                     _ptr(acc), _stream(stream)))
+    return y
+
+
+def i8_head_packed_bytes(v: int, k: int) -> int:
+    return int(lib().i8_head_packed_bytes(v, k))
+
+
+def i8_head_pack(w, out=None, stream=None):
+    """W int8 [V,K] -> its packed copy (int8, i8_head_packed_bytes(V, K) bytes) for i8_head_gemv_packed[_i8]."""
+    import torch
+    _need(w, "W", (torch.int8,), 2)
+    v, k = w.shape
+    nbytes = i8_head_packed_bytes(v, k)
+    if nbytes < 0:
+        _check("i8_head_pack", 2)
+    if out is None:
+        out = torch.empty(nbytes, dtype=torch.int8, device=w.device)
+    _check("i8_head_pack", lib().i8_head_pack(_ptr(w), v, k, _ptr(out), _stream(stream)))
+    return out
+
+
+def i8_head_gemv_packed(wp, row_scale, v: int, k: int, x, y=None, stream=None):
+    """i8_head_gemv over the packed copy wp of W [v,k]; x bf16 [M,K] -> logits fp32 [M,V]."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=x.device)
+    _check("i8_head_gemv_packed", lib().i8_head_gemv_packed(_ptr(wp), _ptr(row_scale), v, k, _ptr(x), m, _ptr(y),
+                                                            _stream(stream)))
+    return y
+
+
+def i8_head_gemv_packed_i8(wp, row_scale, v: int, k: int, q, s_x, y=None, acc=None, stream=None):
+    import torch
+    _need(q, "q", (torch.int8,), 2)
+    m = q.shape[0]
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=q.device)
+    _check("i8_head_gemv_packed_i8", lib().i8_head_gemv_packed_i8(_ptr(wp), _ptr(row_scale), v, k, _ptr(q),
+                                                                  _ptr(s_x), m, _ptr(y), _ptr(acc), _stream(stream)))
     return y
 
 

@@ -174,6 +174,49 @@ int i8_head_gemv_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t 
     return finish(tern::launch_head_i8(W, row_scale, V, K, q, s_x, M, logits, acc_dbg, (hipStream_t)stream));
 }
 
+int64_t i8_head_packed_bytes(int64_t V, int64_t K)
+{
+    if (V < 1 || V > 0xFFFFFFF0ll || K < 128 || K % 128 != 0 || K > (1ll << 20)) return -1;
+    return tern::head_packed_bytes(V, K);
+}
+
+int i8_head_pack(const int8_t* W, int64_t V, int64_t K, int8_t* packed, void* stream)
+{
+    if (i8_head_packed_bytes(V, K) < 0) return TERN_E_SHAPE;
+    if (!W || !packed) return TERN_E_NULL;
+    if (!aligned16(W) || !aligned16(packed)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_head_pack(W, V, K, packed, (hipStream_t)stream));
+}
+
+int i8_head_gemv_packed(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                        int64_t M, float* logits, void* stream)
+{
+    if (i8_head_packed_bytes(V, K) < 0 || M < 1 || M > TERN_MAX_M_GEMV || !tern::head_packed_fits(K, M, false))
+        return TERN_E_SHAPE;
+    if (!packed || !row_scale || !x || !logits) return TERN_E_NULL;
+    if (!aligned16(packed) || !aligned16(x) || !aligned4(logits) || !aligned4(row_scale)) return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_head_packed_bf16(packed, row_scale, V, K, x, M, logits, (hipStream_t)stream));
+}
+
+int i8_head_gemv_packed_i8(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                           const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream)
+{
+    if (i8_head_packed_bytes(V, K) < 0 || M < 1 || M > TERN_MAX_M_GEMV || !tern::head_packed_fits(K, M, true))
+        return TERN_E_SHAPE;
+    if (!packed || !row_scale || !q || !s_x || !logits) return TERN_E_NULL;
+    if (!aligned16(packed) || !aligned16(q) || !aligned4(logits) || !aligned4(row_scale) || !aligned4(s_x) ||
+        (acc_dbg && !aligned4(acc_dbg)))
+        return TERN_E_ALIGN;
+    int rc = check_device();
+    if (rc) return rc;
+    return finish(tern::launch_head_packed_i8(packed, row_scale, V, K, q, s_x, M, logits, acc_dbg,
+                                              (hipStream_t)stream));
+}
+
 int64_t i8_head_argmax_workspace_bytes(int64_t V, int64_t M)
 {
     if (V < 1 || V > 0xFFFFFFF0ll || M < 1 || M > TERN_MAX_M_GEMV) return -1;

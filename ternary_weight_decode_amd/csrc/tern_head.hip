@@ -22,6 +22,7 @@
 namespace tern {
 
 constexpr int kHeadWaves = 4;
+constexpr int kHeadUnitBytes = kTileRows * kBlockK;   // one wave's 128-k unit: 16 rows x 128 bytes
 // byte offsets, within a lane's k range of a 128-k unit, of the four bf16 MFMA
 // steps' activations: k = 16g + {0, 8} and 64 + 16g + {0, 8} (2 bytes each)
 __device__ constexpr int kHalfOff[4] = {0, 16, 128, 144};
@@ -29,6 +30,10 @@ __device__ constexpr int kHalfOff[4] = {0, 16, 128, 144};
 #define TERN_HEAD_TPW 4
 #endif
 constexpr int kHeadTpw = TERN_HEAD_TPW;   // 128-k units in flight per wave (single-chunk path)
+#ifndef TERN_HEAD_PACKED_TPW
+#define TERN_HEAD_PACKED_TPW 8
+#endif
+constexpr int kHeadPackedTpw = TERN_HEAD_PACKED_TPW;   // the same, packed layout
 // 16-byte load of head weights.  Plain (cached) loads: with non-temporal ones
 // the head fetched about 10% more bytes from HBM than it reads and ran ~13%
 // slower at every ring depth measured (V = 151936, K = 4096).
@@ -299,12 +304,17 @@ __global__ __launch_bounds__(1024) void head_argmax_finish_kernel(const unsigned
 // to acc_dbg [M][V][K/256] on request; logits = total (bf16) or
 // s_x[m] * total (int8).  Every slot also loads its block's scale (4 bytes
 // per lane, shared by the 4 lanes of a row and the block's two units).
-template <bool kInt8, int TPW, bool kBlk = false>
+//
+// kPacked: W is the head_pack layout (below): the workgroup's 64 rows are one
+// block of memory in which 128-k unit j of all four waves is 8 KiB, read with
+// non-temporal loads, so the workgroup streams one sequential region.
+template <bool kInt8, int TPW, bool kBlk = false, bool kPacked = false>
 __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict__ W, const float* __restrict__ rs,
                                                         int64_t V, int64_t K, const void* __restrict__ act,
                                                         const float* __restrict__ s_x, int M, float* __restrict__ y,
                                                         int32_t* __restrict__ acc_dbg, HeadArgmax am)
 {
+    static_assert(!(kBlk && kPacked), "the packed layout holds per-row-scaled weights");
     static_assert(!kBlk || TPW % 2 == 0, "a block's two units share a ring parity");
     extern __shared__ __align__(16) uint8_t smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -323,11 +333,18 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
     const int nblk = (int)(K >> 8);                        // 256-weight blocks per row (kBlk)
     u32x4 lo[TPW], hi[TPW];
     float bs[TPW];
+    const int8_t* grp = W + (int64_t)blockIdx.x * (kHeadWaves * kTileRows) * K + wave * kHeadUnitBytes + 16 * lane;
     auto load = [&](int s, int j) {
         const bool valid = has && j < nunit;
-        const int8_t* p = valid ? row + (int64_t)j * kBlockK : W;
-        lo[s] = head_ld16(p);
-        hi[s] = head_ld16(valid ? p + 64 : W);
+        if constexpr (kPacked) {
+            const int8_t* p = valid ? grp + (int64_t)j * (kHeadWaves * kHeadUnitBytes) : W;
+            lo[s] = __builtin_nontemporal_load((const u32x4*)p);
+            hi[s] = __builtin_nontemporal_load((const u32x4*)(valid ? p + kHeadUnitBytes / 2 : W));
+        } else {
+            const int8_t* p = valid ? row + (int64_t)j * kBlockK : W;
+            lo[s] = head_ld16(p);
+            hi[s] = head_ld16(valid ? p + 64 : W);
+        }
         if constexpr (kBlk) bs[s] = rs[valid ? v * nblk + (j >> 1) : 0];
     };
 #pragma unroll
@@ -418,16 +435,69 @@ static int head_chunk(int64_t K, int64_t M, int ebytes)
     return (int)(K < cap ? K : cap);
 }
 
-template <bool kInt8, int TPW, bool kBlk = false>
+template <bool kInt8, int TPW, bool kBlk = false, bool kPacked = false>
 static hipError_t launch_head_fast(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                    const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream,
                                    HeadArgmax am = HeadArgmax{nullptr})
 {
     const size_t lds = (size_t)M * (K * (kInt8 ? 1 : 2) + 16);
     const int64_t grid = ((V + 15) / 16 + kHeadWaves - 1) / kHeadWaves;
-    head_fast_kernel<kInt8, TPW, kBlk><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(
+    head_fast_kernel<kInt8, TPW, kBlk, kPacked><<<dim3((unsigned)grid), dim3(64 * kHeadWaves), lds, stream>>>(
         W, rs, V, K, act, s_x, (int)M, y, acc, am);
     return hipGetLastError();
+}
+
+// ---- packed head layout ----------------------------------------------------
+// Rows in groups of 64 (a workgroup's four 16-row tiles; V padded to a
+// multiple of 64 with zero rows); inside a group, for 128-k unit j, for wave
+// w (rows 16w .. 16w + 15 of the group), 2 KiB: the low half holds, for lane
+// l = r + 16g, bytes 16g .. 16g + 15 of the unit's row 16w + r, the high half
+// bytes 64 + 16g .. 64 + 16g + 15.  A lane thus loads the same 32 bytes as
+// from the row-major matrix, and a workgroup reads 8 KiB contiguously per
+// unit (size: head_packed_bytes).
+
+__global__ __launch_bounds__(256) void head_pack_kernel(const int8_t* __restrict__ W, int64_t V, int64_t K,
+                                                        int8_t* __restrict__ out)
+{
+    const int64_t n16 = head_packed_bytes(V, K) / 16;
+    const int64_t per_group = 64 * K / 16;
+    for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < n16; c += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t grp = c / per_group;
+        int64_t rem = c - grp * per_group;
+        const int64_t j = rem / (kHeadWaves * kHeadUnitBytes / 16);
+        rem -= j * (kHeadWaves * kHeadUnitBytes / 16);
+        const int w = (int)(rem / (kHeadUnitBytes / 16));
+        rem -= (int64_t)w * (kHeadUnitBytes / 16);
+        const int h = (int)(rem / 64), l = (int)(rem % 64);
+        const int64_t row = grp * 64 + w * kTileRows + (l & 15);
+        const int64_t col = j * kBlockK + 64 * h + 16 * (l >> 4);
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (row < V) v = *(const u32x4*)(W + row * K + col);
+        *(u32x4*)(out + c * 16) = v;
+    }
+}
+
+hipError_t launch_head_pack(const int8_t* W, int64_t V, int64_t K, int8_t* out, hipStream_t stream)
+{
+    const int64_t n16 = head_packed_bytes(V, K) / 16;
+    const int64_t blocks = (n16 + 255) / 256;
+    head_pack_kernel<<<dim3((unsigned)(blocks < 65536 ? blocks : 65536)), dim3(256), 0, stream>>>(W, V, K, out);
+    return hipGetLastError();
+}
+
+// packed head: the single-pass kernel only (x of all M rows in LDS)
+bool head_packed_fits(int64_t K, int64_t M, bool int8_act) { return head_argmax_fits(K, M, int8_act); }
+
+hipError_t launch_head_packed_bf16(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                   int64_t M, float* y, hipStream_t stream)
+{
+    return launch_head_fast<false, kHeadPackedTpw, false, true>(Wp, rs, V, K, x, nullptr, M, y, nullptr, stream);
+}
+
+hipError_t launch_head_packed_i8(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                 const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    return launch_head_fast<true, kHeadPackedTpw, false, true>(Wp, rs, V, K, q, s_x, M, y, acc, stream);
 }
 
 template <bool kInt8>

@@ -39,6 +39,14 @@ hipError_t launch_head_argmax_bf16(const int8_t* W, const float* rs, int64_t V, 
 hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, int64_t K, const int8_t* q,
                                  const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                  hipStream_t stream);
+// the head over its packed layout (workgroup-contiguous row groups of 64)
+__host__ __device__ inline int64_t head_packed_bytes(int64_t V, int64_t K) { return (V + 63) / 64 * 64 * K; }
+hipError_t launch_head_pack(const int8_t* W, int64_t V, int64_t K, int8_t* out, hipStream_t stream);
+bool head_packed_fits(int64_t K, int64_t M, bool int8_act);
+hipError_t launch_head_packed_bf16(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const uint16_t* x,
+                                   int64_t M, float* y, hipStream_t stream);
+hipError_t launch_head_packed_i8(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                 const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
 // the bf16 head + argmax with its keys in a library-owned device array of
 // kHeadArgmaxScratchBytes (no workspace argument, nothing allocated)
 constexpr int64_t kHeadArgmaxScratchBytes = 2 << 20;

@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 def test_version_and_strings():
     L = tw.lib()
-    assert L.tern_abi_version() == 9
+    assert L.tern_abi_version() == 10
     for rc in range(6):
         assert len(L.tern_strerror(rc)) > 0
     assert L.tern_last_error() == b""
@@ -302,3 +302,37 @@ def test_head_argmax_noalloc_validation():
     assert L.i8_head_argmax_noalloc(p, p, 100, 128, p, 17, p, p, None, None) == E_SHAPE     # M > 16
     assert L.i8_head_argmax_noalloc(p, p, 100, 128, p, 1, None, p, None, None) == E_NULL
     assert L.i8_head_argmax_noalloc(p, p, 100, 128, MISALIGNED, 1, p, p, None, None) == E_ALIGN
+
+
+def test_packed_head_sizes_and_argument_errors():
+    L = tw.lib()
+    p, m = ALIGNED, MISALIGNED
+    assert tw.i8_head_packed_bytes(151936, 4096) == 151936 * 4096          # 151936 = 2374 * 64
+    assert tw.i8_head_packed_bytes(70, 256) == 2 * 64 * 256
+    assert tw.i8_head_packed_bytes(1, 128) == 64 * 128
+    for v, k in ((0, 128), (100, 96), (100, 0), (100, 64), (1 << 33, 128), (16, (1 << 20) + 128)):
+        assert tw.i8_head_packed_bytes(v, k) == -1, (v, k)
+    assert L.i8_head_pack(p, 100, 96, p, None) == E_SHAPE
+    assert L.i8_head_pack(p, 0, 128, p, None) == E_SHAPE
+    assert L.i8_head_pack(None, 100, 128, p, None) == E_NULL
+    assert L.i8_head_pack(p, 100, 128, None, None) == E_NULL
+    assert L.i8_head_pack(m, 100, 128, p, None) == E_ALIGN
+    assert L.i8_head_pack(p, 100, 128, m, None) == E_ALIGN
+    g, gi = L.i8_head_gemv_packed, L.i8_head_gemv_packed_i8
+    assert g(p, p, 100, 96, p, 1, p, None) == E_SHAPE                      # K % 128
+    assert g(p, p, 0, 128, p, 1, p, None) == E_SHAPE                       # V = 0
+    assert g(p, p, 100, 128, p, 0, p, None) == E_SHAPE                     # M = 0
+    assert g(p, p, 100, 128, p, 17, p, None) == E_SHAPE                    # M > 16
+    assert g(p, p, 100, 8192, p, 16, p, None) == E_SHAPE                   # bf16 x of 16 x 8192 exceeds LDS
+    assert gi(p, p, 100, 8192, p, p, 16, p, None, None) != E_SHAPE         # int8 x of 16 x 8192 fits ...
+    assert gi(p, p, 100, 8192, p, None, 16, p, None, None) == E_NULL       # ... (s_x missing here)
+    assert gi(p, p, 100, 16384, p, p, 16, p, None, None) == E_SHAPE        # 16 x 16384 int8 does not
+    assert g(None, p, 100, 128, p, 1, p, None) == E_NULL
+    assert g(p, None, 100, 128, p, 1, p, None) == E_NULL
+    assert g(p, p, 100, 128, None, 1, p, None) == E_NULL
+    assert g(p, p, 100, 128, p, 1, None, None) == E_NULL
+    assert g(m, p, 100, 128, p, 1, p, None) == E_ALIGN
+    assert g(p, p, 100, 128, m, 1, p, None) == E_ALIGN
+    assert g(p, p, 100, 128, p, 1, ctypes.c_void_p(0x10002), None) == E_ALIGN   # logits
+    assert gi(p, p, 100, 128, m, p, 1, p, None, None) == E_ALIGN
+    assert gi(p, p, 100, 128, p, p, 1, p, ctypes.c_void_p(0x10002), None) == E_ALIGN   # acc_dbg
