@@ -617,6 +617,209 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     }
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident activations (17 <= M <= 64, K % 512 == 0, K <= 4096): one
+// wave per k-tile of K.  A wave loads its k-tile of all MG*16 activation rows
+// once, straight into the int8 MFMA A operands (32-byte word 512*kw + 128*bq +
+// 32*g of row mg*16 + r for lane (r, g) and block bq, gathered from two
+// row-contiguous loads by a cross-lane swap and permuted in registers to the
+// decoded byte order), and reuses them over the R consecutive row tiles
+// of its workgroup, whose plane words it requests up front: no activation
+// staging and no barrier before the compute.  Per row tile and 128-k block two
+// MFMAs per row group give the exact int32 block sums, folded in fp32 with the
+// block scale in block order; the nkt partials of each output meet in LDS once
+// and are summed in k-tile order (deterministic).  Rows past M repeat row M-1
+// and row tiles past N the last real one; their outputs are dropped.
+template <int MG, int R, bool kDbg>
+__global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
+                                                          const int8_t* __restrict__ q,
+                                                          const float* __restrict__ s_x, int M,
+                                                          float* __restrict__ y, int32_t* __restrict__ acc_dbg)
+{
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int nkt = (int)(blockDim.x >> 6);                          // one wave per k-tile
+    const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    const int r = lane & 15, g = lane >> 4;
+    const int nb = (int)(K >> 7);
+    const int64_t nrt = (N + 15) >> 4;
+    const int64_t rt0 = (int64_t)blockIdx.x * R;
+    const int m0 = (int)blockIdx.y * (MG * 16);                     // this workgroup's activation rows
+    const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
+    const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
+
+    // the plane words of this wave's R units, then its activations, all requested up front
+    PlaneTile t[R];
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t rt = rt0 + i < nrt ? rt0 + i : nrt - 1;
+        const int64_t wb = tile_word_base(rt, kw, nb);
+        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        const int64_t rt = rt0 + i < nrt ? rt0 + i : nrt - 1;
+        t[i].sc = ld_nt8(scales + tile_scale_base(rt, kw, nb) + r * 4);
+    }
+    // Each load covers 64 contiguous bytes of every row (lane group g takes 16-byte piece
+    // c(g) = 2(g & 1) + (g >> 1) of the block's first, then second, 64 bytes); one swap of
+    // the upper 32 lanes of the first with the lower 32 lanes of the second then leaves
+    // lane group g with pieces 2g and 2g + 1, its 32-byte word.
+    const TERN_GLOBAL u32x4* qg = (const TERN_GLOBAL u32x4*)q;
+    u32x4 A[MG][4][2];
+    const int piece = 2 * (g & 1) + (g >> 1);
+#pragma unroll
+    for (int mg = 0; mg < MG; ++mg) {
+        const int m = m0 + mg * 16 + r < M ? m0 + mg * 16 + r : M - 1;
+        const int64_t base = (((int64_t)m * K + kTileK * kw) >> 4) + piece;   // in 16-byte units
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq) {
+            A[mg][bq][0] = qg[base + 8 * bq];
+            A[mg][bq][1] = qg[base + 8 * bq + 4];
+        }
+    }
+
+    float* red = (float*)smem;                                       // [R][nkt][MG][4][64]
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+        f32x4 acc[MG];
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg) acc[mg] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t n = (rt0 + i) * kTileRows + r;
+#pragma unroll
+        for (int bq = 0; bq < 4; ++bq) {
+            if (i == 0) {
+                // pieces to words, then natural bytes -> the decoded order, once per activation word
+#pragma unroll
+                for (int mg = 0; mg < MG; ++mg) {
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) {
+                        const auto sw = __builtin_amdgcn_permlane32_swap(A[mg][bq][0][d], A[mg][bq][1][d], false,
+                                                                         false);
+                        A[mg][bq][0][d] = sw[0];
+                        A[mg][bq][1][d] = sw[1];
+                    }
+                    const uint32_t Q[8] = {A[mg][bq][0][0], A[mg][bq][0][1], A[mg][bq][0][2], A[mg][bq][0][3],
+                                           A[mg][bq][1][0], A[mg][bq][1][1], A[mg][bq][1][2], A[mg][bq][1][3]};
+#pragma unroll
+                    for (int d = 0; d < 4; ++d) A[mg][bq][0][d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+#pragma unroll
+                    for (int d = 4; d < 8; ++d) A[mg][bq][1][d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+                }
+            }
+            u32x4 B[2];
+            decode_i8(t[i].nz[bq], t[i].sg[bq], B);
+            const float sc = tile_scale(t[i], bq) * (1.0f / 64.0f);    // decoded weights are 64*t
+            i32x4 dd[MG];
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][bq][0], B[0], i32x4{0, 0, 0, 0});
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][bq][1], B[1], dd[mg]);
+#pragma unroll
+            for (int mg = 0; mg < MG; ++mg) {
+                const i32x4 d = dd[mg];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[mg][e] = __builtin_fmaf(sc, (float)d[e], acc[mg][e]);
+                if constexpr (kDbg) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int m = m0 + mg * 16 + 4 * g + e;
+                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kw * 4 + bq] = d[e] >> 6;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int mg = 0; mg < MG; ++mg)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) red[((((i * nkt + kw) * MG + mg) * 4 + e) << 6) + lane] = acc[mg][e];
+    }
+    __syncthreads();
+    const int nout = R * MG * 4 * 64;
+    for (int o = threadIdx.x; o < nout; o += (int)blockDim.x) {
+        const int l = o & 63, e = (o >> 6) & 3, mg = (o >> 8) % MG, i = (o >> 8) / MG;
+        const int m = m0 + mg * 16 + 4 * (l >> 4) + e;
+        const int64_t n = (rt0 + i) * kTileRows + (l & 15);
+        if (m < M && n < N) {
+            float sum = 0.f;
+            for (int kt = 0; kt < nkt; ++kt) sum += red[((((i * nkt + kt) * MG + mg) * 4 + e) << 6) + l];
+            y[(int64_t)m * N + n] = s_x[m] * sum;
+        }
+    }
+}
+
+// Launch configuration of prefill_reg_kernel, or false when it does not
+// apply: nkt = K/512 waves (at most 8: two waves per SIMD keep the MG*32
+// activation registers), the smallest R (1-4, 6 or 8 row tiles per workgroup)
+// for which the grid fits the CUs at eight waves per CU.  Each CU reads the
+// activations of its rows for all of K from L2, which sets the time (8B gate,
+// M = 64: 14.3 us, 8.1 us with every activation row read from one row); at
+// four row groups the workgroups take two rows of the grid, one per half of
+// the activation rows, and read half as many activation bytes while every
+// weight tile is read twice (the second time mostly from L2: the two halves'
+// workgroups sit on the same XCD): 14.2 -> 12.8 us.  At three groups the
+// split (16 rows wasted) measured 12.6 against 12.1 us, at M = 32 a split
+// into single groups 9.4 against 9.5 us (decode work doubled), so those stay
+// whole.
+struct PfReg {
+    int MG, R, nw, S;
+    int64_t grid;
+    size_t lds;
+};
+
+static bool pick_pf_reg(int64_t N, int64_t K, int64_t M, PfReg& c)
+{
+    if (K % kTileK != 0 || K > 8 * kTileK || M < 17 || M > 64 || N < 1) return false;
+    // two or three 16-row groups in one workgroup; four as two halves in two grid rows
+    const int64_t groups = (M + 15) / 16;
+    c.MG = (int)(groups <= 3 ? groups : 2);
+    c.S = (int)(groups <= 3 ? 1 : 2);
+    c.nw = (int)(K / kTileK);
+    const int64_t nrt = (N + 15) / 16, slots = device_cus() * (8 / c.nw);
+    int64_t R = (nrt * c.S + slots - 1) / slots;
+    R = R < 1 ? 1 : R;
+    c.R = (int)(R <= 4 ? R : (R <= 6 ? 6 : 8));
+    c.grid = (nrt + c.R - 1) / c.R;
+    c.lds = (size_t)c.R * c.nw * c.MG * 4 * 64 * 4;
+    return c.lds <= (size_t)kCuLds;
+}
+
+template <int MG, int R>
+static hipError_t launch_pf_reg_r(const PfReg& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
+                                  const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    if (acc)
+        prefill_reg_kernel<MG, R, true><<<dim3((unsigned)c.grid, (unsigned)c.S), dim3(64 * c.nw), c.lds, stream>>>(
+            packed, N, K, q, s_x, (int)M, y, acc);
+    else
+        prefill_reg_kernel<MG, R, false><<<dim3((unsigned)c.grid, (unsigned)c.S), dim3(64 * c.nw), c.lds, stream>>>(
+            packed, N, K, q, s_x, (int)M, y, acc);
+    return hipGetLastError();
+}
+
+template <int MG>
+static hipError_t launch_pf_reg_mg(const PfReg& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
+                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    switch (c.R) {
+    case 1: return launch_pf_reg_r<MG, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 2: return launch_pf_reg_r<MG, 2>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 3: return launch_pf_reg_r<MG, 3>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 4: return launch_pf_reg_r<MG, 4>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 6: return launch_pf_reg_r<MG, 6>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    default: return launch_pf_reg_r<MG, 8>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    }
+}
+
+static hipError_t launch_pf_reg(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
+                                int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    PfReg c;
+    if (!pick_pf_reg(N, K, M, c)) return hipErrorNotSupported;
+    if (c.MG == 2) return launch_pf_reg_mg<2>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    return launch_pf_reg_mg<3>(c, packed, N, K, q, s_x, M, y, acc, stream);
+}
+
 struct PfSmall {
     int MG, R, nw, XC;
     int64_t grid;
@@ -706,8 +909,13 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
         if (M >= 1024) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
         return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
     }
-    {   // 17 <= M <= 64: K split across the waves of a workgroup.  Measured on the 8B
-        // shapes against the paths below: gate M = 64 16.2 us vs 24.6 us, down M = 64
+    {   // 17 <= M <= 64, K <= 4096: activations held in registers, one wave per k-tile
+        const hipError_t e = launch_pf_reg(packed, N, K, q, s_x, M, y, acc, stream);
+        if (e != hipErrorNotSupported) return e;
+    }
+    {   // 17 <= M <= 64 above K = 4096: K split across the waves of a workgroup.  Measured
+        // on the 8B shapes against the paths below (before the register-resident kernel took
+        // K <= 4096): gate M = 64 16.2 us vs 24.6 us, down M = 64
         // 26.4 us vs 30.5 us, gate M = 32 10.6 us vs 12.5 us, gate M = 48 13.0 us vs 18.3 us.
         const hipError_t e = launch_pf_small(packed, N, K, q, s_x, M, y, acc, stream);
         if (e != hipErrorNotSupported) return e;

@@ -363,9 +363,10 @@ def test_prefill_exact_on_power_of_two_scales(tw):
 @pytest.mark.parametrize("n,k,m", [(300, 8192, 64), (100, 4096, 37), (37, 12288, 17), (1000, 4096, 48),
                                    (5000, 12288, 33), (77, 1536, 64)])
 def test_prefill_small_m_split_k(tw, n, k, m):
-    """17 <= M <= 64 (K a multiple of 512): K split across the waves of a
-    workgroup, activations staged a phase at a time, each decoded weight tile
-    reused over the 16-row groups (ragged last group and last row tile):
+    """17 <= M <= 64 (K a multiple of 512): above K = 4096, K split across the
+    waves of a workgroup, activations staged a phase at a time, each decoded
+    weight tile reused over the 16-row groups (ragged last group and last row
+    tile); up to K = 4096 the register-resident kernel:
     block sums bit for bit, y against the oracle, and the production
     instance (no block sums) the same bytes."""
     import torch
@@ -379,6 +380,45 @@ def test_prefill_small_m_split_k(tw, n, k, m):
     assert oracle.rel_l2(y, y64) <= TOL
     y2 = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
     assert np.array_equal(y, y2)
+
+
+@pytest.mark.parametrize("n,k,m", [(16, 512, 17), (1000, 1024, 40), (9000, 2048, 64), (12290, 4096, 33),
+                                   (6000, 4096, 64), (333, 2560, 50)])
+def test_prefill_register_activations(tw, n, k, m):
+    """17 <= M <= 64 with K <= 4096 (K a multiple of 512): one wave per k-tile
+    holding its activations in registers over 1 to 4 row tiles per workgroup
+    (ragged last row tile and last 16-row group, two to four row groups):
+    block sums bit for bit, y against the oracle, and the production instance
+    (no block sums) the same bytes."""
+    import torch
+    t, s, x = gen(n, k, m, seed=n + 11 * m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t, s), n, k, q0, s0)
+    assert np.array_equal(host(acc), acc0)
+    assert oracle.rel_l2(y, y64) <= TOL
+    assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
+
+
+def test_prefill_register_activations_four_row_tiles_sampled(tw):
+    """The fused 8B gate|up shape (24576 x 4096) at M = 64: four row tiles per
+    workgroup, more workgroups than CUs; sampled rows' block sums bit for bit
+    and y against the oracle, the production instance the same bytes."""
+    import torch
+    n, k, m = 24576, 4096, 64
+    t, s, x = gen(n, k, m, seed=2457)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    rng = np.random.default_rng(4)
+    rows = np.unique(np.concatenate([rng.choice(n, 80, replace=False), np.arange(n - 16, n), [0]]))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+    assert np.array_equal(host(acc)[:, rows], acc0)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
 
 
 @pytest.mark.parametrize("n,k,m", [(300, 8192, 100), (100, 4096, 16), (37, 12288, 9)])
