@@ -594,6 +594,10 @@ def mode_head(args, tw, synth, torch):
         "head_argmax_bf16": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws), row_bytes),
         "head_argmax_bf16_with_logits": (lambda c: tw.i8_head_argmax(c, RS, x, workspace=ws, logits=y), row_bytes),
         "head_argmax_int8": (lambda c: tw.i8_head_argmax_i8(c, RS, q, sx, workspace=ws), row_bytes),
+        "head_argmax_bf16_packed": (lambda c: tw.i8_head_argmax_packed(pk[id(c)], RS, v, k, x, workspace=ws),
+                                    row_bytes),
+        "head_argmax_int8_packed": (lambda c: tw.i8_head_argmax_packed_i8(pk[id(c)], RS, v, k, q, sx, workspace=ws),
+                                    row_bytes),
         "fv5b_head_bf16": (lambda c: tw.fv5b_head_gemv(c, S, x, y=y), blk_bytes),
         "fv5b_head_int8": (lambda c: tw.fv5b_head_gemv_i8(c, S, q, sx, y=y), blk_bytes),
         "fv5b_head_argmax_bf16": (lambda c: tw.fv5b_head_argmax(c, S, x, workspace=ws), blk_bytes),

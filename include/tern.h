@@ -212,6 +212,19 @@ int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_
                       const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
                       void* stream);
 
+/* i8_head_argmax / i8_head_argmax_i8 over the packed copy of W written by
+ * i8_head_pack (same arguments with W replaced by it, same limits, errors
+ * and workspace): idx, val and logits bit for bit those of the row-major
+ * calls; the copy's padding rows (V up to a multiple of 64) are never
+ * candidates.  The head is the largest tensor of the step ([P2] section
+ * "뉴트리노 엔진: 토큰 하나의 시간은 어디로 가는가"); the packed copy is
+ * read at a higher rate. */
+int i8_head_argmax_packed(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                          int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+int i8_head_argmax_packed_i8(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                             const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
+                             void* stream);
+
 /* i8_head_argmax without a workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc).  Same inputs, outputs, limits and result

@@ -17,7 +17,7 @@ fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
 block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
 ``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed``, the
 packed int8 head ``i8_head_packed_bytes``, ``i8_head_pack``,
-``i8_head_gemv_packed[_i8]``, and the launch-configuration view
+``i8_head_gemv_packed[_i8]``, ``i8_head_argmax_packed[_i8]``, and the launch-configuration view
 ``tern_gemv_config``.
 """
 from __future__ import annotations
@@ -34,13 +34,13 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
            "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
            "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_packed_bytes", "i8_head_pack",
-           "i8_head_gemv_packed", "i8_head_gemv_packed_i8")
+           "i8_head_gemv_packed", "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
                "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak",
                "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_pack", "i8_head_gemv_packed",
-               "i8_head_gemv_packed_i8")
+               "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -107,6 +107,8 @@ def lib():
         L.i8_head_pack.argtypes = [_p, _i64, _i64, _p, _p]
         L.i8_head_gemv_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
         L.i8_head_gemv_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        L.i8_head_argmax_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+        L.i8_head_argmax_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -271,6 +273,36 @@ def i8_head_gemv_packed_i8(wp, row_scale, v: int, k: int, q, s_x, y=None, acc=No
     _check("i8_head_gemv_packed_i8", lib().i8_head_gemv_packed_i8(_ptr(wp), _ptr(row_scale), v, k, _ptr(q),
                                                                   _ptr(s_x), m, _ptr(y), _ptr(acc), _stream(stream)))
     return y
+
+
+def i8_head_argmax_packed(wp, row_scale, v: int, k: int, x, workspace=None, logits=None, stream=None):
+    """i8_head_argmax over the packed copy wp of W [v,k]: (idx int32 [M], val fp32 [M])."""
+    import torch
+    _need(x, "x", (torch.bfloat16, torch.int16, torch.uint16), 2)
+    m = x.shape[0]
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, x.device)
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    val = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("i8_head_argmax_packed", lib().i8_head_argmax_packed(_ptr(wp), _ptr(row_scale), v, k, _ptr(x), m,
+                                                                _ptr(idx), _ptr(val), _ptr(logits),
+                                                                _ptr(workspace), _stream(stream)))
+    return idx, val
+
+
+def i8_head_argmax_packed_i8(wp, row_scale, v: int, k: int, q, s_x, workspace=None, logits=None, stream=None):
+    import torch
+    _need(q, "q", (torch.int8,), 2)
+    m = q.shape[0]
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, q.device)
+    idx = torch.empty(m, dtype=torch.int32, device=q.device)
+    val = torch.empty(m, dtype=torch.float32, device=q.device)
+    _check("i8_head_argmax_packed_i8", lib().i8_head_argmax_packed_i8(_ptr(wp), _ptr(row_scale), v, k, _ptr(q),
+                                                                      _ptr(s_x), m, _ptr(idx), _ptr(val),
+                                                                      _ptr(logits), _ptr(workspace),
+                                                                      _stream(stream)))
+    return idx, val
 
 
 def i8_head_argmax_workspace_bytes(v: int, m: int) -> int:

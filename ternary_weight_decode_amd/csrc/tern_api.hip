@@ -259,6 +259,27 @@ int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, i
                                                         (hipStream_t)stream));
 }
 
+int i8_head_argmax_packed(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const uint16_t* x,
+                          int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream)
+{
+    if (i8_head_packed_bytes(V, K) < 0) return TERN_E_SHAPE;
+    const int rc = head_argmax_check(packed, row_scale, V, K, x, nullptr, false, M, idx, val, logits, workspace);
+    if (rc) return rc;
+    return finish(tern::launch_head_argmax_packed_bf16(packed, row_scale, V, K, x, M, logits, idx, val, workspace,
+                                                       (hipStream_t)stream));
+}
+
+int i8_head_argmax_packed_i8(const int8_t* packed, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
+                             const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
+                             void* stream)
+{
+    if (i8_head_packed_bytes(V, K) < 0) return TERN_E_SHAPE;
+    const int rc = head_argmax_check(packed, row_scale, V, K, q, s_x, true, M, idx, val, logits, workspace);
+    if (rc) return rc;
+    return finish(tern::launch_head_argmax_packed_i8(packed, row_scale, V, K, q, s_x, M, logits, idx, val, workspace,
+                                                     (hipStream_t)stream));
+}
+
 int i8_head_argmax_i8(const int8_t* W, const float* row_scale, int64_t V, int64_t K, const int8_t* q,
                       const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
                       void* stream)

@@ -536,14 +536,16 @@ bool head_argmax_fits(int64_t K, int64_t M, bool int8_act)
     return (size_t)M * (K * (int8_act ? 1 : 2) + 16) <= (size_t)160 * 1024;
 }
 
-template <bool kInt8, bool kBlk = false>
+template <bool kInt8, bool kBlk = false, bool kPacked = false>
 static hipError_t launch_head_argmax(const int8_t* W, const float* rs, int64_t V, int64_t K, const void* act,
                                      const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                      hipStream_t stream, EmbedRows emb = EmbedRows{nullptr, nullptr, 0, 0, nullptr,
                                                                                   nullptr})
 {
     const HeadArgmax am{(unsigned long long*)ws};
-    hipError_t e = launch_head_fast<kInt8, kHeadTpw, kBlk>(W, rs, V, K, act, s_x, M, y, nullptr, stream, am);
+    hipError_t e = launch_head_fast<kInt8, kPacked ? kHeadPackedTpw : kHeadTpw, kBlk, kPacked>(W, rs, V, K, act, s_x,
+                                                                                              M, y, nullptr, stream,
+                                                                                              am);
     if (e != hipSuccess) return e;
     head_argmax_finish_kernel<<<dim3((unsigned)M), dim3(1024), 0, stream>>>((const unsigned long long*)ws,
                                                                            (V + 15) / 16, (int)M, idx, val, emb);
@@ -561,6 +563,21 @@ hipError_t launch_head_argmax_i8(const int8_t* W, const float* rs, int64_t V, in
                                  hipStream_t stream)
 {
     return launch_head_argmax<true>(W, rs, V, K, q, s_x, M, y, idx, val, ws, stream);
+}
+
+// the same over the packed copy (padding rows past V carry no key: their logits are never candidates)
+hipError_t launch_head_argmax_packed_bf16(const int8_t* Wp, const float* rs, int64_t V, int64_t K,
+                                          const uint16_t* x, int64_t M, float* y, int32_t* idx, float* val,
+                                          void* ws, hipStream_t stream)
+{
+    return launch_head_argmax<false, false, true>(Wp, rs, V, K, x, nullptr, M, y, idx, val, ws, stream);
+}
+
+hipError_t launch_head_argmax_packed_i8(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                        const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                        hipStream_t stream)
+{
+    return launch_head_argmax<true, false, true>(Wp, rs, V, K, q, s_x, M, y, idx, val, ws, stream);
 }
 
 // ---- the argmax keys in a library-owned array (for callers that cannot

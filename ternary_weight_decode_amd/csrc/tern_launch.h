@@ -47,6 +47,12 @@ hipError_t launch_head_packed_bf16(const int8_t* Wp, const float* rs, int64_t V,
                                    int64_t M, float* y, hipStream_t stream);
 hipError_t launch_head_packed_i8(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const int8_t* q,
                                  const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_head_argmax_packed_bf16(const int8_t* Wp, const float* rs, int64_t V, int64_t K,
+                                          const uint16_t* x, int64_t M, float* y, int32_t* idx, float* val,
+                                          void* ws, hipStream_t stream);
+hipError_t launch_head_argmax_packed_i8(const int8_t* Wp, const float* rs, int64_t V, int64_t K, const int8_t* q,
+                                        const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
+                                        hipStream_t stream);
 // the bf16 head + argmax with its keys in a library-owned device array of
 // kHeadArgmaxScratchBytes (no workspace argument, nothing allocated)
 constexpr int64_t kHeadArgmaxScratchBytes = 2 << 20;

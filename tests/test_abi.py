@@ -336,3 +336,21 @@ def test_packed_head_sizes_and_argument_errors():
     assert g(p, p, 100, 128, p, 1, ctypes.c_void_p(0x10002), None) == E_ALIGN   # logits
     assert gi(p, p, 100, 128, m, p, 1, p, None, None) == E_ALIGN
     assert gi(p, p, 100, 128, p, p, 1, p, ctypes.c_void_p(0x10002), None) == E_ALIGN   # acc_dbg
+
+
+def test_packed_head_argmax_argument_errors():
+    L = tw.lib()
+    p, m = ALIGNED, MISALIGNED
+    f, fi = L.i8_head_argmax_packed, L.i8_head_argmax_packed_i8
+    assert f(p, p, 100, 96, p, 1, p, p, None, p, None) == E_SHAPE          # K % 128
+    assert f(p, p, 0, 128, p, 1, p, p, None, p, None) == E_SHAPE           # V = 0
+    assert f(p, p, 100, 128, p, 0, p, p, None, p, None) == E_SHAPE         # M = 0
+    assert f(p, p, 100, 128, p, 17, p, p, None, p, None) == E_SHAPE        # M > 16
+    assert f(p, p, 100, 8192, p, 16, p, p, None, p, None) == E_SHAPE       # bf16 x exceeds LDS
+    assert fi(p, p, 100, 8192, p, None, 16, p, p, None, p, None) == E_NULL  # int8 fits; s_x missing
+    assert f(p, p, 100, 128, p, 1, p, p, None, None, None) == E_NULL       # workspace
+    assert f(None, p, 100, 128, p, 1, p, p, None, p, None) == E_NULL
+    assert f(p, p, 100, 128, p, 1, None, p, None, p, None) == E_NULL       # idx
+    assert f(m, p, 100, 128, p, 1, p, p, None, p, None) == E_ALIGN
+    assert f(p, p, 100, 128, p, 1, p, p, ctypes.c_void_p(0x10002), p, None) == E_ALIGN   # logits
+    assert fi(p, p, 100, 128, p, p, 1, p, p, None, ctypes.c_void_p(0x10004), None) == E_ALIGN   # workspace % 8

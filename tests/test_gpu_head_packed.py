@@ -116,3 +116,54 @@ def test_pack_leaves_bytes_past_its_size(tw):
     o = host(out)
     assert np.array_equal(o[:n], head_pack.pack(w))
     assert (o[n:] == 77).all()
+
+
+@pytest.mark.parametrize("v,k,m", [(70, 256, 1), (1000, 4096, 4), (2374, 1024, 16), (151936, 4096, 1)])
+def test_packed_argmax_matches_row_major(tw, v, k, m):
+    """The fused head + greedy argmax over the packed copy: index, value and
+    logits bit for bit those of the row-major call (bf16 and int8
+    activations), and the int8 result the oracle's exact greedy choice."""
+    import torch
+    rng = np.random.default_rng(v + 5 * k + m)
+    w, rs = synth.gen_head(rng, rng, v, k)
+    x = synth.gen_x_bf16(rng, m, k)
+    q, sx = oracle.quantize_i8(x)
+    wd, rsd, xd, qd, sxd = dev(w), dev(rs), dev(x), dev(q), dev(sx)
+    wp = tw.i8_head_pack(wd)
+    ws = tw.i8_head_argmax_workspace(v, m)
+    for fn_rm, fn_p, args in ((tw.i8_head_argmax, tw.i8_head_argmax_packed, (xd,)),
+                              (tw.i8_head_argmax_i8, tw.i8_head_argmax_packed_i8, (qd, sxd))):
+        y_rm = torch.empty((m, v), dtype=torch.float32, device="cuda")
+        y_p = torch.empty((m, v), dtype=torch.float32, device="cuda")
+        i_rm, v_rm = fn_rm(wd, rsd, *args, workspace=ws, logits=y_rm)
+        i_rm, v_rm, y_rm = host(i_rm), host(v_rm), host(y_rm)
+        i_p, v_p = fn_p(wp, rsd, v, k, *args, workspace=ws, logits=y_p)
+        assert np.array_equal(host(i_p), i_rm)
+        assert np.array_equal(host(v_p).view(np.uint32), v_rm.view(np.uint32))
+        assert np.array_equal(host(y_p), y_rm)
+    if v * k <= 4096 * 1000:
+        acc0, _, _ = oracle.head_i8(w, rs, q, sx)
+        idx0, val0 = oracle.greedy_argmax(oracle.head_i8_logits_f32(acc0, rs, sx))
+        assert np.array_equal(host(i_p), idx0) and np.array_equal(host(v_p), val0)
+
+
+def test_packed_argmax_padding_rows_never_win(tw):
+    """V = 70 (58 zero padding rows in the copy) with every real logit
+    negative: the winner is a real row, the oracle's exact greedy choice."""
+    v, k, m = 70, 256, 2
+    rng = np.random.default_rng(70)
+    w = -rng.integers(1, 128, size=(v, k)).astype(np.int8)          # every weight in [-127, -1]
+    rs = rng.uniform(0.002, 0.02, size=v).astype(np.float32)
+    q = rng.integers(1, 128, size=(m, k)).astype(np.int8)           # positive activations
+    sx = np.array([0.01, 0.5], np.float32)
+    x = synth.f32_to_bf16_bits(np.ones((m, k), np.float32))
+    wp = tw.i8_head_pack(dev(w))
+    idx, val = tw.i8_head_argmax_packed_i8(wp, dev(rs), v, k, dev(q), dev(sx))
+    acc0, _, _ = oracle.head_i8(w, rs, q, sx)
+    idx0, val0 = oracle.greedy_argmax(oracle.head_i8_logits_f32(acc0, rs, sx))
+    assert (val0 < 0).all()
+    assert np.array_equal(host(idx), idx0) and np.array_equal(host(val), val0)
+    idx_b, val_b = tw.i8_head_argmax_packed(wp, dev(rs), v, k, dev(x))
+    idx_r, val_r = tw.i8_head_argmax(dev(w), dev(rs), dev(x))
+    assert (host(idx_b) < v).all() and (host(val_b) < 0).all()
+    assert np.array_equal(host(idx_b), host(idx_r)) and np.array_equal(host(val_b), host(val_r))
