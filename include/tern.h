@@ -242,11 +242,13 @@ int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, i
 /* Prefill-size ternary GEMM with int8 activations (batched prefill, [P2]
  * section "실행해보기: pip부터 llama.cpp 포크까지"; batched verify is
  * compute-bound, section "노트북에서는 이야기가 다르다"),
- * same arithmetic as tern_gemv_i8 for any M >= 1, built for M >= 64: planes
- * are decoded to int8 and fed to the int8 matrix cores.  Below M = 128, where
- * the contraction's time is set by its per-block latency, the call may run
- * the int8 GEMV on 16-row slices of q instead (chosen on the host from the
- * shape); the result is the same contraction.
+ * same arithmetic as tern_gemv_i8 for any M >= 1, with kernels of its own
+ * from M = 17: planes are decoded to int8 and fed to the int8 matrix cores.
+ * Outside 17 <= M <= 64 and below M = 128, where the contraction's time is
+ * set by its per-block latency, the call may run the int8 GEMV on 16-row
+ * slices of q instead (chosen on the host from the shape); the result is the
+ * same contraction (fp32 y may differ in the last bits with the kernel: the
+ * block sums are added in a kernel-specific order).
  *   q int8 [M][K]; s_x fp32 [M]; y fp32 [M][N];
  *   acc_dbg NULL or int32 [M][N][K/128] (debug; small shapes). */
 int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
