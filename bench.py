@@ -602,6 +602,9 @@ def mode_head(args, tw, synth, torch):
         "fv5b_head_int8": (lambda c: tw.fv5b_head_gemv_i8(c, S, q, sx, y=y), blk_bytes),
         "fv5b_head_argmax_bf16": (lambda c: tw.fv5b_head_argmax(c, S, x, workspace=ws), blk_bytes),
         "fv5b_head_argmax_int8": (lambda c: tw.fv5b_head_argmax_i8(c, S, q, sx, workspace=ws), blk_bytes),
+        "fv5b_head_bf16_packed": (lambda c: tw.fv5b_head_gemv_packed(pk[id(c)], S, v, k, x, y=y), blk_bytes),
+        "fv5b_head_argmax_bf16_packed": (lambda c: tw.fv5b_head_argmax_packed(pk[id(c)], S, v, k, x, workspace=ws),
+                                         blk_bytes),
     }
     out = []
     for name, (fn, nbytes) in runs.items():

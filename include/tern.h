@@ -390,6 +390,23 @@ int fv5b_head_argmax(const int8_t* W, const float* S, int64_t V, int64_t K, cons
 int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q, const float* s_x,
                         int64_t M, int32_t* idx, float* val, float* logits, void* workspace, void* stream);
 
+/* The block-scaled head calls above over the packed copy of W's int8 rows
+ * (i8_head_pack; the scales S stay [V][K/256] row-major): same arguments
+ * with W replaced by the copy, same limits and errors, results bit for bit
+ * those of the row-major calls; the copy's padding rows are never argmax
+ * candidates.  The head is the step's largest tensor ([P2] section
+ * "뉴트리노 엔진: 토큰 하나의 시간은 어디로 가는가"); the copy is read at a
+ * higher rate. */
+int fv5b_head_gemv_packed(const int8_t* packed, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                          float* logits, void* stream);
+int fv5b_head_gemv_packed_i8(const int8_t* packed, const float* S, int64_t V, int64_t K, const int8_t* q,
+                             const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream);
+int fv5b_head_argmax_packed(const int8_t* packed, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                            int32_t* idx, float* val, float* logits, void* workspace, void* stream);
+int fv5b_head_argmax_packed_i8(const int8_t* packed, const float* S, int64_t V, int64_t K, const int8_t* q,
+                               const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
+                               void* stream);
+
 /* The end of one decode token and the start of the next in one call:
  * fv5b_head_argmax (bf16 x), then the embedding row of each chosen index
  * idx[m] from the block-scaled table E int8 [Ve][Ke] with scales ES f32

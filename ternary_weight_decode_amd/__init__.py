@@ -15,7 +15,9 @@ Names follow the C ABI: ``tern_pack``, ``tern_stats``, ``tern_quantize_i8``,
 fused head + greedy argmax ``i8_head_argmax[_i8]``, and the five-level
 (FV5-style) weights ``tern5_packed_bytes``, ``tern5_pack``, ``tern5_gemv[_i8]``, and the
 block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
-``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed``, the
+``fv5b_head_argmax[_i8]``, ``fv5b_head_argmax_embed``, ``fv5b_embed`` (and
+``fv5b_head_gemv_packed[_i8]``, ``fv5b_head_argmax_packed[_i8]`` over the
+packed copy), the
 packed int8 head ``i8_head_packed_bytes``, ``i8_head_pack``,
 ``i8_head_gemv_packed[_i8]``, ``i8_head_argmax_packed[_i8]``, and the launch-configuration view
 ``tern_gemv_config``.
@@ -34,13 +36,17 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
            "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
            "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_packed_bytes", "i8_head_pack",
-           "i8_head_gemv_packed", "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8")
+           "i8_head_gemv_packed", "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8",
+           "fv5b_head_gemv_packed", "fv5b_head_gemv_packed_i8", "fv5b_head_argmax_packed",
+           "fv5b_head_argmax_packed_i8")
 _INT_STATUS = ("tern_pack", "tern_stats", "tern_quantize_i8", "tern_gemv", "tern_gemv_i8", "i8_head_gemv",
                "i8_head_gemv_i8", "tern_gemm_prefill", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax",
                "i8_head_argmax_i8", "tern5_pack", "tern5_gemv", "tern5_gemv_i8", "fv5b_head_gemv", "fv5b_head_gemv_i8",
                "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed", "tern_mfma_peak",
                "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_pack", "i8_head_gemv_packed",
-               "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8")
+               "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8",
+               "fv5b_head_gemv_packed", "fv5b_head_gemv_packed_i8", "fv5b_head_argmax_packed",
+               "fv5b_head_argmax_packed_i8")
 
 _lib = None
 _i64 = ctypes.c_int64
@@ -109,6 +115,10 @@ def lib():
         L.i8_head_gemv_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
         L.i8_head_argmax_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
         L.i8_head_argmax_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
+        L.fv5b_head_gemv_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p]
+        L.fv5b_head_gemv_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p]
+        L.fv5b_head_argmax_packed.argtypes = [_p, _p, _i64, _i64, _p, _i64, _p, _p, _p, _p, _p]
+        L.fv5b_head_argmax_packed_i8.argtypes = [_p, _p, _i64, _i64, _p, _p, _i64, _p, _p, _p, _p, _p]
         for name in _INT_STATUS:
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -532,6 +542,63 @@ def fv5b_head_argmax_i8(w, s, q, s_x, workspace=None, logits=None, stream=None):
     _check("fv5b_head_argmax_i8", lib().fv5b_head_argmax_i8(_ptr(w), _ptr(s), v, k, _ptr(q), _ptr(s_x), m,
                                                             _ptr(idx), _ptr(val), _ptr(logits), _ptr(workspace),
                                                             _stream(stream)))
+    return idx, val
+
+
+def _fv5b_packed_args(s, v, k, act, act_dtypes):
+    import torch
+    _need(s, "S", (torch.float32,), 2)
+    _need(act, "activations", act_dtypes, 2)
+    if tuple(s.shape) != (v, k // 256):
+        raise RuntimeError("S must be [V, K/256]")
+    return act.shape[0]
+
+
+def fv5b_head_gemv_packed(wp, s, v: int, k: int, x, y=None, stream=None):
+    """fv5b_head_gemv over the packed copy wp (i8_head_pack) of W [v,k]."""
+    import torch
+    m = _fv5b_packed_args(s, v, k, x, (torch.bfloat16, torch.int16, torch.uint16))
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=x.device)
+    _check("fv5b_head_gemv_packed", lib().fv5b_head_gemv_packed(_ptr(wp), _ptr(s), v, k, _ptr(x), m, _ptr(y),
+                                                                _stream(stream)))
+    return y
+
+
+def fv5b_head_gemv_packed_i8(wp, s, v: int, k: int, q, s_x, y=None, acc=None, stream=None):
+    import torch
+    m = _fv5b_packed_args(s, v, k, q, (torch.int8,))
+    if y is None:
+        y = torch.empty((m, v), dtype=torch.float32, device=q.device)
+    _check("fv5b_head_gemv_packed_i8", lib().fv5b_head_gemv_packed_i8(_ptr(wp), _ptr(s), v, k, _ptr(q), _ptr(s_x),
+                                                                      m, _ptr(y), _ptr(acc), _stream(stream)))
+    return y
+
+
+def fv5b_head_argmax_packed(wp, s, v: int, k: int, x, workspace=None, logits=None, stream=None):
+    import torch
+    m = _fv5b_packed_args(s, v, k, x, (torch.bfloat16, torch.int16, torch.uint16))
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, x.device)
+    idx = torch.empty(m, dtype=torch.int32, device=x.device)
+    val = torch.empty(m, dtype=torch.float32, device=x.device)
+    _check("fv5b_head_argmax_packed", lib().fv5b_head_argmax_packed(_ptr(wp), _ptr(s), v, k, _ptr(x), m, _ptr(idx),
+                                                                    _ptr(val), _ptr(logits), _ptr(workspace),
+                                                                    _stream(stream)))
+    return idx, val
+
+
+def fv5b_head_argmax_packed_i8(wp, s, v: int, k: int, q, s_x, workspace=None, logits=None, stream=None):
+    import torch
+    m = _fv5b_packed_args(s, v, k, q, (torch.int8,))
+    if workspace is None:
+        workspace = i8_head_argmax_workspace(v, m, q.device)
+    idx = torch.empty(m, dtype=torch.int32, device=q.device)
+    val = torch.empty(m, dtype=torch.float32, device=q.device)
+    _check("fv5b_head_argmax_packed_i8", lib().fv5b_head_argmax_packed_i8(_ptr(wp), _ptr(s), v, k, _ptr(q),
+                                                                          _ptr(s_x), m, _ptr(idx), _ptr(val),
+                                                                          _ptr(logits), _ptr(workspace),
+                                                                          _stream(stream)))
     return idx, val
 
 

@@ -530,6 +530,52 @@ int fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, c
                                                    (hipStream_t)stream));
 }
 
+int fv5b_head_gemv_packed(const int8_t* packed, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                          float* logits, void* stream)
+{
+    int rc = fv5b_head_check(packed, S, V, K, x, nullptr, false, M, logits, true);
+    if (rc) return rc;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_packed_bf16(packed, S, V, K, x, M, logits, (hipStream_t)stream));
+}
+
+int fv5b_head_gemv_packed_i8(const int8_t* packed, const float* S, int64_t V, int64_t K, const int8_t* q,
+                             const float* s_x, int64_t M, float* logits, int32_t* acc_dbg, void* stream)
+{
+    int rc = fv5b_head_check(packed, S, V, K, q, s_x, true, M, logits, true);
+    if (rc) return rc;
+    if (acc_dbg && !aligned4(acc_dbg)) return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_packed_i8(packed, S, V, K, q, s_x, M, logits, acc_dbg, (hipStream_t)stream));
+}
+
+int fv5b_head_argmax_packed(const int8_t* packed, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
+                            int32_t* idx, float* val, float* logits, void* workspace, void* stream)
+{
+    int rc = fv5b_head_check(packed, S, V, K, x, nullptr, false, M, workspace, false);
+    if (rc) return rc;
+    if (!idx || !val) return TERN_E_NULL;
+    if (!aligned4(idx) || !aligned4(val) || (logits && !aligned4(logits)) || ((uintptr_t)workspace & 7))
+        return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_argmax_packed_bf16(packed, S, V, K, x, M, logits, idx, val, workspace,
+                                                            (hipStream_t)stream));
+}
+
+int fv5b_head_argmax_packed_i8(const int8_t* packed, const float* S, int64_t V, int64_t K, const int8_t* q,
+                               const float* s_x, int64_t M, int32_t* idx, float* val, float* logits, void* workspace,
+                               void* stream)
+{
+    int rc = fv5b_head_check(packed, S, V, K, q, s_x, true, M, workspace, false);
+    if (rc) return rc;
+    if (!idx || !val) return TERN_E_NULL;
+    if (!aligned4(idx) || !aligned4(val) || (logits && !aligned4(logits)) || ((uintptr_t)workspace & 7))
+        return TERN_E_ALIGN;
+    if ((rc = check_device())) return rc;
+    return finish(tern::launch_fv5b_head_argmax_packed_i8(packed, S, V, K, q, s_x, M, logits, idx, val, workspace,
+                                                          (hipStream_t)stream));
+}
+
 int fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x, int64_t M,
                            int32_t* idx, float* val, float* logits, void* workspace, const int8_t* E, const float* ES,
                            int64_t Ve, int64_t Ke, float* emb, uint16_t* emb_bf16, void* stream)

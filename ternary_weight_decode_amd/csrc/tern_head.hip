@@ -314,7 +314,6 @@ __global__ __launch_bounds__(256) void head_fast_kernel(const int8_t* __restrict
                                                         const float* __restrict__ s_x, int M, float* __restrict__ y,
                                                         int32_t* __restrict__ acc_dbg, HeadArgmax am)
 {
-    static_assert(!(kBlk && kPacked), "the packed layout holds per-row-scaled weights");
     static_assert(!kBlk || TPW % 2 == 0, "a block's two units share a ring parity");
     extern __shared__ __align__(16) uint8_t smem[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -647,6 +646,33 @@ hipError_t launch_fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V
                                       hipStream_t stream)
 {
     return launch_head_argmax<true, true>(W, S, V, K, q, s_x, M, y, idx, val, ws, stream);
+}
+
+// the block-scaled head over the packed copy of its int8 rows (the scales stay [V][K/256])
+hipError_t launch_fv5b_head_packed_bf16(const int8_t* Wp, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                        int64_t M, float* y, hipStream_t stream)
+{
+    return launch_head_fast<false, kHeadPackedTpw, true, true>(Wp, S, V, K, x, nullptr, M, y, nullptr, stream);
+}
+
+hipError_t launch_fv5b_head_packed_i8(const int8_t* Wp, const float* S, int64_t V, int64_t K, const int8_t* q,
+                                      const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    return launch_head_fast<true, kHeadPackedTpw, true, true>(Wp, S, V, K, q, s_x, M, y, acc, stream);
+}
+
+hipError_t launch_fv5b_head_argmax_packed_bf16(const int8_t* Wp, const float* S, int64_t V, int64_t K,
+                                               const uint16_t* x, int64_t M, float* y, int32_t* idx, float* val,
+                                               void* ws, hipStream_t stream)
+{
+    return launch_head_argmax<false, true, true>(Wp, S, V, K, x, nullptr, M, y, idx, val, ws, stream);
+}
+
+hipError_t launch_fv5b_head_argmax_packed_i8(const int8_t* Wp, const float* S, int64_t V, int64_t K,
+                                             const int8_t* q, const float* s_x, int64_t M, float* y, int32_t* idx,
+                                             float* val, void* ws, hipStream_t stream)
+{
+    return launch_head_argmax<true, true, true>(Wp, S, V, K, q, s_x, M, y, idx, val, ws, stream);
 }
 
 // Embedding rows: one thread per 16 weights of an output row (embed_chunk).

@@ -69,6 +69,16 @@ hipError_t launch_fv5b_head_argmax_bf16(const int8_t* W, const float* S, int64_t
 hipError_t launch_fv5b_head_argmax_i8(const int8_t* W, const float* S, int64_t V, int64_t K, const int8_t* q,
                                       const float* s_x, int64_t M, float* y, int32_t* idx, float* val, void* ws,
                                       hipStream_t stream);
+hipError_t launch_fv5b_head_packed_bf16(const int8_t* Wp, const float* S, int64_t V, int64_t K, const uint16_t* x,
+                                        int64_t M, float* y, hipStream_t stream);
+hipError_t launch_fv5b_head_packed_i8(const int8_t* Wp, const float* S, int64_t V, int64_t K, const int8_t* q,
+                                      const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream);
+hipError_t launch_fv5b_head_argmax_packed_bf16(const int8_t* Wp, const float* S, int64_t V, int64_t K,
+                                               const uint16_t* x, int64_t M, float* y, int32_t* idx, float* val,
+                                               void* ws, hipStream_t stream);
+hipError_t launch_fv5b_head_argmax_packed_i8(const int8_t* Wp, const float* S, int64_t V, int64_t K,
+                                             const int8_t* q, const float* s_x, int64_t M, float* y, int32_t* idx,
+                                             float* val, void* ws, hipStream_t stream);
 hipError_t launch_fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int32_t* ids, int64_t M,
                              float* out, uint16_t* out_bf16, hipStream_t stream);
 hipError_t launch_fv5b_head_argmax_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const uint16_t* x,

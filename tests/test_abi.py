@@ -354,3 +354,23 @@ def test_packed_head_argmax_argument_errors():
     assert f(m, p, 100, 128, p, 1, p, p, None, p, None) == E_ALIGN
     assert f(p, p, 100, 128, p, 1, p, p, ctypes.c_void_p(0x10002), p, None) == E_ALIGN   # logits
     assert fi(p, p, 100, 128, p, p, 1, p, p, None, ctypes.c_void_p(0x10004), None) == E_ALIGN   # workspace % 8
+
+
+def test_fv5b_packed_head_argument_errors():
+    L = tw.lib()
+    p, m = ALIGNED, MISALIGNED
+    g, gi = L.fv5b_head_gemv_packed, L.fv5b_head_gemv_packed_i8
+    f, fi = L.fv5b_head_argmax_packed, L.fv5b_head_argmax_packed_i8
+    assert g(p, p, 100, 128, p, 1, p, None) == E_SHAPE                     # K % 256
+    assert g(p, p, 0, 256, p, 1, p, None) == E_SHAPE
+    assert g(p, p, 100, 256, p, 17, p, None) == E_SHAPE
+    assert g(p, p, 100, 8192, p, 16, p, None) == E_SHAPE                   # bf16 x exceeds LDS
+    assert g(None, p, 100, 256, p, 1, p, None) == E_NULL
+    assert g(p, None, 100, 256, p, 1, p, None) == E_NULL
+    assert g(m, p, 100, 256, p, 1, p, None) == E_ALIGN
+    assert gi(p, p, 100, 256, p, None, 1, p, None, None) == E_NULL         # s_x
+    assert gi(p, p, 100, 256, p, p, 1, p, ctypes.c_void_p(0x10002), None) == E_ALIGN   # acc_dbg
+    assert f(p, p, 100, 128, p, 1, p, p, None, p, None) == E_SHAPE
+    assert f(p, p, 100, 256, p, 1, None, p, None, p, None) == E_NULL       # idx
+    assert f(p, p, 100, 256, p, 1, p, p, None, None, None) == E_NULL       # workspace
+    assert fi(p, p, 100, 256, p, p, 1, p, p, None, ctypes.c_void_p(0x10004), None) == E_ALIGN

@@ -167,3 +167,42 @@ def test_packed_argmax_padding_rows_never_win(tw):
     idx_r, val_r = tw.i8_head_argmax(dev(w), dev(rs), dev(x))
     assert (host(idx_b) < v).all() and (host(val_b) < 0).all()
     assert np.array_equal(host(idx_b), host(idx_r)) and np.array_equal(host(val_b), host(val_r))
+
+
+@pytest.mark.parametrize("v,k,m", [(70, 256, 1), (1000, 4096, 4), (300, 1024, 16), (151936, 4096, 1)])
+def test_fv5b_packed_matches_row_major(tw, v, k, m):
+    """The block-scaled (FV5B-style) head over the packed copy of its int8
+    rows: logits, block sums, and the fused argmax's index, value and logits
+    bit for bit those of the row-major calls (bf16 and int8 activations);
+    against the oracle where it runs in seconds."""
+    import torch
+    from oracle import fv5b
+    rng = np.random.default_rng(v + 3 * k + m)
+    w, S = synth.gen_head_blocks(rng, rng, v, k)
+    x = synth.gen_x_bf16(rng, m, k)
+    q, sx = oracle.quantize_i8(x)
+    wd, Sd, xd, qd, sxd = dev(w), dev(S), dev(x), dev(q), dev(sx)
+    wp = tw.i8_head_pack(wd)
+    y_rm = host(tw.fv5b_head_gemv(wd, Sd, xd))
+    assert np.array_equal(host(tw.fv5b_head_gemv_packed(wp, Sd, v, k, xd)), y_rm)
+    acc_rm = torch.empty((m, v, k // 256), dtype=torch.int32, device="cuda")
+    acc_p = torch.empty((m, v, k // 256), dtype=torch.int32, device="cuda")
+    yi_rm = host(tw.fv5b_head_gemv_i8(wd, Sd, qd, sxd, acc=acc_rm))
+    yi_p = host(tw.fv5b_head_gemv_packed_i8(wp, Sd, v, k, qd, sxd, acc=acc_p))
+    assert np.array_equal(yi_p, yi_rm) and np.array_equal(host(acc_p), host(acc_rm))
+    ws = tw.i8_head_argmax_workspace(v, m)
+    for fn_rm, fn_p, args in ((tw.fv5b_head_argmax, tw.fv5b_head_argmax_packed, (xd,)),
+                              (tw.fv5b_head_argmax_i8, tw.fv5b_head_argmax_packed_i8, (qd, sxd))):
+        l_rm = torch.empty((m, v), dtype=torch.float32, device="cuda")
+        l_p = torch.empty((m, v), dtype=torch.float32, device="cuda")
+        i_rm, v_rm = fn_rm(wd, Sd, *args, workspace=ws, logits=l_rm)
+        i_rm, v_rm, l_rm = host(i_rm), host(v_rm), host(l_rm)
+        i_p, v_p = fn_p(wp, Sd, v, k, *args, workspace=ws, logits=l_p)
+        assert np.array_equal(host(i_p), i_rm)
+        assert np.array_equal(host(v_p).view(np.uint32), v_rm.view(np.uint32))
+        assert np.array_equal(host(l_p), l_rm)
+    if v * k <= 4096 * 1000:
+        y64, _ = fv5b.head_bf16(w, S, x)
+        assert oracle.rel_l2(y_rm, y64) <= TOL
+        acc0 = fv5b.head_i8(w, S, q, sx)[0]
+        assert np.array_equal(host(acc_p), acc0)
