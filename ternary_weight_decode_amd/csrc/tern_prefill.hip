@@ -630,14 +630,14 @@ __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
 // block scale in block order; the nkt partials of each output meet in LDS once
 // and are summed in k-tile order (deterministic).  Rows past M repeat row M-1
 // and row tiles past N the last real one; their outputs are dropped.
-template <int MG, int R, bool kDbg>
+template <int MG, int R, int KT, bool kDbg>
 __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restrict__ packed, int64_t N, int64_t K,
                                                           const int8_t* __restrict__ q,
                                                           const float* __restrict__ s_x, int M,
                                                           float* __restrict__ y, int32_t* __restrict__ acc_dbg)
 {
     extern __shared__ __align__(16) uint8_t smem[];
-    const int nkt = (int)(blockDim.x >> 6);                          // one wave per k-tile
+    const int nw = (int)(blockDim.x >> 6);                           // KT k-tiles per wave
     const int kw = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int r = lane & 15, g = lane >> 4;
     const int nb = (int)(K >> 7);
@@ -647,39 +647,43 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
     const TERN_GLOBAL uint32_t* words = (const TERN_GLOBAL uint32_t*)packed;
     const TERN_GLOBAL uint16_t* scales = (const TERN_GLOBAL uint16_t*)(packed + scale_region_offset(N, K));
 
-    // the plane words of this wave's R units, then its activations, all requested up front
-    PlaneTile t[R];
+    // the plane words of this wave's R x KT units, then its activations, all requested up front
+    PlaneTile t[R][KT];
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int64_t rt = rt0 + i < nrt ? rt0 + i : nrt - 1;
-        const int64_t wb = tile_word_base(rt, kw, nb);
-        t[i].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
-        t[i].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+#pragma unroll
+        for (int j = 0; j < KT; ++j) {
+            const int64_t wb = tile_word_base(rt, kw * KT + j, nb);
+            t[i][j].nz = ld_nt16(words + wb + (int64_t)(g * 16 + r) * 4);
+            t[i][j].sg = ld_nt16(words + wb + (int64_t)((4 + g) * 16 + r) * 4);
+        }
     }
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         const int64_t rt = rt0 + i < nrt ? rt0 + i : nrt - 1;
-        t[i].sc = ld_nt8(scales + tile_scale_base(rt, kw, nb) + r * 4);
+#pragma unroll
+        for (int j = 0; j < KT; ++j) t[i][j].sc = ld_nt8(scales + tile_scale_base(rt, kw * KT + j, nb) + r * 4);
     }
     // Each load covers 64 contiguous bytes of every row (lane group g takes 16-byte piece
     // c(g) = 2(g & 1) + (g >> 1) of the block's first, then second, 64 bytes); one swap of
     // the upper 32 lanes of the first with the lower 32 lanes of the second then leaves
     // lane group g with pieces 2g and 2g + 1, its 32-byte word.
     const TERN_GLOBAL u32x4* qg = (const TERN_GLOBAL u32x4*)q;
-    u32x4 A[MG][4][2];
+    u32x4 A[MG][4 * KT][2];
     const int piece = 2 * (g & 1) + (g >> 1);
 #pragma unroll
     for (int mg = 0; mg < MG; ++mg) {
         const int m = m0 + mg * 16 + r < M ? m0 + mg * 16 + r : M - 1;
-        const int64_t base = (((int64_t)m * K + kTileK * kw) >> 4) + piece;   // in 16-byte units
+        const int64_t base = (((int64_t)m * K + kTileK * KT * kw) >> 4) + piece;   // in 16-byte units
 #pragma unroll
-        for (int bq = 0; bq < 4; ++bq) {
-            A[mg][bq][0] = qg[base + 8 * bq];
-            A[mg][bq][1] = qg[base + 8 * bq + 4];
+        for (int b = 0; b < 4 * KT; ++b) {
+            A[mg][b][0] = qg[base + 8 * b];
+            A[mg][b][1] = qg[base + 8 * b + 4];
         }
     }
 
-    float* red = (float*)smem;                                       // [R][nkt][MG][4][64]
+    float* red = (float*)smem;                                       // [R][nw][MG][4][64]
 #pragma unroll
     for (int i = 0; i < R; ++i) {
         f32x4 acc[MG];
@@ -687,34 +691,35 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
         for (int mg = 0; mg < MG; ++mg) acc[mg] = f32x4{0.f, 0.f, 0.f, 0.f};
         const int64_t n = (rt0 + i) * kTileRows + r;
 #pragma unroll
-        for (int bq = 0; bq < 4; ++bq) {
+        for (int b = 0; b < 4 * KT; ++b) {
+            const int j = b >> 2, bq = b & 3;
             if (i == 0) {
                 // pieces to words, then natural bytes -> the decoded order, once per activation word
 #pragma unroll
                 for (int mg = 0; mg < MG; ++mg) {
 #pragma unroll
                     for (int d = 0; d < 4; ++d) {
-                        const auto sw = __builtin_amdgcn_permlane32_swap(A[mg][bq][0][d], A[mg][bq][1][d], false,
+                        const auto sw = __builtin_amdgcn_permlane32_swap(A[mg][b][0][d], A[mg][b][1][d], false,
                                                                          false);
-                        A[mg][bq][0][d] = sw[0];
-                        A[mg][bq][1][d] = sw[1];
+                        A[mg][b][0][d] = sw[0];
+                        A[mg][b][1][d] = sw[1];
                     }
-                    const uint32_t Q[8] = {A[mg][bq][0][0], A[mg][bq][0][1], A[mg][bq][0][2], A[mg][bq][0][3],
-                                           A[mg][bq][1][0], A[mg][bq][1][1], A[mg][bq][1][2], A[mg][bq][1][3]};
+                    const uint32_t Q[8] = {A[mg][b][0][0], A[mg][b][0][1], A[mg][b][0][2], A[mg][b][0][3],
+                                           A[mg][b][1][0], A[mg][b][1][1], A[mg][b][1][2], A[mg][b][1][3]};
 #pragma unroll
-                    for (int d = 0; d < 4; ++d) A[mg][bq][0][d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+                    for (int d = 0; d < 4; ++d) A[mg][b][0][d] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
 #pragma unroll
-                    for (int d = 4; d < 8; ++d) A[mg][bq][1][d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
+                    for (int d = 4; d < 8; ++d) A[mg][b][1][d - 4] = i8_act_quad(Q[d >> 1], Q[4 + (d >> 1)], d);
                 }
             }
             u32x4 B[2];
-            decode_i8(t[i].nz[bq], t[i].sg[bq], B);
-            const float sc = tile_scale(t[i], bq) * (1.0f / 64.0f);    // decoded weights are 64*t
+            decode_i8(t[i][j].nz[bq], t[i][j].sg[bq], B);
+            const float sc = tile_scale(t[i][j], bq) * (1.0f / 64.0f);    // decoded weights are 64*t
             i32x4 dd[MG];
 #pragma unroll
-            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][bq][0], B[0], i32x4{0, 0, 0, 0});
+            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][b][0], B[0], i32x4{0, 0, 0, 0});
 #pragma unroll
-            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][bq][1], B[1], dd[mg]);
+            for (int mg = 0; mg < MG; ++mg) dd[mg] = mfma_i8(A[mg][b][1], B[1], dd[mg]);
 #pragma unroll
             for (int mg = 0; mg < MG; ++mg) {
                 const i32x4 d = dd[mg];
@@ -724,7 +729,7 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int m = m0 + mg * 16 + 4 * g + e;
-                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kw * 4 + bq] = d[e] >> 6;
+                        if (m < M && n < N) acc_dbg[((int64_t)m * N + n) * nb + kw * KT * 4 + b] = d[e] >> 6;
                     }
                 }
             }
@@ -732,7 +737,7 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
 #pragma unroll
         for (int mg = 0; mg < MG; ++mg)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) red[((((i * nkt + kw) * MG + mg) * 4 + e) << 6) + lane] = acc[mg][e];
+            for (int e = 0; e < 4; ++e) red[((((i * nw + kw) * MG + mg) * 4 + e) << 6) + lane] = acc[mg][e];
     }
     __syncthreads();
     const int nout = R * MG * 4 * 64;
@@ -742,7 +747,7 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
         const int64_t n = (rt0 + i) * kTileRows + (l & 15);
         if (m < M && n < N) {
             float sum = 0.f;
-            for (int kt = 0; kt < nkt; ++kt) sum += red[((((i * nkt + kt) * MG + mg) * 4 + e) << 6) + l];
+            for (int w = 0; w < nw; ++w) sum += red[((((i * nw + w) * MG + mg) * 4 + e) << 6) + l];
             y[(int64_t)m * N + n] = s_x[m] * sum;
         }
     }
@@ -762,38 +767,60 @@ __global__ __launch_bounds__(512) void prefill_reg_kernel(const uint8_t* __restr
 // into single groups 9.4 against 9.5 us (decode work doubled), so those stay
 // whole.
 struct PfReg {
-    int MG, R, nw, S;
+    int MG, R, nw, S, KT;
     int64_t grid;
     size_t lds;
 };
 
 static bool pick_pf_reg(int64_t N, int64_t K, int64_t M, PfReg& c)
 {
-    if (K % kTileK != 0 || K > 8 * kTileK || M < 17 || M > 64 || N < 1) return false;
-    // two or three 16-row groups in one workgroup; four as two halves in two grid rows
-    const int64_t groups = (M + 15) / 16;
-    c.MG = (int)(groups <= 3 ? groups : 2);
-    c.S = (int)(groups <= 3 ? 1 : 2);
-    c.nw = (int)(K / kTileK);
+    if (K % kTileK != 0 || M < 17 || M > 64 || N < 1) return false;
+    const int64_t nkt = K / kTileK, groups = (M + 15) / 16;
+    if (nkt <= 8) {
+        // one k-tile per wave; two or three 16-row groups in one workgroup, four as two
+        // halves in two grid rows
+        c.KT = 1;
+        c.MG = (int)(groups <= 3 ? groups : 2);
+        c.S = (int)(groups <= 3 ? 1 : 2);
+    } else if (nkt % 8 == 0 && nkt / 8 <= 3) {
+        // eight waves of KT k-tiles each, every 16-row group in a grid row of its own
+        // (K up to 12288: KT*32 activation registers per wave)
+        c.KT = (int)(nkt / 8);
+        c.MG = 1;
+        c.S = (int)groups;
+    } else {
+        return false;
+    }
+    c.nw = (int)(nkt / c.KT);
+    // the smallest R whose grid fits the CUs in one round (at most 8 row tiles, 4 with several
+    // k-tiles per wave: the plane words of R*KT units stay in registers)
     const int64_t nrt = (N + 15) / 16, slots = device_cus() * (8 / c.nw);
-    int64_t R = (nrt * c.S + slots - 1) / slots;
-    R = R < 1 ? 1 : R;
-    c.R = (int)(R <= 4 ? R : (R <= 6 ? 6 : 8));
+    static const int kR1[] = {1, 2, 3, 4, 6, 8}, kR3[] = {1, 2, 3, 4};
+    const int* rs = c.KT == 1 ? kR1 : kR3;
+    const int nr = c.KT == 1 ? 6 : 4;
+    c.R = rs[nr - 1];
+    for (int i = 0; i < nr; ++i) {
+        if ((nrt + rs[i] - 1) / rs[i] * c.S <= slots) {
+            c.R = rs[i];
+            break;
+        }
+    }
     c.grid = (nrt + c.R - 1) / c.R;
     c.lds = (size_t)c.R * c.nw * c.MG * 4 * 64 * 4;
     return c.lds <= (size_t)kCuLds;
 }
 
-template <int MG, int R>
+template <int MG, int R, int KT>
 static hipError_t launch_pf_reg_r(const PfReg& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
+    const dim3 grid((unsigned)c.grid, (unsigned)c.S);
     if (acc)
-        prefill_reg_kernel<MG, R, true><<<dim3((unsigned)c.grid, (unsigned)c.S), dim3(64 * c.nw), c.lds, stream>>>(
-            packed, N, K, q, s_x, (int)M, y, acc);
+        prefill_reg_kernel<MG, R, KT, true><<<grid, dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, q, s_x, (int)M,
+                                                                                        y, acc);
     else
-        prefill_reg_kernel<MG, R, false><<<dim3((unsigned)c.grid, (unsigned)c.S), dim3(64 * c.nw), c.lds, stream>>>(
-            packed, N, K, q, s_x, (int)M, y, acc);
+        prefill_reg_kernel<MG, R, KT, false><<<grid, dim3(64 * c.nw), c.lds, stream>>>(packed, N, K, q, s_x, (int)M,
+                                                                                         y, acc);
     return hipGetLastError();
 }
 
@@ -802,12 +829,24 @@ static hipError_t launch_pf_reg_mg(const PfReg& c, const uint8_t* packed, int64_
                                    const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     switch (c.R) {
-    case 1: return launch_pf_reg_r<MG, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
-    case 2: return launch_pf_reg_r<MG, 2>(c, packed, N, K, q, s_x, M, y, acc, stream);
-    case 3: return launch_pf_reg_r<MG, 3>(c, packed, N, K, q, s_x, M, y, acc, stream);
-    case 4: return launch_pf_reg_r<MG, 4>(c, packed, N, K, q, s_x, M, y, acc, stream);
-    case 6: return launch_pf_reg_r<MG, 6>(c, packed, N, K, q, s_x, M, y, acc, stream);
-    default: return launch_pf_reg_r<MG, 8>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 1: return launch_pf_reg_r<MG, 1, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 2: return launch_pf_reg_r<MG, 2, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 3: return launch_pf_reg_r<MG, 3, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 4: return launch_pf_reg_r<MG, 4, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 6: return launch_pf_reg_r<MG, 6, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    default: return launch_pf_reg_r<MG, 8, 1>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    }
+}
+
+template <int KT>
+static hipError_t launch_pf_reg_kt(const PfReg& c, const uint8_t* packed, int64_t N, int64_t K, const int8_t* q,
+                                   const float* s_x, int64_t M, float* y, int32_t* acc, hipStream_t stream)
+{
+    switch (c.R) {
+    case 1: return launch_pf_reg_r<1, 1, KT>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 2: return launch_pf_reg_r<1, 2, KT>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    case 3: return launch_pf_reg_r<1, 3, KT>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    default: return launch_pf_reg_r<1, 4, KT>(c, packed, N, K, q, s_x, M, y, acc, stream);
     }
 }
 
@@ -816,6 +855,8 @@ static hipError_t launch_pf_reg(const uint8_t* packed, int64_t N, int64_t K, con
 {
     PfReg c;
     if (!pick_pf_reg(N, K, M, c)) return hipErrorNotSupported;
+    if (c.KT == 2) return launch_pf_reg_kt<2>(c, packed, N, K, q, s_x, M, y, acc, stream);
+    if (c.KT == 3) return launch_pf_reg_kt<3>(c, packed, N, K, q, s_x, M, y, acc, stream);
     if (c.MG == 2) return launch_pf_reg_mg<2>(c, packed, N, K, q, s_x, M, y, acc, stream);
     return launch_pf_reg_mg<3>(c, packed, N, K, q, s_x, M, y, acc, stream);
 }

@@ -383,11 +383,13 @@ def test_prefill_small_m_split_k(tw, n, k, m):
 
 
 @pytest.mark.parametrize("n,k,m", [(16, 512, 17), (1000, 1024, 40), (9000, 2048, 64), (12290, 4096, 33),
-                                   (6000, 4096, 64), (333, 2560, 50)])
+                                   (6000, 4096, 64), (333, 2560, 50), (700, 8192, 50), (130, 12288, 64),
+                                   (4100, 12288, 19)])
 def test_prefill_register_activations(tw, n, k, m):
-    """17 <= M <= 64 with K <= 4096 (K a multiple of 512): one wave per k-tile
-    holding its activations in registers over 1 to 4 row tiles per workgroup
-    (ragged last row tile and last 16-row group, two to four row groups):
+    """17 <= M <= 64, K a multiple of 512: up to K = 4096 one wave per k-tile,
+    above (K = 8192, 12288) eight waves of two or three k-tiles, holding their
+    activations in registers over 1 to 4 row tiles per workgroup (ragged last
+    row tile and last 16-row group, one to four row groups per grid row):
     block sums bit for bit, y against the oracle, and the production instance
     (no block sums) the same bytes."""
     import torch
