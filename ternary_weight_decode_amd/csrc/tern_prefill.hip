@@ -234,10 +234,10 @@ struct Pf2 {
     static_assert(kActPerThread >= 2 && kActPerThread % 2 == 0, "activations staged in 32-byte words");
 };
 
-template <int TM, int TN, int WGM, int WGN, bool kDbg>
+template <int TM, int TN, int WGM, int WGN, bool kSplit, bool kDbg>
 __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
     const uint8_t* __restrict__ packed, int64_t N, int64_t K, const int8_t* __restrict__ q,
-    const float* __restrict__ s_x, int64_t M, float* __restrict__ y, int32_t* __restrict__ acc_dbg)
+    const float* __restrict__ s_x, int64_t M, float* __restrict__ y, int32_t* __restrict__ acc_dbg, int kts)
 {
     using C = Pf2<TM, TN, WGM, WGN>;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -247,7 +247,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
     const int wm = wave / WGN, wn = wave % WGN;
     const int64_t m0 = (int64_t)blockIdx.y * C::BM;
     const int64_t rt0 = (int64_t)blockIdx.x * C::NRT;
-    const int nb = (int)(K / kBlockK), nkt = nb >> 2;
+    const int nb = (int)(K / kBlockK);
+    // this workgroup's k-tiles: [kt0, kt0 + nkt) of the row's K / 512 (all of them unless split)
+    const int kt0 = kSplit ? (int)blockIdx.z * kts : 0;
+    const int nkt = kSplit ? min(kts, (nb >> 2) - kt0) : nb >> 2;
+    const int nbl = 4 * nkt;
     const int64_t nrt = (N + 15) >> 4;
     const uint32_t* words = (const uint32_t*)packed;
     const uint16_t* scales = (const uint16_t*)(packed + scale_region_offset(N, K));
@@ -269,7 +273,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
 
     // plane words of k-tile kt for this thread's (row tile, r, g); rows past N read tile 0 (outputs dropped)
     auto load_planes = [&](int kt, PfPlanes<1>& P) {
-        const int ktc = kt < nkt ? kt : nkt - 1;
+        const int ktc = (kt < nkt ? kt : nkt - 1) + kt0;
         const int64_t rt = drow_ok ? drt : 0;
         const int64_t wb = tile_word_base(rt, ktc, nb);
         P.nz[0] = ld_nt16(words + wb + ((0 * 4 + g) * 16 + r) * 4);
@@ -277,7 +281,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
         P.sc[0] = ld_nt8(scales + tile_scale_base(rt, ktc, nb) + r * 4);
     };
     auto load_act = [&](int b, u32x4 (&v)[C::kActPerThread]) {
-        const int bc = b < nb ? b : nb - 1;
+        const int bc = (b < nbl ? b : nbl - 1) + 4 * kt0;
         const u32x4* src = (const u32x4*)(asrc + (int64_t)bc * kBlockK);
 #pragma unroll
         for (int i = 0; i < C::kActPerThread; ++i) v[i] = src[i];
@@ -356,7 +360,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             const int64_t m = m0 + wm * 16 * TM + 16 * i + 4 * g + e;
-                            if (m < M && n < N) acc_dbg[(m * N + n) * nb + b] = dprev[i][e] >> 6;
+                            if (m < M && n < N) acc_dbg[(m * N + n) * nb + 4 * kt0 + b] = dprev[i][e] >> 6;
                         }
                     }
                 }
@@ -384,8 +388,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
     // last block, compute and writes are skipped but the (clamped) loads are
     // still issued, so every pass issues the same loads.
     auto block = [&](int b, const PfPlanes<1>& Pnext_src, int nbq_src, u32x4 (&vnext)[C::kActPerThread]) {
-        if (b < nb) compute(b & 1, b);
-        if (b + 1 < nb) write_stage((b + 1) & 1, Pnext_src, nbq_src, vnext);
+        if (b < nbl) compute(b & 1, b);
+        if (b + 1 < nbl) write_stage((b + 1) & 1, Pnext_src, nbq_src, vnext);
         load_act(b + 3, vnext);
         __syncthreads();
     };
@@ -412,9 +416,34 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int64_t m = m0 + wm * 16 * TM + 16 * i + 4 * g + e;
-                if (m < M) y[m * N + n] = s_x[m] * facc[i][j][e];
+                if (m < M) {
+                    if constexpr (kSplit)
+                        unsafeAtomicAdd(y + m * N + n, facc[i][j][e]);
+                    else
+                        y[m * N + n] = s_x[m] * facc[i][j][e];
+                }
             }
     }
+}
+
+// y[m][n] *= s_x[m] over an M x N row-major output (the split prefill's last pass)
+__global__ __launch_bounds__(256) void scale_rows_kernel(float* __restrict__ y, const float* __restrict__ s_x,
+                                                         int64_t M, int64_t N)
+{
+    for (int64_t m = blockIdx.y; m < M; m += gridDim.y) {
+        const float s = s_x[m];
+        float* row = y + m * N;
+        for (int64_t n = (int64_t)blockIdx.x * 256 + threadIdx.x; n < N; n += (int64_t)gridDim.x * 256)
+            row[n] = s * row[n];
+    }
+}
+
+static hipError_t launch_scale_rows(float* y, const float* s_x, int64_t M, int64_t N, hipStream_t stream)
+{
+    const int64_t gx = (N + 255) / 256;
+    const dim3 grid((unsigned)(gx < 64 ? gx : 64), (unsigned)(M < 4096 ? M : 4096));
+    scale_rows_kernel<<<grid, 256, 0, stream>>>(y, s_x, M, N);
+    return hipGetLastError();
 }
 
 template <int TM, int TN, int WGM, int WGN>
@@ -422,13 +451,40 @@ static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const 
                              int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     using C = Pf2<TM, TN, WGM, WGN>;
-    const dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM));
-    if (acc)
-        prefill2_kernel<TM, TN, WGM, WGN, true><<<grid, C::kThreads, C::kLds, stream>>>(packed, N, K, q, s_x, M, y,
-                                                                                      acc);
-    else
-        prefill2_kernel<TM, TN, WGM, WGN, false><<<grid, C::kThreads, C::kLds, stream>>>(packed, N, K, q, s_x, M, y,
-                                                                                       acc);
+    const int nkt = (int)(K / 512);
+    const int64_t tiles = ((N + C::BN - 1) / C::BN) * ((M + C::BM - 1) / C::BM);
+    // K split in two halves when both halves' workgroups still fit one per CU and each half
+    // keeps at least 4 k-tiles.  A lone workgroup on a CU runs its blocks one after another
+    // (about 0.65 us per 128-k block on the 8B down shape whatever the tile count), so the
+    // split halves the time where CUs would otherwise idle: 8B down at M = 128 / 256 / 1024
+    // 61.5 / 61.8 / 135.0 us -> 38.6 / 43.7 / 102.4 us.  Two workgroups per CU gain nothing
+    // (down at M = 512: 62.6 vs 63.7 us) and short K loses to the two extra passes (gate at
+    // M = 128: 26.4 vs 31.8 us).  y is cleared first, each half adds its unscaled partial
+    // with one atomic fp32 add per element (two addends onto zero give the same sum in
+    // either order, so y is deterministic), and a last pass multiplies each row by s_x:
+    // y = fl(s_x * fl(a + b)).
+    const bool split = nkt >= 8 && 2 * tiles <= 256;
+    const int kts = split ? (nkt + 1) / 2 : nkt;
+    const dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM), split ? 2u : 1u);
+    if (split) {
+        const hipError_t e = launch_fill_zero(y, M * N * 4, stream);
+        if (e != hipSuccess) return e;
+        if (acc)
+            prefill2_kernel<TM, TN, WGM, WGN, true, true><<<grid, C::kThreads, C::kLds, stream>>>(
+                packed, N, K, q, s_x, M, y, acc, kts);
+        else
+            prefill2_kernel<TM, TN, WGM, WGN, true, false><<<grid, C::kThreads, C::kLds, stream>>>(
+                packed, N, K, q, s_x, M, y, acc, kts);
+        const hipError_t e2 = hipGetLastError();
+        if (e2 != hipSuccess) return e2;
+        return launch_scale_rows(y, s_x, M, N, stream);
+    } else if (acc) {
+        prefill2_kernel<TM, TN, WGM, WGN, false, true><<<grid, C::kThreads, C::kLds, stream>>>(
+            packed, N, K, q, s_x, M, y, acc, kts);
+    } else {
+        prefill2_kernel<TM, TN, WGM, WGN, false, false><<<grid, C::kThreads, C::kLds, stream>>>(
+            packed, N, K, q, s_x, M, y, acc, kts);
+    }
     return hipGetLastError();
 }
 

@@ -289,8 +289,11 @@ def test_head_one_hot_exact(tw):
     assert np.array_equal(y[0], (rs.astype(np.float64) * w[:, 333]).astype(np.float32))
 
 
-@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (40, 640, 64), (256, 1536, 130), (200, 2048, 300)])
+@pytest.mark.parametrize("n,k,m", [(16, 128, 1), (40, 640, 64), (256, 1536, 130), (200, 2048, 300),
+                                   (200, 4608, 300), (100, 8192, 1100)])
 def test_prefill_small(tw, n, k, m):
+    """Block sums bit for bit and y against the oracle.  The last two cases run the
+    workgroup-shared decode with K split in two halves (9 and 16 k-tiles of 512)."""
     t, s, x = gen(n, k, m, seed=n + m)
     q0, s0 = oracle.quantize_i8(x)
     import torch
@@ -341,12 +344,14 @@ def test_prefill_no_debug_matches_oracle(tw, n, k, m):
     assert np.array_equal(y, yi)
 
 
-def test_prefill_exact_on_power_of_two_scales(tw):
+@pytest.mark.parametrize("n,k,m", [(300, 4096, 200), (300, 2048, 200), (200, 4096, 1100), (100, 2048, 1100)])
+def test_prefill_exact_on_power_of_two_scales(tw, n, k, m):
     """Block scales from {1/4, 1/2, 1, 2}: every scaled block sum and every
     partial sum of the fold is a multiple of 1/4 below 2^22, so fp32 holds it
     exactly and y must equal fl32(s_x * sum_b scale_b * acc_b) bit for bit,
-    with acc the oracle's exact block sums."""
-    n, k, m = 300, 4096, 200
+    with acc the oracle's exact block sums.  Both workgroup tiles (M below and
+    above 1024), with K split in two halves (K = 4096 on a small grid) and
+    whole (K = 2048)."""
     rng = np.random.default_rng(8)
     t = synth.gen_ternary(rng, n, k)
     s = rng.choice(np.array([0.25, 0.5, 1.0, 2.0], np.float16), size=(n, k // 128)).view(np.uint16)
