@@ -248,7 +248,11 @@ int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, i
  * set by its per-block latency, the call may run the int8 GEMV on 16-row
  * slices of q instead (chosen on the host from the shape); the result is the
  * same contraction (fp32 y may differ in the last bits with the kernel: the
- * block sums are added in a kernel-specific order).
+ * block sums are added in a kernel-specific order).  From M = 128, when the
+ * output tiles leave most CUs idle and K >= 4096, K is split in two halves:
+ * the call then enqueues three kernels (y cleared, the two halves' unscaled
+ * fp32 partials added with atomics, rows scaled by s_x), so y is
+ * fl(s_x * fl(a + b)) and the same on every run.
  *   q int8 [M][K]; s_x fp32 [M]; y fp32 [M][N];
  *   acc_dbg NULL or int32 [M][N][K/128] (debug; small shapes). */
 int tern_gemm_prefill(const void* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x, int64_t M,
