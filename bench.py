@@ -207,11 +207,18 @@ class ProfilerRegion:
             self.lib.roctxProfilerPause(0)
 
 
-def time_replays(torch, g, reps: int, region: ProfilerRegion | None = None) -> float:
-    """Mean milliseconds per replay from HIP events on the replay stream.  With a region,
-    exactly the timed replays run inside it."""
-    g.replay()
-    torch.cuda.synchronize()
+def time_replays(torch, g, reps: int, region: ProfilerRegion | None = None, warm_ms: float = 20.0) -> float:
+    """Mean milliseconds per replay from HIP events on the replay stream, after untimed
+    replays for at least warm_ms (at least one): a case timed right after its inputs were
+    generated ran up to 10% slower with a single warm-up replay (8B gate prefill at
+    M = 2048: 178.7 vs 165.6 us for the same kernel timed later).  With a region, exactly
+    the timed replays run inside it."""
+    t0 = time.perf_counter()
+    for i in range(1000):
+        g.replay()
+        torch.cuda.synchronize()
+        if (time.perf_counter() - t0) * 1e3 >= warm_ms:
+            break
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     if region is not None:
         region.resume()

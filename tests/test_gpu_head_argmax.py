@@ -53,12 +53,21 @@ def test_head_argmax_i8_exact(tw, v, k, m):
     q, sx = oracle.quantize_i8(x)
     logits = torch.full((m, v), float("nan"), dtype=torch.float32, device="cuda")
     idx, val = tw.i8_head_argmax_i8(dev(w), dev(rs), dev(q), dev(sx), logits=logits)
-    acc, _, _ = oracle.head_i8(w, rs, q, sx)
+    acc, y64, _ = oracle.head_i8(w, rs, q, sx)
     l32 = oracle.head_i8_logits_f32(acc, rs, sx)
     i0, v0 = oracle.greedy_argmax(l32)
     assert np.array_equal(host(idx), i0)
     assert np.array_equal(host(val).view(np.uint32), v0.view(np.uint32))
     assert np.array_equal(host(logits), l32)
+    # independent of the stated fp32 product order: the chosen row is a maximum of the
+    # fp64 logits up to the two fp32 roundings of each logit, and it is the fp64 argmax
+    # wherever the top two are further apart than that
+    for r in range(m):
+        top = np.sort(y64[r])[::-1]
+        tol = 4 * 2.0 ** -24 * np.abs(y64[r]).max()
+        assert y64[r, i0[r]] >= top[0] - tol, (r, i0[r])
+        if top[0] - top[1] > 2 * tol:
+            assert i0[r] == int(np.argmax(y64[r]))
 
 
 def test_head_argmax_i8_ties_take_the_lowest_row(tw):

@@ -290,10 +290,11 @@ def test_head_one_hot_exact(tw):
 
 
 @pytest.mark.parametrize("n,k,m", [(16, 128, 1), (40, 640, 64), (256, 1536, 130), (200, 2048, 300),
-                                   (200, 4608, 300), (100, 8192, 1100)])
+                                   (200, 4608, 300), (203, 4096, 300), (100, 8192, 1100)])
 def test_prefill_small(tw, n, k, m):
-    """Block sums bit for bit and y against the oracle.  The last two cases run the
-    workgroup-shared decode with K split in two halves (9 and 16 k-tiles of 512)."""
+    """Block sums bit for bit and y against the oracle.  The last three cases run the
+    workgroup-shared decode with K split in two halves (9, 8 and 16 k-tiles of 512;
+    N = 203 takes the row-scaling pass with 4-byte accesses)."""
     t, s, x = gen(n, k, m, seed=n + m)
     q0, s0 = oracle.quantize_i8(x)
     import torch
