@@ -238,13 +238,14 @@ TRAFFIC_PROFILE = "profiles/tern_gemv_m1_8b_token_fused_hbm_traffic.txt"
 GEMV_SOURCES = ("tern_gemv.hip", "tern_oneshot.h", "tern_tile.h", "tern_device.h")   # the M = 1 GEMV's sources
 
 
-def measured_traffic(root: str, compose: str):
+def measured_traffic(root: str, compose: str, config: int = 2):
     """HBM bytes per ternary-GEMV launch from the committed memory-counter
-    summary, or None when it does not apply: other composition, or the GEMV
-    kernel source changed since the counters were taken."""
+    summary, or None when it does not apply: other shapes (the summary covers
+    the 8B shapes), other composition, or the GEMV kernel source changed since
+    the counters were taken."""
     import hashlib
     import re
-    if compose != "fused":
+    if compose != "fused" or config != 2:
         return None
     try:
         text = open(os.path.join(root, TRAFFIC_PROFILE)).read()
@@ -276,7 +277,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
     base = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4)}
     if args.engine == "chain":
-        base.update({"traffic": measured_chain_traffic(root, args.compose),
+        base.update({"traffic": measured_chain_traffic(root, args.compose) if args.config == 2 else None,
                      "kernel": f"chain_kernel (tern_gemv_chain, M=1, {n_tern} dependent steps per launch)",
                      "avg_launch_us": round(tern_ms * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes),
@@ -284,7 +285,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
                      "us_per_linear_step": round(tern_ms / n_tern * 1e3, 3),
                      "timing": "HIP events around back-to-back launches of the step's ternary chain"})
     else:
-        base.update({"traffic": measured_traffic(root, args.compose),
+        base.update({"traffic": measured_traffic(root, args.compose, args.config),
                      "kernel": "gemv_m1_kernel<U> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),

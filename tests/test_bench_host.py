@@ -36,6 +36,7 @@ def test_traffic_figure_follows_the_kernel_sources(tmp_path):
     assert bench.measured_traffic(str(tmp_path), "fused") == 13023000
     # other compositions have no counter figure
     assert bench.measured_traffic(str(tmp_path), "separate") is None
+    assert bench.measured_traffic(str(tmp_path), "fused", 1) is None     # the summary covers the 8B shapes
     # a changed source voids it
     (src_dir / bench.GEMV_SOURCES[0]).write_bytes(blob[:10])
     assert bench.measured_traffic(str(tmp_path), "fused") is None
