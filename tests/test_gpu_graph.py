@@ -47,6 +47,13 @@ def test_decode_calls_replay_in_a_graph(tw):
     x1 = dev(synth.gen_x_bf16(rng, 1, k))
     x8 = dev(synth.gen_x_bf16(rng, 8, k))
     ids = dev(np.array([5, 19999, 0, 123], np.int32))
+    # prefill: 300 activation rows; the 512-row weight gives a small grid, so K is split in
+    # two halves (clear, atomic partial sums, row scaling), the 6144-row one is not
+    n2, mp = 512, 300
+    t2 = synth.gen_ternary(rng, n2, k)
+    s2 = synth.gen_scales(rng, n2, k // 128)
+    packed2 = tw.tern_pack(dev(t2), dev(s2))
+    xp = dev(synth.gen_x_bf16(rng, mp, k))
     ws = tw.i8_head_argmax_workspace(v, 8)
     ws_b = tw.i8_head_argmax_workspace(v, 1)
 
@@ -57,6 +64,8 @@ def test_decode_calls_replay_in_a_graph(tw):
         "idx": torch.empty(8, dtype=torch.int32, device="cuda"), "val": f32(8), "logits": f32(8, v),
         "idxb": torch.empty(1, dtype=torch.int32, device="cuda"), "valb": f32(1),
         "emb": f32(4, k), "embh": torch.empty((4, k), dtype=torch.bfloat16, device="cuda"),
+        "qp": torch.empty((mp, k), dtype=torch.int8, device="cuda"), "sxp": f32(mp),
+        "yp": f32(mp, n2), "yp2": f32(mp, n),
     }
 
     def step():
@@ -73,6 +82,9 @@ def test_decode_calls_replay_in_a_graph(tw):
         out["idxb"].copy_(i)
         out["valb"].copy_(vv)
         tw.fv5b_embed(WB, SB, ids, out=out["emb"], out_bf16=out["embh"])
+        tw.tern_quantize_i8(xp, q=out["qp"], s_x=out["sxp"])
+        tw.tern_gemm_prefill(packed2, n2, k, out["qp"], out["sxp"], y=out["yp"])
+        tw.tern_gemm_prefill(packed, n, k, out["qp"], out["sxp"], y=out["yp2"])
 
     step()
     torch.cuda.synchronize()
@@ -92,6 +104,12 @@ def test_decode_calls_replay_in_a_graph(tw):
     assert oracle.rel_l2(eager["y5i"].cpu().numpy(), y5i) < 1e-5
     emb = fv5b.embed_f32(wb, sb, ids.cpu().numpy())
     assert np.array_equal(eager["emb"].cpu().numpy(), emb)
+    qp0, sxp0 = oracle.quantize_i8(xp.view(torch.int16).cpu().numpy().view(np.uint16))
+    _, yp64, _ = oracle.tern_i8(oracle.pack(t2, s2), n2, k, qp0, sxp0, want_acc=False)
+    assert oracle.rel_l2(eager["yp"].cpu().numpy(), yp64) < 1e-5
+    rows = np.arange(0, n, 97)
+    _, yq64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, qp0, sxp0, want_acc=False)
+    assert oracle.rel_l2(eager["yp2"].cpu().numpy()[:, rows], yq64) < 1e-5
 
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
