@@ -499,7 +499,7 @@ static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const 
     // with one atomic fp32 add per element (two addends onto zero give the same sum in
     // either order, so y is deterministic), and a last pass multiplies each row by s_x:
     // y = fl(s_x * fl(a + b)).
-    const bool split = nkt >= 8 && 2 * tiles <= 256;
+    const bool split = nkt >= 8 && 2 * tiles <= device_cus();
     const int kts = split ? (nkt + 1) / 2 : nkt;
     const dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM), split ? 2u : 1u);
     if (split) {
