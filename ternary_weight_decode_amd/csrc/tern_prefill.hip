@@ -493,7 +493,7 @@ static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const 
     // keeps at least 4 k-tiles.  A lone workgroup on a CU runs its blocks one after another
     // (about 0.65 us per 128-k block on the 8B down shape whatever the tile count), so the
     // split halves the time where CUs would otherwise idle: 8B down at M = 128 / 256 / 1024
-    // 61.5 / 61.8 / 135.0 us -> 38.6 / 43.7 / 102.4 us.  Two workgroups per CU gain nothing
+    // 61.5 / 61.8 / 135.0 us -> 38.1 / 41.7 / 98.9 us.  Two workgroups per CU gain nothing
     // (down at M = 512: 62.6 vs 63.7 us) and short K loses to the two extra passes (gate at
     // M = 128: 26.4 vs 31.8 us).  y is cleared first, each half adds its unscaled partial
     // with one atomic fp32 add per element (two addends onto zero give the same sum in
