@@ -1034,12 +1034,21 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
     if (K % 512 == 0 && M >= 128) {
-        // workgroup-shared decode.  256 x 128 workgroup tiles (8 waves of
-        // 64 x 64) from M = 1024; below, 128 x 64 tiles (4 waves of 32 x 64,
-        // three workgroups per CU).  Measured on the 8B shapes: gate M = 2048
-        // 170 us vs 174 us, down M = 2048 141 us vs 167 us; gate M = 512
-        // 51 us vs 59 us, down M = 512 65 us vs 132 us.
-        if (M >= 1024) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+        // workgroup-shared decode: 256 x 128 workgroup tiles (8 waves of 64 x 64, one
+        // workgroup per CU) or 128 x 64 tiles (4 waves of 32 x 64, up to three per CU),
+        // whichever a measured cost model favours.  Per 128-k block on the 8B shapes, a CU
+        // with j tiles of 128 x 64 takes about 0.65, 1.0 and 1.5 us for j = 1, 2, 3 and
+        // 0.48 j us beyond (they run three at a time); with j tiles of 256 x 128 (one at a
+        // time) about 1.6 j us.  So the large tile wins where its tiles fill whole rounds
+        // (gate M = 2048: 165 vs 184 us, down M = 2048: 139 vs 168 us, down M = 4096: 274
+        // vs 314 us) and the small one elsewhere (gate M = 768 / 1024 / 1536: 76.8 / 91.2 /
+        // 133.8 us against 106.8 / 108.1 / 159.8 us; down M = 1024 / 1536 / 3072: 90.6 /
+        // 122.7 / 238.7 us against 99.5 / 136.3 / 269.3 us).
+        const int64_t cus = device_cus();
+        const int64_t j_small = ((N + 63) / 64 * ((M + 127) / 128) + cus - 1) / cus;
+        const int64_t j_big = ((N + 127) / 128 * ((M + 255) / 256) + cus - 1) / cus;
+        const double small_us = j_small == 1 ? 0.65 : j_small == 2 ? 1.0 : j_small == 3 ? 1.5 : 0.48 * (double)j_small;
+        if (1.6 * (double)j_big < small_us) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
         return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
     }
     {   // 17 <= M <= 64, K <= 4096: activations held in registers, one wave per k-tile
