@@ -428,8 +428,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
 
 // The split prefill's first and last passes over y (M x N fp32, row-major): clear it, and
 // multiply row m by s_x[m].  16-byte accesses where y is 16-byte aligned (and, for the
-// row scaling, rows are too: N % 4 == 0); 8B down at M = 1024 (16 MB of y) took 6.5 and
-// 9.5 us with 4-byte accesses.
+// row scaling, rows are too: N % 4 == 0); on 16 MB of y (8B down, M = 1024) they took 6.5 and
+// 9.5 us with 4-byte accesses, 6.5 and 6.8 us with these.
 __global__ __launch_bounds__(256) void zero_f32_kernel(float* __restrict__ y, int64_t n, bool vec)
 {
     const int64_t stride = (int64_t)gridDim.x * 256;
@@ -492,8 +492,9 @@ static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const 
     // K split in two halves when both halves' workgroups still fit one per CU and each half
     // keeps at least 4 k-tiles.  A lone workgroup on a CU runs its blocks one after another
     // (about 0.65 us per 128-k block on the 8B down shape whatever the tile count), so the
-    // split halves the time where CUs would otherwise idle: 8B down at M = 128 / 256 / 1024
-    // 61.5 / 61.8 / 135.0 us -> 38.1 / 41.7 / 98.9 us.  Two workgroups per CU gain nothing
+    // split halves the time where CUs would otherwise idle: 8B down at M = 128 / 256 61.5 /
+    // 61.8 us -> 38.1 / 41.7 us (128 x 64 tiles), at M = 1024 135.0 -> 98.9 us with the
+    // 256 x 128 tile (which the tile model no longer picks there).  Two workgroups per CU gain nothing
     // (down at M = 512: 62.6 vs 63.7 us) and short K loses to the two extra passes (gate at
     // M = 128: 26.4 vs 31.8 us).  y is cleared first, each half adds its unscaled partial
     // with one atomic fp32 add per element (two addends onto zero give the same sum in
