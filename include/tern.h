@@ -453,6 +453,16 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * N, K >= 1, kind 0..8.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
 
+/* The launch of tern_gemm_prefill's workgroup-shared-decode kernel (from M = 128
+ * with K % 512 == 0), computed on the host exactly as the launcher does (CU count
+ * of the current device, or 256 without one): returns 1 and fills out[6] =
+ * {workgroup rows of M (256 or 128), workgroup rows of N (128 or 64), K split in
+ * two halves (0/1; three kernels then), grid x (tiles over N), grid y (tiles over
+ * M), grid z (2 when split, else 1)}; 0 when another kernel takes the shape;
+ * -TERN_E_NULL for a NULL out, -TERN_E_SHAPE for N, K or M below 1 or
+ * K % 128 != 0.  Touches no device memory. */
+int tern_prefill_config(int64_t N, int64_t K, int64_t M, int64_t* out);
+
 /* ---- matrix-core throughput probe (a measurement aid; no operation of the method) ----
  *
  * The contraction of tern_gemm_prefill runs on the int8 matrix cores and the

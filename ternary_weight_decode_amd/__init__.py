@@ -19,8 +19,8 @@ block-scaled int8 head and embedding (FV5B-style) ``fv5b_head_gemv[_i8]``,
 ``fv5b_head_gemv_packed[_i8]``, ``fv5b_head_argmax_packed[_i8]`` over the
 packed copy), the
 packed int8 head ``i8_head_packed_bytes``, ``i8_head_pack``,
-``i8_head_gemv_packed[_i8]``, ``i8_head_argmax_packed[_i8]``, and the launch-configuration view
-``tern_gemv_config``.
+``i8_head_gemv_packed[_i8]``, ``i8_head_argmax_packed[_i8]``, and the launch-configuration views
+``tern_gemv_config`` and ``tern_prefill_config``.
 """
 from __future__ import annotations
 
@@ -34,7 +34,7 @@ SYMBOLS = ("tern_strerror", "tern_last_error", "tern_abi_version", "tern_packed_
            "tern_chain_workspace_bytes", "tern_chain_plan", "tern_gemv_chain", "i8_head_argmax_workspace_bytes",
            "i8_head_argmax", "i8_head_argmax_i8", "tern5_packed_bytes", "tern5_pack", "tern5_gemv", "tern5_gemv_i8",
            "fv5b_head_gemv", "fv5b_head_gemv_i8", "fv5b_head_argmax", "fv5b_head_argmax_i8", "fv5b_head_argmax_embed", "fv5b_embed",
-           "tern_gemv_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
+           "tern_gemv_config", "tern_prefill_config", "tern_mfma_peak_ops", "tern_mfma_peak_sink_bytes", "tern_mfma_peak",
            "tern_launch_probe", "i8_head_argmax_noalloc", "i8_head_packed_bytes", "i8_head_pack",
            "i8_head_gemv_packed", "i8_head_gemv_packed_i8", "i8_head_argmax_packed", "i8_head_argmax_packed_i8",
            "fv5b_head_gemv_packed", "fv5b_head_gemv_packed_i8", "fv5b_head_argmax_packed",
@@ -102,6 +102,8 @@ def lib():
                                              _p]
         L.tern_gemv_config.restype = ctypes.c_int
         L.tern_gemv_config.argtypes = [_i64, _i64, _i64, ctypes.c_int, ctypes.POINTER(_i64)]
+        L.tern_prefill_config.restype = ctypes.c_int
+        L.tern_prefill_config.argtypes = [_i64, _i64, _i64, ctypes.POINTER(_i64)]
         L.tern_mfma_peak_ops.restype = ctypes.c_double
         L.tern_mfma_peak_ops.argtypes = [ctypes.c_int, _i64, _i64]
         L.tern_mfma_peak_sink_bytes.restype = _i64
@@ -660,6 +662,19 @@ def tern_gemv_config(n: int, k: int, m: int, kind: str = "ternary_bf16"):
     if rc == 0:
         return None
     keys = ("R", "waves", "U", "XC", "grid", "lds", "rounds", "MT")
+    return dict(zip(keys, (int(v) for v in out)))
+
+
+def tern_prefill_config(n: int, k: int, m: int):
+    """The workgroup-shared-decode prefill launch for this shape (host-side, no device
+    needed), as a dict, or None when another kernel takes the shape."""
+    out = (_i64 * 6)()
+    rc = lib().tern_prefill_config(n, k, m, out)
+    if rc < 0:
+        _check("tern_prefill_config", -rc)
+    if rc == 0:
+        return None
+    keys = ("BM", "BN", "split", "grid_x", "grid_y", "grid_z")
     return dict(zip(keys, (int(v) for v in out)))
 
 

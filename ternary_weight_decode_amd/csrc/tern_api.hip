@@ -635,6 +635,21 @@ int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out)
     return 1;
 }
 
+int tern_prefill_config(int64_t N, int64_t K, int64_t M, int64_t* out)
+{
+    if (!out) return -TERN_E_NULL;
+    if (N < 1 || K < 1 || M < 1 || K % 128 != 0) return -TERN_E_SHAPE;
+    tern::Pf2Config c{};
+    if (!tern::prefill2_config(N, K, M, c)) return 0;
+    out[0] = c.BM;
+    out[1] = c.BN;
+    out[2] = c.split ? 1 : 0;
+    out[3] = c.grid_x;
+    out[4] = c.grid_y;
+    out[5] = c.grid_z;
+    return 1;
+}
+
 }  // extern "C"
 
 extern "C" {

@@ -139,4 +139,14 @@ hipError_t launch_probe(int kind, int64_t grid, const void* src, int64_t src_byt
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream);
 
+// Host-side view of the workgroup-shared-decode prefill's launch (M >= 128, K % 512 == 0):
+// workgroup tile, whether K is split in two halves, and the grid; false when another
+// kernel takes the shape.
+struct Pf2Config {
+    int BM, BN;
+    bool split;
+    int64_t grid_x, grid_y, grid_z;
+};
+bool prefill2_config(int64_t N, int64_t K, int64_t M, Pf2Config& c);
+
 }  // namespace tern

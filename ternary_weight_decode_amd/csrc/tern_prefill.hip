@@ -426,6 +426,13 @@ __global__ __launch_bounds__(64 * WGM * WGN, 2) void prefill2_kernel(
     }
 }
 
+// K split in two halves (the reason and the measurements are at launch_pf2): nkt k-tiles
+// of 512, `tiles` output tiles of the workgroup tile.
+static bool pf2_split(int64_t nkt, int64_t tiles)
+{
+    return nkt >= 8 && 2 * tiles <= device_cus();
+}
+
 // The split prefill's first and last passes over y (M x N fp32, row-major): clear it, and
 // multiply row m by s_x[m].  16-byte accesses where y is 16-byte aligned (and, for the
 // row scaling, rows are too: N % 4 == 0); on 16 MB of y (8B down, M = 1024) they took 6.5 and
@@ -500,7 +507,7 @@ static hipError_t launch_pf2(const uint8_t* packed, int64_t N, int64_t K, const 
     // with one atomic fp32 add per element (two addends onto zero give the same sum in
     // either order, so y is deterministic), and a last pass multiplies each row by s_x:
     // y = fl(s_x * fl(a + b)).
-    const bool split = nkt >= 8 && 2 * tiles <= device_cus();
+    const bool split = pf2_split(nkt, tiles);
     const int kts = split ? (nkt + 1) / 2 : nkt;
     const dim3 grid((unsigned)((N + C::BN - 1) / C::BN), (unsigned)((M + C::BM - 1) / C::BM), split ? 2u : 1u);
     if (split) {
@@ -1031,6 +1038,30 @@ static hipError_t launch_pf_small(const uint8_t* packed, int64_t N, int64_t K, c
     }
 }
 
+// The workgroup tile of the shared-decode kernel from the measured cost model described at
+// its call in launch_prefill: true for 256 x 128, false for 128 x 64.
+static bool pf2_big_tile(int64_t N, int64_t M)
+{
+    const int64_t cus = device_cus();
+    const int64_t j_small = ((N + 63) / 64 * ((M + 127) / 128) + cus - 1) / cus;
+    const int64_t j_big = ((N + 127) / 128 * ((M + 255) / 256) + cus - 1) / cus;
+    const double small_us = j_small == 1 ? 0.65 : j_small == 2 ? 1.0 : j_small == 3 ? 1.5 : 0.48 * (double)j_small;
+    return 1.6 * (double)j_big < small_us;
+}
+
+bool prefill2_config(int64_t N, int64_t K, int64_t M, Pf2Config& c)
+{
+    if (K % 512 != 0 || M < 128 || N < 1) return false;
+    const bool big = pf2_big_tile(N, M);
+    c.BM = big ? 256 : 128;
+    c.BN = big ? 128 : 64;
+    c.grid_x = (N + c.BN - 1) / c.BN;
+    c.grid_y = (M + c.BM - 1) / c.BM;
+    c.split = pf2_split(K / 512, c.grid_x * c.grid_y);
+    c.grid_z = c.split ? 2 : 1;
+    return true;
+}
+
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
@@ -1045,11 +1076,7 @@ hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int
         // vs 314 us) and the small one elsewhere (gate M = 768 / 1024 / 1536: 76.8 / 91.2 /
         // 133.8 us against 106.8 / 108.1 / 159.8 us; down M = 1024 / 1536 / 3072: 90.6 /
         // 122.7 / 238.7 us against 99.5 / 136.3 / 269.3 us).
-        const int64_t cus = device_cus();
-        const int64_t j_small = ((N + 63) / 64 * ((M + 127) / 128) + cus - 1) / cus;
-        const int64_t j_big = ((N + 127) / 128 * ((M + 255) / 256) + cus - 1) / cus;
-        const double small_us = j_small == 1 ? 0.65 : j_small == 2 ? 1.0 : j_small == 3 ? 1.5 : 0.48 * (double)j_small;
-        if (1.6 * (double)j_big < small_us) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
+        if (pf2_big_tile(N, M)) return launch_pf2<4, 4, 4, 2>(packed, N, K, q, s_x, M, y, acc, stream);
         return launch_pf2<2, 4, 4, 1>(packed, N, K, q, s_x, M, y, acc, stream);
     }
     {   // 17 <= M <= 64, K <= 4096: activations held in registers, one wave per k-tile

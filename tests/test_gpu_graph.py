@@ -54,6 +54,7 @@ def test_decode_calls_replay_in_a_graph(tw):
     s2 = synth.gen_scales(rng, n2, k // 128)
     packed2 = tw.tern_pack(dev(t2), dev(s2))
     xp = dev(synth.gen_x_bf16(rng, mp, k))
+    assert tw.tern_prefill_config(n2, k, mp)["split"] == 1 and tw.tern_prefill_config(n, k, mp)["split"] == 0
     ws = tw.i8_head_argmax_workspace(v, 8)
     ws_b = tw.i8_head_argmax_workspace(v, 1)
 

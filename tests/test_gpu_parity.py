@@ -295,6 +295,8 @@ def test_prefill_small(tw, n, k, m):
     """Block sums bit for bit and y against the oracle.  The last three cases run the
     workgroup-shared decode with K split in two halves (9, 8 and 16 k-tiles of 512;
     N = 203 takes the row-scaling pass with 4-byte accesses)."""
+    if k >= 4096:
+        assert tw.tern_prefill_config(n, k, m)["split"] == 1
     t, s, x = gen(n, k, m, seed=n + m)
     q0, s0 = oracle.quantize_i8(x)
     import torch
@@ -355,6 +357,8 @@ def test_prefill_exact_on_power_of_two_scales(tw, n, k, m):
     case).  K split in two halves (K = 4096 on a small grid) and whole
     (K = 2048); the last case has enough tiles to run the 256 x 128 workgroup
     tile, the others the 128 x 64 one."""
+    c = tw.tern_prefill_config(n, k, m)
+    assert c["BM"] == (256 if n == 4096 else 128) and c["split"] == (1 if k == 4096 else 0)
     rng = np.random.default_rng(8)
     t = synth.gen_ternary(rng, n, k)
     s = rng.choice(np.array([0.25, 0.5, 1.0, 2.0], np.float16), size=(n, k // 128)).view(np.uint16)

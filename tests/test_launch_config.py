@@ -187,3 +187,49 @@ def test_picker_argument_errors():
     assert L.tern_gemv_config(16, 512, 17, 0, out) == -2
     assert L.tern_gemv_config(16, 512, 1, 9, out) == -2
     assert L.tern_gemv_config(0, 512, 1, 0, out) == -2
+
+
+def test_prefill_tile_and_split_on_the_8b_shapes():
+    """The workgroup-shared-decode prefill's tile and K split on the 8B gate / down shapes
+    (a 256-CU device): the 256 x 128 tile where its tiles fill whole rounds, the 128 x 64
+    tile elsewhere, and K split in two halves only where the doubled grid still fits one
+    workgroup per CU (the measured choices)."""
+    big, small = (256, 128), (128, 64)
+    want = {(12288, 4096, 512): (small, 0), (12288, 4096, 1024): (small, 0), (12288, 4096, 1536): (small, 0),
+            (12288, 4096, 2048): (big, 0), (12288, 4096, 4096): (big, 0),
+            (4096, 12288, 128): (small, 1), (4096, 12288, 256): (small, 1), (4096, 12288, 512): (small, 0),
+            (4096, 12288, 1024): (small, 0), (4096, 12288, 3072): (small, 0), (4096, 12288, 2048): (big, 0),
+            (4096, 12288, 4096): (big, 0)}
+    for (n, k, m), (tile, split) in want.items():
+        c = tw.tern_prefill_config(n, k, m)
+        assert (c["BM"], c["BN"]) == tile and c["split"] == split, (n, k, m, c)
+
+
+@pytest.mark.parametrize("m", [128, 129, 200, 255, 256, 300, 511, 512, 777, 1024, 1100, 2048, 3000, 4096])
+def test_prefill_config_invariants(m):
+    """Over N and K: the grid covers M x N with the chosen tile, z = 2 exactly when K is
+    split, a split keeps at least 4 of 512-k tiles per half and at most one workgroup per
+    CU, and the shapes the kernel does not take (M < 128, K % 512 != 0) return None."""
+    for n, k in itertools.product([1, 16, 17, 300, 1000, 4096, 12288, 24576], [512, 1024, 3584, 4096, 4608, 12288]):
+        c = tw.tern_prefill_config(n, k, m)
+        assert c is not None
+        assert c["grid_x"] * c["BN"] >= n > (c["grid_x"] - 1) * c["BN"]
+        assert c["grid_y"] * c["BM"] >= m > (c["grid_y"] - 1) * c["BM"]
+        assert c["grid_z"] == (2 if c["split"] else 1)
+        if c["split"]:
+            assert k // 512 >= 8 and 2 * c["grid_x"] * c["grid_y"] <= 256
+        else:
+            assert k // 512 < 8 or 2 * c["grid_x"] * c["grid_y"] > 256
+    assert tw.tern_prefill_config(4096, 4096, 127) is None
+    assert tw.tern_prefill_config(4096, 4096 + 128, m) is None
+
+
+def test_prefill_config_argument_errors():
+    L = tw.lib()
+    import ctypes
+    out = (ctypes.c_int64 * 6)()
+    assert L.tern_prefill_config(16, 512, 128, None) == -1
+    assert L.tern_prefill_config(0, 512, 128, out) == -2
+    assert L.tern_prefill_config(16, 0, 128, out) == -2
+    assert L.tern_prefill_config(16, 96, 128, out) == -2
+    assert L.tern_prefill_config(16, 512, 0, out) == -2
