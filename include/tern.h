@@ -248,8 +248,10 @@ int i8_head_argmax_noalloc(const int8_t* W, const float* row_scale, int64_t V, i
  * set by its per-block latency, the call may run the int8 GEMV on 16-row
  * slices of q instead (chosen on the host from the shape); the result is the
  * same contraction (fp32 y may differ in the last bits with the kernel: the
- * block sums are added in a kernel-specific order).  From M = 128, when the
- * output tiles leave most CUs idle and K >= 4096, K is split in two halves:
+ * block sums are added in a kernel-specific order).  The workgroup-shared
+ * decode kernel runs from M = 128, and at 65 <= M < 128 where a measured model
+ * puts it ahead of the other two (see tern_prefill_config).  When its output
+ * tiles leave most CUs idle and K >= 4096, K is split in two halves:
  * the call then enqueues three kernels (y cleared, the two halves' unscaled
  * fp32 partials added with atomics, rows scaled by s_x), so y is
  * fl(s_x * fl(a + b)) and the same on every run.
@@ -453,8 +455,9 @@ int fv5b_embed(const int8_t* W, const float* S, int64_t V, int64_t K, const int3
  * N, K >= 1, kind 0..8.  Touches no device memory. */
 int tern_gemv_config(int64_t N, int64_t K, int64_t M, int kind, int64_t* out);
 
-/* The launch of tern_gemm_prefill's workgroup-shared-decode kernel (from M = 128
- * with K % 512 == 0), computed on the host exactly as the launcher does (CU count
+/* The launch of tern_gemm_prefill's workgroup-shared-decode kernel (K % 512 == 0,
+ * from M = 128 and, where a measured model favours it, at 65 <= M < 128),
+ * computed on the host exactly as the launcher does (CU count
  * of the current device, or 256 without one): returns 1 and fills out[6] =
  * {workgroup rows of M (256 or 128), workgroup rows of N (128 or 64), K split in
  * two halves (0/1; three kernels then), grid x (tiles over N), grid y (tiles over

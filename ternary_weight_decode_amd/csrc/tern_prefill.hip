@@ -1049,9 +1049,31 @@ static bool pf2_big_tile(int64_t N, int64_t M)
     return 1.6 * (double)j_big < small_us;
 }
 
+// Whether the shared-decode kernel takes the shape: from M = 128, and at 65 <= M < 128
+// where a measured model puts it ahead of the other two paths there, the per-block kernel
+// (about 0.62 us per 128-k block) and the int8 GEMV on 16-row slices (about 4 us plus the
+// weight bytes at 5.3 TB/s per slice).  The shared-decode kernel alone on a CU takes about
+// 0.65 us per block, and its K split in two adds about 5 us for the clear and the row
+// scaling: 8B down at M = 96 / 112 / 127 42.8 / 49.9 / 56.9 us (GEMV slices) -> 36.5 / 37.2 /
+// 37.6 us, down at M = 65 / 80 and gate at M = 65..127 keep their paths (33.1 / 35.9 us
+// against 36.1 / 35.9 us, gate 24.0-25.2 us against 25.4-25.9 us).
+static bool use_pf2(int64_t N, int64_t K, int64_t M)
+{
+    if (K % 512 != 0 || N < 1 || M < 65) return false;
+    if (M >= 128) return true;
+    const int64_t nb = K / kBlockK, cus = device_cus();
+    const int64_t tiles = (N + 63) / 64;                        // 128 x 64 tiles, one row of them
+    const int64_t j = (tiles + cus - 1) / cus;
+    const double small_us = j == 1 ? 0.65 : j == 2 ? 1.0 : j == 3 ? 1.5 : 0.48 * (double)j;
+    const double pf2_us = pf2_split(nb / 4, tiles) ? 0.65 * (double)(nb / 2) + 5.0 : small_us * (double)nb;
+    const double pf_us = 0.62 * (double)nb;
+    const double gemv_us = (double)((M + 15) / 16) * (4.0 + (double)N * (double)K * (0.265625 / 5.3e6));
+    return pf2_us < pf_us && pf2_us < gemv_us;
+}
+
 bool prefill2_config(int64_t N, int64_t K, int64_t M, Pf2Config& c)
 {
-    if (K % 512 != 0 || M < 128 || N < 1) return false;
+    if (!use_pf2(N, K, M)) return false;
     const bool big = pf2_big_tile(N, M);
     c.BM = big ? 256 : 128;
     c.BN = big ? 128 : 64;
@@ -1065,7 +1087,7 @@ bool prefill2_config(int64_t N, int64_t K, int64_t M, Pf2Config& c)
 hipError_t launch_prefill(const uint8_t* packed, int64_t N, int64_t K, const int8_t* q, const float* s_x,
                           int64_t M, float* y, int32_t* acc, hipStream_t stream)
 {
-    if (K % 512 == 0 && M >= 128) {
+    if (use_pf2(N, K, M)) {
         // workgroup-shared decode: 256 x 128 workgroup tiles (8 waves of 64 x 64, one
         // workgroup per CU) or 128 x 64 tiles (4 waves of 32 x 64, up to three per CU),
         // whichever a measured cost model favours.  Per 128-k block on the 8B shapes, a CU

@@ -436,12 +436,14 @@ def test_prefill_register_activations_four_row_tiles_sampled(tw):
     assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
 
 
-@pytest.mark.parametrize("n,k,m", [(300, 8192, 100), (100, 4096, 16), (37, 12288, 9)])
+@pytest.mark.parametrize("n,k,m", [(37, 12288, 100), (100, 4096, 16), (37, 12288, 9)])
 def test_prefill_small_m_through_gemv_slices(tw, n, k, m):
     """Outside the split-K kernel's range with many 128-k blocks (M <= 16, or
-    65 <= M < 128) the call runs the int8 GEMV on 16-row slices of q (ragged
-    last slice): block sums bit for bit, y against the oracle."""
+    65 <= M < 128 where the shared-decode kernel does not pay) the call runs the
+    int8 GEMV on 16-row slices of q (ragged last slice): block sums bit for bit,
+    y against the oracle."""
     import torch
+    assert tw.tern_prefill_config(n, k, m) is None
     t, s, x = gen(n, k, m, seed=n + 7 * m)
     q0, s0 = oracle.quantize_i8(x)
     p = gpu_pack(tw, t, s)
@@ -452,6 +454,26 @@ def test_prefill_small_m_through_gemv_slices(tw, n, k, m):
     assert oracle.rel_l2(y, y64) <= TOL
     y2 = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0)))
     assert oracle.rel_l2(y2, y64) <= TOL
+
+
+@pytest.mark.parametrize("n,k,m", [(300, 8192, 100), (100, 4096, 65), (2000, 12288, 127)])
+def test_prefill_shared_decode_below_128(tw, n, k, m):
+    """65 <= M < 128 where the measured model picks the shared-decode kernel with K
+    split in two halves: block sums bit for bit and y against the oracle (sampled
+    output rows for the largest case), the no-debug instance bit for bit the same."""
+    import torch
+    c = tw.tern_prefill_config(n, k, m)
+    assert c is not None and c["BM"] == 128 and c["split"] == 1
+    t, s, x = gen(n, k, m, seed=5 * n + m)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    y = host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0), acc=acc))
+    rows = np.arange(n) if n <= 300 else np.sort(np.random.default_rng(3).choice(n, 64, replace=False))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+    assert np.array_equal(host(acc)[:, rows], acc0)
+    assert oracle.rel_l2(y[:, rows], y64) <= TOL
+    assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
 
 
 def test_prefill_down_m64_sampled(tw):

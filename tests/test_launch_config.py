@@ -220,8 +220,23 @@ def test_prefill_config_invariants(m):
             assert k // 512 >= 8 and 2 * c["grid_x"] * c["grid_y"] <= 256
         else:
             assert k // 512 < 8 or 2 * c["grid_x"] * c["grid_y"] > 256
-    assert tw.tern_prefill_config(4096, 4096, 127) is None
+    assert tw.tern_prefill_config(4096, 4096, 64) is None
     assert tw.tern_prefill_config(4096, 4096 + 128, m) is None
+
+
+def test_prefill_config_below_128():
+    """65 <= M < 128: the shared-decode kernel only where the measured model puts it
+    ahead of the per-block kernel and the GEMV slices (8B down at M >= 96 with K split;
+    8B gate and down at M = 65 / 80 keep their paths); never at M <= 64."""
+    for m in (96, 112, 127):
+        c = tw.tern_prefill_config(4096, 12288, m)
+        assert c is not None and (c["BM"], c["split"], c["grid_z"]) == (128, 1, 2), (m, c)
+    for m in (65, 80):
+        assert tw.tern_prefill_config(4096, 12288, m) is None
+    for m in (65, 96, 127):
+        assert tw.tern_prefill_config(12288, 4096, m) is None
+    for m in (1, 16, 17, 64):
+        assert tw.tern_prefill_config(4096, 12288, m) is None
 
 
 def test_prefill_config_argument_errors():
