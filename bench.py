@@ -827,10 +827,12 @@ def main():
         # the only profiler region of the run: rocprofv3 --selected-regions traces exactly these
         # reps x n_tern launches, the ones the roofline's average is taken over
         g_tern = capture(torch, step.run_tern)
-        tern_ms = time_replays(torch, g_tern, reps, ProfilerRegion())
+        # one warm replay (the step's W warmup replays ran just before): the dispatch
+        # windows the committed trace summaries average over stay fixed
+        tern_ms = time_replays(torch, g_tern, reps, ProfilerRegion(), warm_ms=0.0)
     achieved = step.tern_bytes / (tern_ms * 1e-3) / 1e9
     g_head = capture(torch, step.run_head)
-    head_ms = time_replays(torch, g_head, reps)
+    head_ms = time_replays(torch, g_head, reps, warm_ms=0.0)
     # per launch kind (graph engine only: inside the chain the kinds overlap)
     shapes = None
     if not chain:
@@ -838,7 +840,7 @@ def main():
         for label in dict.fromkeys(l[7] for l in step.launches):
             ls = [l for l in step.launches if l[7] == label]
             gl = capture(torch, lambda lab=label: step.run_tern(lab))
-            ms = time_replays(torch, gl, reps) / len(ls)
+            ms = time_replays(torch, gl, reps, warm_ms=0.0) / len(ls)
             del gl
             b = ls[0][6]
             shapes[label] = {"n_k": [ls[0][2], ls[0][3]], "launches": len(ls), "us": round(ms * 1e3, 2),
