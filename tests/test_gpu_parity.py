@@ -476,6 +476,30 @@ def test_prefill_shared_decode_below_128(tw, n, k, m):
     assert np.array_equal(y, host(tw.tern_gemm_prefill(p, n, k, dev(q0), dev(s0))))
 
 
+def test_prefill_split_full_down_shape_repeatable(tw):
+    """The 8B down shape at M = 256 runs with K split in two halves (two atomic fp32
+    addends per output): five calls give the same bytes, and sampled rows match the
+    oracle with their block sums bit for bit."""
+    import torch
+    n, k = synth.SHAPES_8B["down"]
+    m = 256
+    c = tw.tern_prefill_config(n, k, m)
+    assert c["split"] == 1 and c["grid_z"] == 2
+    t, s, x = gen(n, k, m, seed=11)
+    q0, s0 = oracle.quantize_i8(x)
+    p = gpu_pack(tw, t, s)
+    q, sx = dev(q0), dev(s0)
+    ys = [host(tw.tern_gemm_prefill(p, n, k, q, sx)) for _ in range(5)]
+    assert all(np.array_equal(ys[0], y) for y in ys[1:])
+    rows = np.sort(np.random.default_rng(4).choice(n, 48, replace=False))
+    acc = torch.empty((m, n, k // 128), dtype=torch.int32, device="cuda")
+    yd = host(tw.tern_gemm_prefill(p, n, k, q, sx, acc=acc))
+    acc0, y64, _ = oracle.tern_i8(oracle.pack(t[rows], s[rows]), len(rows), k, q0, s0)
+    assert np.array_equal(host(acc)[:, rows], acc0)
+    assert oracle.rel_l2(ys[0][:, rows], y64) <= TOL
+    assert np.array_equal(yd, ys[0])
+
+
 def test_prefill_down_m64_sampled(tw):
     """The 8B down shape at M = 64 (four GEMV slices): sampled rows."""
     n, k = synth.SHAPES_8B["down"]
