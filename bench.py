@@ -260,6 +260,32 @@ def measured_traffic(root: str, compose: str, config: int = 2):
     return int(float(m.group(1)) * 1e6)
 
 
+TRACE_PROFILE = "profiles/tern_gemv_m1_8b_token_fused_kernel_trace.txt"
+
+
+def measured_trace(root: str, compose: str, config: int = 2):
+    """The dominant kernel's mean device duration per launch from the committed rocprofv3
+    trace summary (the roofline replays' dispatch window), and the roofline fraction it
+    gives, or None when it does not apply: other shapes or composition, or the GEMV kernel
+    source changed since the trace was taken.  Under the tracer every dispatch is timed on
+    its own and runs longer than between graph replays, so this fraction is the lower one."""
+    import hashlib
+    import re
+    if compose != "fused" or config != 2:
+        return None
+    try:
+        text = open(os.path.join(root, TRACE_PROFILE)).read()
+        src = b"".join(open(os.path.join(root, "ternary_weight_decode_amd", "csrc", f), "rb").read()
+                       for f in GEMV_SOURCES)
+    except OSError:
+        return None
+    m = re.search(r"/ ([0-9.]+) us \(roofline replays\) = [0-9.]+ TB/s = ([0-9.]+) of 8 TB/s", text)
+    h = re.search(r"kernel sources sha256 \(" + ", ".join(GEMV_SOURCES) + r"\): ([0-9a-f]{64})", text)
+    if not m or not h or h.group(1) != hashlib.sha256(src).hexdigest():
+        return None
+    return {"avg_launch_us": float(m.group(1)), "frac": float(m.group(2)), "source": TRACE_PROFILE}
+
+
 def time_calls(torch, fn, reps: int) -> float:
     """Mean milliseconds per call of fn (launches only) from HIP events on the current stream."""
     fn()
@@ -286,6 +312,7 @@ def roofline(root, args, achieved, tern_ms, n_tern, step):
                      "timing": "HIP events around back-to-back launches of the step's ternary chain"})
     else:
         base.update({"traffic": measured_traffic(root, args.compose, args.config),
+                     "traced": measured_trace(root, args.compose, args.config),
                      "kernel": "gemv_m1_kernel<U> (tern_gemv, M=1)",
                      "avg_launch_us": round(tern_ms / n_tern * 1e3, 3),
                      "avg_bytes_per_launch": int(step.tern_bytes / n_tern),

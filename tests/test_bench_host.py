@@ -43,3 +43,28 @@ def test_traffic_figure_follows_the_kernel_sources(tmp_path):
     # and the committed summary names the same sources in the same form
     text = open(os.path.join(ROOT, bench.TRAFFIC_PROFILE)).read()
     assert f"kernel sources sha256 ({', '.join(bench.GEMV_SOURCES)}) at measurement:" in text
+
+
+def test_traced_figure_follows_the_kernel_sources(tmp_path):
+    """The traced mean duration is read from the trace summary only while the GEMV sources hash
+    to the value recorded with the trace, and the committed summary yields it now."""
+    import hashlib
+    src_dir = tmp_path / "ternary_weight_decode_amd" / "csrc"
+    src_dir.mkdir(parents=True)
+    (tmp_path / "profiles").mkdir()
+    blob = b""
+    for f in bench.GEMV_SOURCES:
+        data = open(os.path.join(ROOT, "ternary_weight_decode_amd", "csrc", f), "rb").read()
+        (src_dir / f).write_bytes(data)
+        blob += data
+    summary = (f"kernel sources sha256 ({', '.join(bench.GEMV_SOURCES)}): {hashlib.sha256(blob).hexdigest()}\n"
+               "roofline of the dominant kernel from the trace: 12,863,488 algorithmic bytes per launch (mean over the four\n"
+               "kinds) / 5.130 us (roofline replays) = 2.508 TB/s = 0.313 of 8 TB/s.\n")
+    (tmp_path / bench.TRACE_PROFILE).write_text(summary)
+    t = bench.measured_trace(str(tmp_path), "fused")
+    assert t == {"avg_launch_us": 5.130, "frac": 0.313, "source": bench.TRACE_PROFILE}
+    assert bench.measured_trace(str(tmp_path), "separate") is None
+    assert bench.measured_trace(str(tmp_path), "fused", 1) is None
+    (src_dir / bench.GEMV_SOURCES[0]).write_bytes(blob[:10])
+    assert bench.measured_trace(str(tmp_path), "fused") is None
+    assert bench.measured_trace(ROOT, "fused") is not None
